@@ -1,0 +1,400 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for one routed mixture-of-experts FFN
+ * layer restricted to an expert band.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the test suite, the smoke check and the CPU-baseline leg
+ * of the benchmark use it.  It shares no code, header or table with the HIP
+ * library; it is written from the method's definition, one row at a time.
+ *
+ * Pages cited (titles as published):
+ *   [P1] "GLM-5.2 multi-GPU: expert-parallel sharding + the resident-fit
+ *        benchmark" (fak note)
+ *   [P2] "GLM-5.3-Flash on CUDA: attention on one GPU, routed experts on the
+ *        Sparks (proposal) #214"
+ *   [P4] "GLM-5.3-Flash on CUDA over three ranks (--tp 3) ... #310"
+ *   [P5] "GLM-5.3-Flash and full GLM-5.3 on the native CUDA engine (tracker)
+ *        #593"
+ *
+ * Precision: the router logits are fp32 in a fixed reduction order (they
+ * decide integers -- the top-k ids -- so both sides take that decision in the
+ * same precision and order).  Everything after the selection (softmax
+ * weights, SwiGLU, down projection, weighted sum, shared expert) is fp64.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC  (no contraction:
+ * every fp32 fused multiply-add below is an explicit fmaf).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+
+/* bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits. */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router logits.                                                             */
+/*                                                                            */
+/* [P1] "What landed": the router runs replicated on every rank and picks the */
+/* same top-k, so every rank must compute bit-identical logits.  [P5] "What   */
+/* exists now" describes the GLM glue as fp32 fixed-order reductions, and     */
+/* [P4] (maintainer reply) requires every sum to follow one fixed tree.  The  */
+/* fixed order used here (called R-order) is:                                 */
+/*   64 partial sums p_l, l = 0..63, each starting at +0.0;                   */
+/*   for i = 0..H/256-1 (outer), c = 0..3 (inner):                            */
+/*       p_l = fmaf(x[256 i + 4 l + c], w[256 i + 4 l + c], p_l)              */
+/*   then six pairwise rounds s = 1,2,4,8,16,32: p_l <- p_l + p_(l xor s);     */
+/*   the dot is p_0.  logit = dot + bias (one fp32 add), -0.0 becomes +0.0.   */
+/* ------------------------------------------------------------------------ */
+float oracle_dot_r(const float* x, const float* w, int H)
+{
+    float p[64], q[64];
+    for (int l = 0; l < 64; ++l) p[l] = 0.0f;
+    for (int i = 0; i < H / 256; ++i)
+        for (int l = 0; l < 64; ++l)
+            for (int c = 0; c < 4; ++c) {
+                int k = 256 * i + 4 * l + c;
+                p[l] = fmaf(x[k], w[k], p[l]);
+            }
+    for (int s = 1; s < 64; s <<= 1) {
+        for (int l = 0; l < 64; ++l) q[l] = p[l] + p[l ^ s];
+        for (int l = 0; l < 64; ++l) p[l] = q[l];
+    }
+    return p[0];
+}
+
+int oracle_router_logits(const uint16_t* x, int T, int H, const float* wr,
+                         const float* bias, int E, float* logits)
+{
+    if (T < 0 || H <= 0 || H % 256 != 0 || E <= 0) return OR_EINVAL;
+#pragma omp parallel
+    {
+        float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            for (int k = 0; k < H; ++k) xf[k] = bf16_to_f32(x[(size_t)t * H + k]);
+            for (int e = 0; e < E; ++e) {
+                float l = oracle_dot_r(xf, wr + (size_t)e * H, H);
+                if (bias) l = l + bias[e];
+                if (l == 0.0f) l = 0.0f; /* -0.0 -> +0.0 */
+                logits[(size_t)t * E + e] = l;
+            }
+        }
+        free(xf);
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-k selection and renormalised weights, one row.                         */
+/*                                                                            */
+/* [P2] "Per MoE layer": the expert side receives the rows with their top-k   */
+/* ids and weights.  The workload fixes a softmax router whose top-k weights  */
+/* are renormalised to sum to one.  Order: logit descending, expert id        */
+/* ascending on ties (softmax is monotone, so selecting on logits is          */
+/* selecting on probabilities).  The weights are the softmax over the k picks */
+/* -- the full softmax's denominator cancels in the renormalisation.          */
+/* ------------------------------------------------------------------------ */
+static void topk_row(const float* l, int E, int k, int32_t* ids, double* w)
+{
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || l[e] > l[best]) best = e; /* strict: ties keep lower id */
+        }
+        taken[best] = 1;
+        ids[j] = best;
+    }
+    free(taken);
+    double m = (double)l[ids[0]];
+    double s = 0.0;
+    for (int j = 0; j < k; ++j) {
+        w[j] = exp((double)l[ids[j]] - m);
+        s += w[j];
+    }
+    for (int j = 0; j < k; ++j) w[j] = w[j] / s;
+}
+
+int oracle_topk(const float* logits, int T, int E, int k, int32_t* ids, double* w)
+{
+    if (T < 0 || E <= 0 || k < 1 || k > E) return OR_EINVAL;
+    for (int t = 0; t < T; ++t)
+        topk_row(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch for the band [lo, hi).                                            */
+/*                                                                            */
+/* [P1] "What landed": each rank contributes only the picks it owns.  The     */
+/* grouping of picks by expert is the batched dispatch of [P1]'s lever table  */
+/* ("batched expert dispatch"), and [P5] gates the device grouping plan as    */
+/* byte-equal to the host routing.  Definition:                               */
+/*   counts[e-lo]  = #{(t,j) : ids[t,j] = e}                                  */
+/*   offsets       = exclusive prefix sum of counts (length nb+1)             */
+/*   perm          = for e = lo..hi-1, then t ascending, then j: t*k + j      */
+/*   pos[t*k + j]  = index of that pick in perm, or -1 outside the band.      */
+/* Returns the number of in-band picks, or OR_EINVAL.                         */
+/* ------------------------------------------------------------------------ */
+int oracle_dispatch(const int32_t* ids, int T, int k, int lo, int hi,
+                    int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos)
+{
+    if (T < 0 || k < 1 || lo < 0 || hi <= lo) return OR_EINVAL;
+    int nb = hi - lo;
+    for (int e = 0; e < nb; ++e) counts[e] = 0;
+    for (int p = 0; p < T * k; ++p) {
+        int e = ids[p];
+        if (e >= lo && e < hi) counts[e - lo] += 1;
+    }
+    offsets[0] = 0;
+    for (int e = 0; e < nb; ++e) offsets[e + 1] = offsets[e] + counts[e];
+    for (int p = 0; p < T * k; ++p) pos[p] = -1;
+    int cursor = 0;
+    for (int e = lo; e < hi; ++e)
+        for (int t = 0; t < T; ++t)
+            for (int j = 0; j < k; ++j)
+                if (ids[t * k + j] == e) {
+                    perm[cursor] = t * k + j;
+                    pos[t * k + j] = cursor;
+                    cursor += 1;
+                }
+    return cursor;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert weights.                                                            */
+/*                                                                            */
+/* bf16: w_gate_up [E, 2I, H] (rows 0..I-1 gate, I..2I-1 up: [P5]'s fused     */
+/*       gate/up rows are 2w wide), w_down [E, H, I].                          */
+/* w4:   4-bit unsigned codes, two per byte, low nibble = even k, with a bf16 */
+/*       scale s and zero z per 32-wide group along k; the weight is          */
+/*       (q - z) * s.  [P5] "The pieces, in order" lists W4A16 checkpoints    */
+/*       (4-bit weights, 16-bit activations) on the family; [P4] names the    */
+/*       group units.                                                         */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t fmt; /* 0 = bf16, 1 = w4 (group 32) */
+    int32_t E, H, I;
+    const uint16_t* w_gate_up;
+    const uint16_t* w_down;
+    const uint8_t* q_gate_up;
+    const uint16_t* s_gate_up;
+    const uint16_t* z_gate_up;
+    const uint8_t* q_down;
+    const uint16_t* s_down;
+    const uint16_t* z_down;
+} oracle_experts;
+
+/* Row n of a [rows, K] matrix of expert e, as doubles. */
+static void bf16_row(const uint16_t* base, size_t rows, int K, int e, int n, double* out)
+{
+    const uint16_t* r = base + ((size_t)e * rows + (size_t)n) * (size_t)K;
+    for (int k = 0; k < K; ++k) out[k] = (double)bf16_to_f32(r[k]);
+}
+
+static void w4_row(const uint8_t* q, const uint16_t* s, const uint16_t* z, size_t rows, int K,
+                   int e, int n, double* out)
+{
+    size_t row = (size_t)e * rows + (size_t)n;
+    const uint8_t* qr = q + row * (size_t)(K / 2);
+    const uint16_t* sr = s + row * (size_t)(K / 32);
+    const uint16_t* zr = z + row * (size_t)(K / 32);
+    for (int k = 0; k < K; ++k) {
+        uint8_t byte = qr[k / 2];
+        int code = (k % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+        double sc = (double)bf16_to_f32(sr[k / 32]);
+        double zr_ = (double)bf16_to_f32(zr[k / 32]);
+        out[k] = ((double)code - zr_) * sc;
+    }
+}
+
+static void gate_up_row(const oracle_experts* ex, int e, int n, double* out)
+{
+    size_t rows = 2 * (size_t)ex->I;
+    if (ex->fmt == 0) bf16_row(ex->w_gate_up, rows, ex->H, e, n, out);
+    else w4_row(ex->q_gate_up, ex->s_gate_up, ex->z_gate_up, rows, ex->H, e, n, out);
+}
+
+static void down_row(const oracle_experts* ex, int e, int n, double* out)
+{
+    size_t rows = (size_t)ex->H;
+    if (ex->fmt == 0) bf16_row(ex->w_down, rows, ex->I, e, n, out);
+    else w4_row(ex->q_down, ex->s_down, ex->z_down, rows, ex->I, e, n, out);
+}
+
+static double dot(const double* a, const double* b, int n)
+{
+    double s = 0.0;
+    for (int i = 0; i < n; ++i) s += a[i] * b[i];
+    return s;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One expert's SwiGLU FFN on one row: y = W_down (silu(W_gate x) * W_up x),  */
+/* silu(g) = g / (1 + exp(-g)).  [P1] "Update (later 2026-06-29)" names the   */
+/* per-expert expertSwiGLU; [P5] "What exists now" fixes the fused gate/up    */
+/* rows as 2w wide.  fp64 throughout.                                          */
+/* ------------------------------------------------------------------------ */
+int oracle_expert_ffn(const double* x, const oracle_experts* ex, int e, double* y)
+{
+    if (e < 0 || e >= ex->E) return OR_EINVAL;
+    int H = ex->H, I = ex->I;
+    double* row = (double*)malloc(sizeof(double) * (size_t)(H > I ? H : I));
+    double* h = (double*)malloc(sizeof(double) * (size_t)I);
+    for (int i = 0; i < I; ++i) {
+        gate_up_row(ex, e, i, row);
+        double g = dot(row, x, H);
+        gate_up_row(ex, e, I + i, row);
+        double u = dot(row, x, H);
+        h[i] = g / (1.0 + exp(-g)) * u;
+    }
+    for (int c = 0; c < H; ++c) {
+        down_row(ex, e, c, row);
+        y[c] = dot(row, h, I);
+    }
+    free(row);
+    free(h);
+    return OR_OK;
+}
+
+/* The shared expert: the same SwiGLU FFN with its own bf16 weights
+ * [2Is, H] and [H, Is], applied to every row with weight 1 ([P1] gates table:
+ * GLM shared-expert wrapper; [P2] "Per MoE layer": the shared expert runs
+ * alongside the routed ones). */
+static void shared_ffn(const double* x, const uint16_t* wgu, const uint16_t* wd, int H, int Is,
+                       double* y)
+{
+    oracle_experts sh;
+    memset(&sh, 0, sizeof sh);
+    sh.fmt = 0;
+    sh.E = 1;
+    sh.H = H;
+    sh.I = Is;
+    sh.w_gate_up = wgu;
+    sh.w_down = wd;
+    oracle_expert_ffn(x, &sh, 0, y);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The layer, one row at a time.                                              */
+/*                                                                            */
+/* For each listed row t:                                                     */
+/*   logits over all E experts whatever the band ([P1]: the router runs       */
+/*   replicated and picks the same top-k); top-k ids in pick order and their  */
+/*   renormalised weights; then, in pick order j = 0..k-1 and only for picks  */
+/*   with lo <= id < hi ([P1]: each rank contributes only the picks it owns), */
+/*   acc += w_j * FFN_{id_j}(x_t), acc starting at +0.0; then, if a shared     */
+/*   expert is given, acc += FFN_shared(x_t) last.  The result is the row's    */
+/*   partial residual for the band ([P1]: per-rank [H] residual partials;     */
+/*   [P2]: partials summed in rank order).                                    */
+/*                                                                            */
+/* rows == NULL means rows 0..T-1 (nrows must equal T).  out is [nrows, H];   */
+/* ids_out [nrows, k] and w_out [nrows, k] may be NULL.                        */
+/* ------------------------------------------------------------------------ */
+static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
+                      const oracle_experts* ex, const uint16_t* sh_wgu, const uint16_t* sh_wd,
+                      int Is, int use_band, int lo, int hi, int k, const int32_t* rows, int nrows,
+                      double* out, int32_t* ids_out, double* w_out)
+{
+    if (T < 1 || H % 256 != 0 || E < 1 || k < 1 || k > E) return OR_EINVAL;
+    if (ex->E != E || ex->H != H) return OR_EINVAL;
+    if (use_band && (lo < 0 || hi > E || lo >= hi)) return OR_EINVAL;
+    if (!rows && nrows != T) return OR_EINVAL;
+    int status = OR_OK;
+#pragma omp parallel
+    {
+        float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+        double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+        float* l = (float*)malloc(sizeof(float) * (size_t)E);
+        int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+        double* w = (double*)malloc(sizeof(double) * (size_t)k);
+        double* y = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(dynamic, 1)
+        for (int r = 0; r < nrows; ++r) {
+            int t = rows ? rows[r] : r;
+            if (t < 0 || t >= T) {
+#pragma omp atomic write
+                status = OR_EINVAL;
+                continue;
+            }
+            for (int c = 0; c < H; ++c) {
+                xf[c] = bf16_to_f32(x[(size_t)t * H + c]);
+                xd[c] = (double)xf[c];
+            }
+            for (int e = 0; e < E; ++e) {
+                float v = oracle_dot_r(xf, wr + (size_t)e * H, H);
+                if (bias) v = v + bias[e];
+                if (v == 0.0f) v = 0.0f;
+                l[e] = v;
+            }
+            topk_row(l, E, k, ids, w);
+            double* acc = out + (size_t)r * H;
+            for (int c = 0; c < H; ++c) acc[c] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                if (use_band && (ids[j] < lo || ids[j] >= hi)) continue;
+                oracle_expert_ffn(xd, ex, ids[j], y);
+                for (int c = 0; c < H; ++c) acc[c] += w[j] * y[c];
+            }
+            if (sh_wgu && sh_wd) {
+                shared_ffn(xd, sh_wgu, sh_wd, H, Is, y);
+                for (int c = 0; c < H; ++c) acc[c] += y[c];
+            }
+            if (ids_out)
+                for (int j = 0; j < k; ++j) ids_out[(size_t)r * k + j] = ids[j];
+            if (w_out)
+                for (int j = 0; j < k; ++j) w_out[(size_t)r * k + j] = w[j];
+        }
+        free(xf);
+        free(xd);
+        free(l);
+        free(ids);
+        free(w);
+        free(y);
+    }
+    return status;
+}
+
+/* The layer restricted to the expert band [lo, hi). */
+int oracle_moe_ffn(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
+                   const oracle_experts* ex, const uint16_t* sh_wgu, const uint16_t* sh_wd, int Is,
+                   int lo, int hi, int k, const int32_t* rows, int nrows, double* out,
+                   int32_t* ids_out, double* w_out)
+{
+    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 1, lo, hi, k, rows, nrows, out,
+                      ids_out, w_out);
+}
+
+/* The routed monolith: the same layer with no band logic at all (every pick
+ * contributes).  [P1] gates table: EP with one rank must equal it bit for bit. */
+int oracle_moe_ffn_monolith(const uint16_t* x, int T, int H, const float* wr, const float* bias,
+                            int E, const oracle_experts* ex, const uint16_t* sh_wgu,
+                            const uint16_t* sh_wd, int Is, int k, const int32_t* rows, int nrows,
+                            double* out)
+{
+    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 0, 0, E, k, rows, nrows, out,
+                      NULL, NULL);
+}
+
+/* Dequantised weight matrix of one expert, for pins that compare the 4-bit
+ * decode against a known matrix.  which = 0: gate/up [2I, H]; 1: down [H, I]. */
+int oracle_expert_matrix(const oracle_experts* ex, int e, int which, double* out)
+{
+    if (e < 0 || e >= ex->E) return OR_EINVAL;
+    if (which == 0) {
+        for (int n = 0; n < 2 * ex->I; ++n) gate_up_row(ex, e, n, out + (size_t)n * ex->H);
+    } else {
+        for (int n = 0; n < ex->H; ++n) down_row(ex, e, n, out + (size_t)n * ex->I);
+    }
+    return OR_OK;
+}

@@ -1,0 +1,224 @@
+"""Python access to the plain CPU oracle (moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use this module; the product path never imports it.  It
+shares no code with the HIP library.
+
+All arguments are CPU torch tensors (bf16 tensors are passed by their bits).
+Results come back as CPU tensors: logits fp32, weights and outputs fp64,
+indices int32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fp contraction: explicit fmaf only)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", "-Wall",
+             "-o", tmp, _SRC, "-lm"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32),
+        ("E", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("I", ctypes.c_int32),
+        ("w_gate_up", ctypes.c_void_p),
+        ("w_down", ctypes.c_void_p),
+        ("q_gate_up", ctypes.c_void_p),
+        ("s_gate_up", ctypes.c_void_p),
+        ("z_gate_up", ctypes.c_void_p),
+        ("q_down", ctypes.c_void_p),
+        ("s_down", ctypes.c_void_p),
+        ("z_down", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        lib.oracle_dot_r.restype = ctypes.c_float
+        lib.oracle_dot_r.argtypes = [P, P, I32]
+        lib.oracle_router_logits.restype = I32
+        lib.oracle_router_logits.argtypes = [P, I32, I32, P, P, I32, P]
+        lib.oracle_topk.restype = I32
+        lib.oracle_topk.argtypes = [P, I32, I32, I32, P, P]
+        lib.oracle_dispatch.restype = I32
+        lib.oracle_dispatch.argtypes = [P, I32, I32, I32, I32, P, P, P, P]
+        lib.oracle_expert_ffn.restype = I32
+        lib.oracle_expert_ffn.argtypes = [P, ctypes.POINTER(_Experts), I32, P]
+        lib.oracle_expert_matrix.restype = I32
+        lib.oracle_expert_matrix.argtypes = [ctypes.POINTER(_Experts), I32, I32, P]
+        layer = [P, I32, I32, P, P, I32, ctypes.POINTER(_Experts), P, P, I32]
+        lib.oracle_moe_ffn.restype = I32
+        lib.oracle_moe_ffn.argtypes = layer + [I32, I32, I32, P, I32, P, P, P]
+        lib.oracle_moe_ffn_monolith.restype = I32
+        lib.oracle_moe_ffn_monolith.argtypes = layer + [I32, P, I32, P]
+        _lib = lib
+    return _lib
+
+
+def _cpu(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    return t.detach().to("cpu").contiguous()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(rc: int, what: str):
+    if rc < 0:
+        raise ValueError(f"oracle: {what} rejected its arguments")
+    return rc
+
+
+class Experts:
+    """Holds CPU copies of routed expert weights and the ctypes descriptor."""
+
+    def __init__(self, experts: dict, E: int, H: int, I: int):
+        self.keep = {k: _cpu(v) for k, v in experts.items() if isinstance(v, torch.Tensor)}
+        fmt = experts["fmt"]
+        want = ({"w_gate_up": (2 * I, H), "w_down": (H, I)} if fmt == "bf16" else
+                {"q_gate_up": (2 * I, H // 2), "s_gate_up": (2 * I, H // 32), "z_gate_up": (2 * I, H // 32),
+                 "q_down": (H, I // 2), "s_down": (H, I // 32), "z_down": (H, I // 32)})
+        for name, shape in want.items():
+            t = self.keep.get(name)
+            if t is not None and (tuple(t.shape[1:]) != shape or t.shape[0] < E):
+                raise ValueError(f"oracle: {name} has shape {tuple(t.shape)}, want [{E}, {shape}]")
+        d = _Experts()
+        d.fmt = 0 if experts["fmt"] == "bf16" else 1
+        d.E, d.H, d.I = E, H, I
+        for name in ("w_gate_up", "w_down", "q_gate_up", "s_gate_up", "z_gate_up",
+                     "q_down", "s_down", "z_down"):
+            t = self.keep.get(name)
+            setattr(d, name, None if t is None else t.data_ptr())
+        self.desc = d
+
+
+def dot_r(x: torch.Tensor, w: torch.Tensor) -> float:
+    """The fixed-order fp32 router dot of two fp32 vectors (length % 256 == 0)."""
+    x, w = _cpu(x).float(), _cpu(w).float()
+    return float(_load().oracle_dot_r(_ptr(x), _ptr(w), x.numel()))
+
+
+def router_logits(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor]) -> torch.Tensor:
+    x, wr, b = _cpu(x), _cpu(router_w).float(), _cpu(bias)
+    T, H = x.shape
+    E = wr.shape[0]
+    out = torch.empty((T, E), dtype=torch.float32)
+    _check(_load().oracle_router_logits(_ptr(x), T, H, _ptr(wr), _ptr(b), E, _ptr(out)), "router")
+    return out
+
+
+def topk(logits: torch.Tensor, k: int):
+    lg = _cpu(logits).float()
+    T, E = lg.shape
+    ids = torch.empty((T, k), dtype=torch.int32)
+    w = torch.empty((T, k), dtype=torch.float64)
+    _check(_load().oracle_topk(_ptr(lg), T, E, k, _ptr(ids), _ptr(w)), "topk")
+    return ids, w
+
+
+def dispatch(ids: torch.Tensor, lo: int, hi: int):
+    """Returns (counts [nb], offsets [nb+1], perm [N_in], pos [T*k])."""
+    ids = _cpu(ids).to(torch.int32)
+    T, k = ids.shape
+    nb = hi - lo
+    counts = torch.empty(nb, dtype=torch.int32)
+    offsets = torch.empty(nb + 1, dtype=torch.int32)
+    perm = torch.empty(max(T * k, 1), dtype=torch.int32)
+    pos = torch.empty(max(T * k, 1), dtype=torch.int32)
+    n = _check(_load().oracle_dispatch(_ptr(ids), T, k, lo, hi, _ptr(counts), _ptr(offsets),
+                                       _ptr(perm), _ptr(pos)), "dispatch")
+    return counts, offsets, perm[:n].clone(), pos[: T * k].clone()
+
+
+def expert_ffn(x_row: torch.Tensor, experts: Experts, e: int) -> torch.Tensor:
+    """One expert's SwiGLU FFN on one fp64 row."""
+    xd = _cpu(x_row).to(torch.float64)
+    y = torch.empty(experts.desc.H, dtype=torch.float64)
+    _check(_load().oracle_expert_ffn(_ptr(xd), ctypes.byref(experts.desc), e, _ptr(y)), "expert_ffn")
+    return y
+
+
+def expert_matrix(experts: Experts, e: int, which: int) -> torch.Tensor:
+    """Dequantised fp64 weights of expert e: which=0 gate/up [2I,H], 1 down [H,I]."""
+    d = experts.desc
+    shape = (2 * d.I, d.H) if which == 0 else (d.H, d.I)
+    out = torch.empty(shape, dtype=torch.float64)
+    _check(_load().oracle_expert_matrix(ctypes.byref(d), e, which, _ptr(out)), "expert_matrix")
+    return out
+
+
+def moe_ffn(inputs: dict, E: int, I: int, Is: int, lo: int, hi: int, k: int,
+            rows: Optional[torch.Tensor] = None, experts: Optional[Experts] = None):
+    """The layer for the band [lo, hi) on the listed rows (all rows if None).
+    Returns (out fp64 [nrows, H], ids int32 [nrows, k], w fp64 [nrows, k])."""
+    x, wr, b = _cpu(inputs["x"]), _cpu(inputs["router_w"]).float(), _cpu(inputs["bias"])
+    T, H = x.shape
+    ex = experts if experts is not None else Experts(inputs["experts"], E, H, I)
+    sh = inputs.get("shared")
+    sgu = _cpu(sh["w_gate_up"]) if sh else None
+    sd = _cpu(sh["w_down"]) if sh else None
+    r = None if rows is None else _cpu(rows).to(torch.int32)
+    nrows = T if r is None else r.numel()
+    out = torch.empty((nrows, H), dtype=torch.float64)
+    ids = torch.empty((nrows, k), dtype=torch.int32)
+    w = torch.empty((nrows, k), dtype=torch.float64)
+    # The router's expert count comes from the router weight itself; the
+    # experts' from their descriptor -- the oracle rejects a mismatch.
+    Er = wr.shape[0]
+    if b is not None and b.numel() != Er:
+        raise ValueError("oracle: bias length != router experts")
+    _check(_load().oracle_moe_ffn(_ptr(x), T, H, _ptr(wr), _ptr(b), Er, ctypes.byref(ex.desc),
+                                  _ptr(sgu), _ptr(sd), Is if sh else 0, lo, hi, k, _ptr(r), nrows,
+                                  _ptr(out), _ptr(ids), _ptr(w)), "moe_ffn")
+    return out, ids, w
+
+
+def moe_ffn_monolith(inputs: dict, E: int, I: int, Is: int, k: int,
+                     rows: Optional[torch.Tensor] = None, experts: Optional[Experts] = None):
+    """The routed layer with no band logic (every pick contributes)."""
+    x, wr, b = _cpu(inputs["x"]), _cpu(inputs["router_w"]).float(), _cpu(inputs["bias"])
+    T, H = x.shape
+    ex = experts if experts is not None else Experts(inputs["experts"], E, H, I)
+    sh = inputs.get("shared")
+    sgu = _cpu(sh["w_gate_up"]) if sh else None
+    sd = _cpu(sh["w_down"]) if sh else None
+    r = None if rows is None else _cpu(rows).to(torch.int32)
+    nrows = T if r is None else r.numel()
+    out = torch.empty((nrows, H), dtype=torch.float64)
+    Er = wr.shape[0]
+    if b is not None and b.numel() != Er:
+        raise ValueError("oracle: bias length != router experts")
+    _check(_load().oracle_moe_ffn_monolith(_ptr(x), T, H, _ptr(wr), _ptr(b), Er, ctypes.byref(ex.desc),
+                                           _ptr(sgu), _ptr(sd), Is if sh else 0, k, _ptr(r), nrows,
+                                           _ptr(out)), "moe_ffn_monolith")
+    return out
