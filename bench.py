@@ -1,0 +1,213 @@
+"""Benchmark of one routed MoE FFN layer on one MI355X.
+
+A step is one call of the whole layer (router, top-k, dispatch, gate/up +
+SwiGLU, down, combine + shared expert) over one batch of synthetic rows whose
+inputs and weights are already resident in HBM.  Before every step a 1 GiB
+scratch write evicts the L2 and the MALL, so every step reads its weights from
+HBM; the layer's own time per step is measured with HIP events recorded by
+the library on the launch stream (the eviction is outside it).
+
+Prints one JSON line: rows/s, us per layer, the dominant kernel's roofline
+fraction (measured live with the same events) and the oracle timed on the
+host cores on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE FFN rows/s + µs/layer; decode % HBM roofline, prefill % bf16 MFMA peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+class Hip:
+    """hipEvent helpers through ctypes (events recorded by the library)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.lib.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return float(ms.value)
+
+
+def roofline_for(w, counts, stage_ms, synth):
+    """Dominant kernel and its algorithmic bytes or flops per launch.
+
+    Decode-sized batches (every group on the GEMV path): the gate/up GEMV
+    launch, which streams each touched expert's fused gate/up weights once
+    (2*I*H*2 bytes per bf16 expert; codes + scales + zeros for 4-bit) plus the
+    shared expert's, the rows of x and the bf16 intermediate it writes.
+    Prefill-sized batches: the gate/up MFMA launch, 2*(2I)*H flops per row of
+    each group on that path."""
+    n_touched = int((counts > 0).sum())
+    if w.T <= 8:
+        if w.fmt == "bf16":
+            per_expert = 2 * w.I * w.H * 2
+        else:
+            per_expert = 2 * w.I * (w.H // 2) + 2 * 2 * w.I * (w.H // 32) * 2
+        sh = 2 * w.Is * w.H * 2 if w.Is else 0
+        act = w.T * w.H * 2 + int(counts.sum()) * w.I * 2 + (w.T * w.Is * 2 if w.Is else 0)
+        traffic = n_touched * per_expert + sh + act
+        ms = stage_ms["gu_gemv"]
+        achieved = traffic / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": "gateup_gemv_kernel", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "algorithmic_bytes": traffic, "touched_experts": n_touched,
+                "kernel_us": round(ms * 1e3, 2)}
+    rows_mfma = int(counts[counts > 8].sum()) + (w.T if w.Is else 0)
+    flops = 2.0 * rows_mfma * 2 * w.I * w.H
+    ms = stage_ms["gu_mfma"]
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": "expert_mfma_kernel<gate/up>", "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops": flops, "kernel_us": round(ms * 1e3, 2)}
+
+
+def cpu_baseline(w, d, ex, rows_budget):
+    """The oracle, as it stands, on a bounded sample of rows of the workload."""
+    import torch
+
+    from oracle import oracle as orc
+
+    rows = list(range(min(w.T, rows_budget)))
+    need = sorted({int(e) for e in ex["topk_ids"][: len(rows)].flatten().tolist()})
+    experts = {"fmt": d["experts"]["fmt"]}
+    for name, t in d["experts"].items():
+        if isinstance(t, torch.Tensor):
+            experts[name] = torch.empty(t.shape, dtype=t.dtype)
+            for e in need:
+                experts[name][e].copy_(t[e])
+    inputs = {"x": d["x"].cpu(), "router_w": d["router_w"].cpu(),
+              "bias": None if d["bias"] is None else d["bias"].cpu(), "experts": experts,
+              "shared": None if d["shared"] is None else {k: v.cpu() for k, v in d["shared"].items()}}
+    ex_o = orc.Experts(experts, w.E, w.H, w.I)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    orc.moe_ffn(inputs, w.E, w.I, w.Is, w.band_lo, w.band_hi, w.topk,
+                rows=torch.tensor(rows, dtype=torch.int32), experts=ex_o)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 3), "unit": "rows/s", "cores": min(threads, len(rows)),
+            "threads_available": threads, "kind": "oracle",
+            "sample": f"rows 0..{len(rows) - 1} of the {w.name} workload (fp64 per-row oracle, "
+                      f"OpenMP over rows), {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict L2/MALL between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the layer's expert bands are run one after another on one GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_ffn_06_amd as moe
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    d = synth.make_inputs(w, dev)
+    torch.cuda.synchronize()
+    print(f"inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev)
+    out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+    ws = torch.empty((moe.workspace_bytes(w.T, w.H, w.E, w.I, w.Is, w.topk,
+                                          0 if w.fmt == "bf16" else 1),), dtype=torch.uint8, device=dev)
+    flush = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    ev = [hip.events(moe.MOE_NUM_EVENTS) for _ in range(args.steps)]
+    ex = {}
+
+    def step(events=None, exports=None):
+        if not args.no_flush:
+            flush.fill_(1)
+        moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
+                    w.band_hi, w.topk, out=out, workspace=ws, events=events, exports=exports)
+
+    step(exports=ex)  # also exports the routing, for the roofline bookkeeping
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events=ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = moe.EVENT_SLOTS
+    stage = {n: 0.0 for n in names[:-1]}
+    layer_ms = []
+    for i in range(args.steps):
+        for s in range(len(names) - 1):
+            stage[names[s]] += hip.elapsed_ms(ev[i][s], ev[i][s + 1]) / args.steps
+        layer_ms.append(hip.elapsed_ms(ev[i][0], ev[i][-1]))
+    ms = sum(layer_ms) / len(layer_ms)
+    counts = ex["counts"].cpu()
+    roof = roofline_for(w, counts, stage, synth)
+
+    line = {
+        "metric": METRIC,
+        "value": round(w.T / (ms * 1e-3), 2),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "us_per_layer": round(ms * 1e3, 2),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.fmt == "bf16" else "w4a16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "topk": w.topk, "I": w.I,
+                   "Is": w.Is, "fmt": w.fmt, "band": [w.band_lo, w.band_hi],
+                   "l2_mall_evicted_each_step": not args.no_flush},
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, d, ex, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

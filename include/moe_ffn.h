@@ -1,0 +1,191 @@
+/*
+ * moe_ffn.h -- C ABI of libmoeffn.so: one routed mixture-of-experts FFN layer,
+ * restricted to an expert band, on an AMD Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows (titles as published):
+ *   [P1] "GLM-5.2 multi-GPU: expert-parallel sharding + the resident-fit
+ *        benchmark" -- "What landed": experts partitioned into contiguous
+ *        bands, a replicated router picking the same top-k on every rank,
+ *        each rank contributing only the picks it owns, per-rank [H] residual
+ *        partials; the gates table (band of one rank == routed monolith,
+ *        fail-closed plan checks, shared-expert wrapper).
+ *   [P2] "GLM-5.3-Flash on CUDA: attention on one GPU, routed experts on the
+ *        Sparks (proposal) #214" -- "Per MoE layer": rows go to the expert
+ *        side with their top-k ids and weights, partials are summed in rank
+ *        order, the shared expert runs alongside.
+ *   [P4] "GLM-5.3-Flash on CUDA over three ranks (--tp 3) ... #310" --
+ *        fp32 partial rows summed in a fixed order.
+ *   [P5] "GLM-5.3-Flash and full GLM-5.3 on the native CUDA engine (tracker)
+ *        #593" -- fused gate/up rows 2w wide; W4A16 checkpoints; device
+ *        grouping plan byte-equal to the host routing.
+ *
+ * What one call computes (for the band [band_lo, band_hi) of the E experts):
+ *   1. router logits l[t,e] = dot(x[t,:], Wr[e,:]) + bias[e] in fp32, for ALL
+ *      E experts whatever the band ([P1]: the router runs replicated), summed
+ *      in a fixed order (64 lane partials over k = 256 i + 4 l + c, i outer,
+ *      c inner, fused multiply-adds from +0.0, then six pairwise rounds
+ *      l xor 1, 2, 4, 8, 16, 32), -0.0 normalised to +0.0;
+ *   2. top-k: experts ordered by (logit descending, id ascending), the first
+ *      topk in that pick order; weights w_j = exp(l_j - l_0) / sum_i exp(l_i -
+ *      l_0) over the picks (softmax renormalised over the picks);
+ *   3. dispatch of the in-band picks by expert (counts, offsets, a stable
+ *      permutation ascending in row, and its inverse);
+ *   4. per in-band expert: h = silu(x W_gate^T) * (x W_up^T), y = h W_down^T
+ *      (SwiGLU; silu(g) = g / (1 + exp(-g)));
+ *   5. out[t,:] = sum over picks j in pick order with the expert in the band
+ *      of w_j * y_j, accumulated in fp32 from +0.0, then + the shared
+ *      expert's output (weight 1) when `shared` is not NULL.
+ * The full band [0, E) gives the whole layer (the routed monolith plus the
+ * shared expert).  Summing the outputs of consecutive bands in band order
+ * gives the whole layer up to fp32 reassociation.
+ *
+ * Memory: every pointer is device memory owned by the caller, contiguous
+ * row-major, 16-byte aligned.  The library never allocates device memory and
+ * keeps no mutable global state; scratch lives in the caller's workspace.
+ * Execution: all work is enqueued asynchronously on `stream`; nothing is
+ * copied back to the host and nothing waits for the GPU.  Calls on different
+ * streams need different workspaces.
+ * Errors: every argument check runs before the first enqueue; on error
+ * nothing is enqueued and no output is written ([P1] gates table:
+ * fail-closed).  Runs are bit-identical from call to call for the same
+ * inputs (no floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOE_OK 0
+#define MOE_E_NULL (-1)      /* a required pointer is NULL */
+#define MOE_E_SHAPE (-2)     /* T < 1 or too large; H differs between arguments; H % 256 != 0;
+                                I or Is not a positive multiple of 64; E > MOE_MAX_E */
+#define MOE_E_DIM (-3)       /* router E != experts E ([P1]: plan.Dim != NumExperts) */
+#define MOE_E_BAND (-4)      /* band_lo < 0, band_hi > E or band_lo >= band_hi */
+#define MOE_E_TOPK (-5)      /* topk < 1, topk > E or topk > MOE_MAX_TOPK */
+#define MOE_E_FORMAT (-6)    /* unknown weight format, or 4-bit group size != 32 */
+#define MOE_E_WORKSPACE (-7) /* workspace NULL or smaller than moe_ffn_workspace_bytes() */
+#define MOE_E_ALIGN (-8)     /* a pointer is not 16-byte aligned */
+#define MOE_E_HIP (-9)       /* the HIP runtime reported an error while enqueuing */
+#define MOE_E_DEVICE (-10)   /* the current device is not a gfx950 GPU */
+
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_E 1024
+#define MOE_MAX_T (1 << 20)
+
+/* Expert weight formats. */
+#define MOE_BF16 0  /* bf16 weights */
+#define MOE_W4A16 1 /* 4-bit unsigned codes, bf16 scale and zero per 32 inputs */
+
+/* Rows: x is bf16 [T, H]. */
+typedef struct moe_x {
+    const void* ptr; /* bf16 [T, H] */
+    int32_t T, H;
+} moe_x;
+
+/* Router: fp32 gate weight [E, H] and an optional fp32 per-expert bias [E]
+ * added to the logits before selection and weighting. */
+typedef struct moe_router {
+    const float* w;    /* fp32 [E, H] */
+    const float* bias; /* fp32 [E] or NULL */
+    int32_t E, H;
+} moe_router;
+
+/* Routed experts, all E of them (the band selects which ones run).
+ * MOE_BF16:  w_gate_up bf16 [E, 2I, H] -- rows 0..I-1 are the gate
+ *            projection, rows I..2I-1 the up projection ([P5]: the fused
+ *            gate/up rows are 2w wide); w_down bf16 [E, H, I].
+ * MOE_W4A16: q_gate_up uint8 [E, 2I, H/2], s_gate_up and z_gate_up bf16
+ *            [E, 2I, H/32]; q_down uint8 [E, H, I/2], s_down and z_down bf16
+ *            [E, H, I/32].  Two 4-bit unsigned codes per byte, the even input
+ *            index in the low nibble; weight = (code - zero) * scale with one
+ *            (scale, zero) per 32 consecutive inputs ([P5] "The pieces, in
+ *            order": W4A16 checkpoints).  Unused pointers of the other format
+ *            are ignored. */
+typedef struct moe_experts {
+    int32_t E, H, I;
+    int32_t fmt;   /* MOE_BF16 or MOE_W4A16 */
+    int32_t group; /* 32 for MOE_W4A16; ignored for MOE_BF16 */
+    const void* w_gate_up;
+    const void* w_down;
+    const uint8_t* q_gate_up;
+    const void* s_gate_up;
+    const void* z_gate_up;
+    const uint8_t* q_down;
+    const void* s_down;
+    const void* z_down;
+} moe_experts;
+
+/* Shared expert (unrouted, weight 1, every row): bf16 w_gate_up [2Is, H]
+ * (gate rows first), w_down [H, Is]. */
+typedef struct moe_shared {
+    int32_t Is, H;
+    const void* w_gate_up;
+    const void* w_down;
+} moe_shared;
+
+/* Event slots recorded on the stream when moe_out.stage_events is set: slot
+ * s is recorded just before stage s is enqueued (also when the stage has no
+ * work for this call), and slot MOE_EV_END after the last stage. */
+#define MOE_EV_ROUTER 0   /* router logits */
+#define MOE_EV_TOPK 1     /* top-k and weights */
+#define MOE_EV_DISPATCH 2 /* histogram, scan, permutation, tile lists */
+#define MOE_EV_GU_GEMV 3  /* gate/up + SwiGLU, groups of <= 8 rows */
+#define MOE_EV_GU_MFMA 4  /* gate/up + SwiGLU, groups of > 8 rows (MFMA) */
+#define MOE_EV_DN_GEMV 5  /* down projection, groups of <= 8 rows */
+#define MOE_EV_DN_MFMA 6  /* down projection, groups of > 8 rows (MFMA) */
+#define MOE_EV_COMBINE 7  /* weighted sum in pick order + shared */
+#define MOE_EV_END 8
+#define MOE_NUM_EVENTS 9
+
+/* Outputs.  y is required and fully overwritten (rows with no in-band pick
+ * and no shared expert become +0.0).  The other outputs are optional exports
+ * of the routing and dispatch (NULL = not exported):
+ *   topk_ids int32 [T, topk] and topk_w fp32 [T, topk], in pick order;
+ *   counts int32 [nb], offsets int32 [nb + 1] (nb = band_hi - band_lo);
+ *   perm int32 [T*topk]: entries 0..N_in-1 hold t*topk + j of the in-band
+ *        picks grouped by expert (band order), rows ascending within an
+ *        expert; entries past N_in = offsets[nb] are left unspecified;
+ *   pos int32 [T*topk]: the index of pick t*topk + j in perm, or -1 when the
+ *        pick is outside the band.
+ * workspace: device scratch of at least moe_ffn_workspace_bytes() bytes.
+ * stage_events: NULL, or MOE_NUM_EVENTS hipEvent_t handles (created by the
+ *        caller) recorded at the stage boundaries, for timing. */
+typedef struct moe_out {
+    float* y; /* fp32 [T, H] */
+    int32_t* topk_ids;
+    float* topk_w;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* pos;
+    void* workspace;
+    size_t workspace_bytes;
+    void* const* stage_events;
+} moe_out;
+
+/* Run the layer for the band [band_lo, band_hi) on `stream` (a hipStream_t;
+ * NULL = the null stream).  shared may be NULL.  Returns MOE_OK or a
+ * negative MOE_E_* code. */
+int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
+                const moe_shared* shared, int32_t band_lo, int32_t band_hi, int32_t topk,
+                const moe_out* out, void* stream);
+
+/* Workspace bytes a call with these sizes needs (Is = 0: no shared expert).
+ * Returns 0 for sizes moe_ffn would reject. */
+size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t I, int32_t Is,
+                               int32_t topk, int32_t fmt);
+
+/* A static, human-readable message for a return code. */
+const char* moe_ffn_strerror(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

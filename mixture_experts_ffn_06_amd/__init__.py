@@ -1,0 +1,189 @@
+"""Python binding of libmoeffn.so: one routed mixture-of-experts FFN layer,
+restricted to an expert band, on an MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoeffn.so.  torch supplies device memory and the stream.  The binding fails
+loudly when the library is not built; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoeffn.so")
+
+MOE_BF16 = 0
+MOE_W4A16 = 1
+MOE_MAX_TOPK = 16
+MOE_MAX_E = 1024
+MOE_NUM_EVENTS = 9
+EVENT_SLOTS = ("router", "topk", "dispatch", "gu_gemv", "gu_mfma", "dn_gemv", "dn_mfma",
+               "combine", "end")
+
+ERRORS = {
+    0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_DIM", -4: "MOE_E_BAND",
+    -5: "MOE_E_TOPK", -6: "MOE_E_FORMAT", -7: "MOE_E_WORKSPACE", -8: "MOE_E_ALIGN",
+    -9: "MOE_E_HIP", -10: "MOE_E_DEVICE",
+}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+
+
+class MoeX(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("T", ctypes.c_int32), ("H", ctypes.c_int32)]
+
+
+class MoeRouter(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("E", ctypes.c_int32),
+                ("H", ctypes.c_int32)]
+
+
+class MoeExperts(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("fmt", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("q_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
+                ("z_gate_up", ctypes.c_void_p), ("q_down", ctypes.c_void_p),
+                ("s_down", ctypes.c_void_p), ("z_down", ctypes.c_void_p)]
+
+
+class MoeShared(ctypes.Structure):
+    _fields_ = [("Is", ctypes.c_int32), ("H", ctypes.c_int32), ("w_gate_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p)]
+
+
+class MoeOut(ctypes.Structure):
+    _fields_ = [("y", ctypes.c_void_p), ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stage_events", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmoeffn.so; raises when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(-9, f"{LIB_PATH} is not built; run `python -m mixture_experts_ffn_06_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I32 = ctypes.c_void_p, ctypes.c_int32
+        lib.moe_ffn.restype = I32
+        lib.moe_ffn.argtypes = [ctypes.POINTER(MoeX), ctypes.POINTER(MoeRouter),
+                                ctypes.POINTER(MoeExperts), ctypes.POINTER(MoeShared), I32, I32,
+                                I32, ctypes.POINTER(MoeOut), P]
+        lib.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
+        lib.moe_ffn_workspace_bytes.argtypes = [I32] * 7
+        lib.moe_ffn_strerror.restype = ctypes.c_char_p
+        lib.moe_ffn_strerror.argtypes = [I32]
+        _lib = lib
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return load_library().moe_ffn_strerror(code).decode()
+
+
+def workspace_bytes(T: int, H: int, E: int, I: int, Is: int, topk: int, fmt: int = MOE_BF16) -> int:
+    return int(load_library().moe_ffn_workspace_bytes(T, H, E, I, Is, topk, fmt))
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _fmt_code(experts: dict) -> int:
+    return MOE_BF16 if experts["fmt"] == "bf16" else MOE_W4A16
+
+
+def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None):
+    """ctypes descriptors for the tensors (no copies, no checks: the library checks)."""
+    T, H = x.shape
+    fmt = _fmt_code(experts)
+    if E is None:
+        E = (experts["w_gate_up"] if fmt == MOE_BF16 else experts["q_gate_up"]).shape[0]
+    if I is None:
+        I = (experts["w_gate_up"] if fmt == MOE_BF16 else experts["q_gate_up"]).shape[1] // 2
+    dx = MoeX(_p(x), T, H)
+    dr = MoeRouter(_p(router_w), _p(bias), router_w.shape[0], router_w.shape[1])
+    de = MoeExperts(E, H, I, fmt, 32 if fmt == MOE_W4A16 else 0,
+                    _p(experts.get("w_gate_up")), _p(experts.get("w_down")),
+                    _p(experts.get("q_gate_up")), _p(experts.get("s_gate_up")),
+                    _p(experts.get("z_gate_up")), _p(experts.get("q_down")),
+                    _p(experts.get("s_down")), _p(experts.get("z_down")))
+    ds = None
+    if shared is not None:
+        ds = MoeShared(shared["w_down"].shape[1], shared["w_gate_up"].shape[1],
+                       _p(shared["w_gate_up"]), _p(shared["w_down"]))
+    return dx, dr, de, ds
+
+
+def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor], experts: dict,
+            shared: Optional[dict], band_lo: int, band_hi: int, topk: int,
+            out: Optional[torch.Tensor] = None, exports: Optional[dict] = None,
+            workspace: Optional[torch.Tensor] = None, stream=None, events=None) -> torch.Tensor:
+    """Run the layer for the expert band [band_lo, band_hi).
+
+    x bf16 [T,H]; router_w fp32 [E,H]; bias fp32 [E] or None; experts / shared
+    as produced by the synth module (dicts of device tensors).  Returns the fp32
+    [T,H] partial residual (`out` if given).  `exports`, if a dict, receives
+    topk_ids, topk_w, counts, offsets, perm, pos.  `events` is a list of
+    MOE_NUM_EVENTS raw hipEvent_t handles recorded at the stage boundaries.
+    """
+    lib = load_library()
+    T, H = x.shape
+    dx, dr, de, ds = make_descriptors(x, router_w, bias, experts, shared)
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ex = {}
+    if exports is not None:
+        nb = band_hi - band_lo
+        ex = {
+            "topk_ids": torch.empty((T, topk), dtype=torch.int32, device=dev),
+            "topk_w": torch.empty((T, topk), dtype=torch.float32, device=dev),
+            "counts": torch.empty((max(nb, 1),), dtype=torch.int32, device=dev),
+            "offsets": torch.empty((max(nb, 0) + 1,), dtype=torch.int32, device=dev),
+            "perm": torch.empty((T * topk,), dtype=torch.int32, device=dev),
+            "pos": torch.empty((T * topk,), dtype=torch.int32, device=dev),
+        }
+    if workspace is None:
+        nbytes = lib.moe_ffn_workspace_bytes(T, H, de.E, de.I, ds.Is if ds else 0, topk, de.fmt)
+        workspace = torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=dev)
+    ev_arr = None
+    if events is not None:
+        ev_arr = (ctypes.c_void_p * MOE_NUM_EVENTS)(*events)
+    dout = MoeOut(_p(out), _p(ex.get("topk_ids")), _p(ex.get("topk_w")), _p(ex.get("counts")),
+                  _p(ex.get("offsets")), _p(ex.get("perm")), _p(ex.get("pos")),
+                  _p(workspace), workspace.numel(),
+                  ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    if stream is None:
+        st = torch.cuda.current_stream(dev).cuda_stream if dev.type == "cuda" else 0
+    else:
+        st = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    rc = lib.moe_ffn(ctypes.byref(dx), ctypes.byref(dr), ctypes.byref(de),
+                     ctypes.byref(ds) if ds is not None else None, band_lo, band_hi, topk,
+                     ctypes.byref(dout), ctypes.c_void_p(st))
+    if rc != 0:
+        raise MoeError(rc, strerror(rc))
+    if exports is not None:
+        exports.update(ex)
+    return out
+
+
+__all__ = ["moe_ffn", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
+           "MOE_BF16", "MOE_W4A16", "MOE_NUM_EVENTS", "EVENT_SLOTS", "make_descriptors",
+           "MoeX", "MoeRouter", "MoeExperts", "MoeShared", "MoeOut"]

@@ -1,0 +1,122 @@
+// common.h -- device helpers and the internal plan shared by the kernels of
+// libmoeffn.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+// Groups of at most this many rows take the bandwidth-bound GEMV path; larger
+// groups take the MFMA path.
+constexpr int kSmallRows = 8;
+// MFMA tile: rows of the group x weight rows x reduction depth.
+constexpr int kBM = 128;
+constexpr int kBN = 128;
+constexpr int kBK = 64;
+// GEMV work items: gate/up covers 16 intermediate columns (16 gate + 16 up
+// weight rows), down covers 64 output columns.
+constexpr int kGuCols = 16;
+constexpr int kDnCols = 64;
+// Rows per dispatch block (four waves of 64 rows).
+constexpr int kDispatchRows = 256;
+
+// One expert group of the dispatch: a routed expert of the band (expert >= 0)
+// or the shared expert (expert == -1).
+struct Group {
+    int32_t expert;  // global expert id, or -1 for the shared expert
+    int32_t row0;    // first row of the group in perm order (0 for the shared expert)
+    int32_t n;       // rows in the group
+    int32_t pad;
+};
+
+// Pointers and sizes every expert kernel needs.  Built on the host per call.
+struct ExpertArgs {
+    // rows
+    const uint16_t* x;  // bf16 [T, H]
+    int32_t T, H, topk;
+    // routed experts
+    int32_t I;
+    int32_t fmt;                // 0 bf16, 1 w4
+    const uint16_t* wgu;        // bf16 [E, 2I, H]
+    const uint16_t* wd;         // bf16 [E, H, I]
+    const uint8_t* qgu;         // [E, 2I, H/2]
+    const uint16_t* sgu;        // [E, 2I, H/32]
+    const uint16_t* zgu;
+    const uint8_t* qd;          // [E, H, I/2]
+    const uint16_t* sd;         // [E, H, I/32]
+    const uint16_t* zd;
+    // shared expert (bf16)
+    int32_t Is;
+    const uint16_t* swgu;       // [2Is, H]
+    const uint16_t* swd;        // [H, Is]
+    // plan (device, written by the dispatch)
+    const Group* groups;        // [nb + 1]
+    const int32_t* gemv_list;   // group indices on the GEMV path
+    const int32_t* mfma_list;   // (group, m0) pairs on the MFMA path
+    const int32_t* plan_counts; // [0] = GEMV groups, [1] = MFMA tiles
+    const int32_t* perm;        // [T*topk]
+    // scratch
+    uint16_t* h_r;  // bf16 [T*topk, I]  (perm order)
+    uint16_t* h_s;  // bf16 [T, Is]
+    float* y_r;     // fp32 [T*topk, H] (perm order)
+    float* y_s;     // fp32 [T, H]
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (hardware convert on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g / (1.0f + __expf(-g)) * u;
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + a.lo*b.lo + a.hi*b.hi with a, b packed bf16 pairs.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Sum over the 64 lanes of a wave (fixed butterfly; every lane gets the sum).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) v += __shfl_xor(v, s, 64);
+    return v;
+}
+
+// Allow a kernel more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
+template <typename F>
+inline void allow_lds(F* kernel, size_t bytes) {
+    if (bytes > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+// Host-side launchers (one per kernel family).
+void launch_router_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H,
+                          int E, float* logits, hipStream_t st);
+void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t st);
+void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_shared,
+                     int32_t* blkcnt, int32_t* counts, int32_t* offsets, int32_t* perm,
+                     int32_t* pos, Group* groups, int32_t* gemv_list, int32_t* mfma_list,
+                     int32_t* plan_counts, hipStream_t st);
+void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
+void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
+void launch_gateup_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
+void launch_down_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
+void launch_combine(const float* y_r, const float* y_s, const int32_t* pos, const float* w,
+                    int T, int H, int k, float* out, hipStream_t st);
+
+}  // namespace moe

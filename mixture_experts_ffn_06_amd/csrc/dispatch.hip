@@ -1,0 +1,191 @@
+// dispatch.hip -- group the in-band picks by expert: histogram, prefix sum,
+// a stable permutation (rows ascending within an expert) and its inverse,
+// plus the work lists of the expert kernels.  Integer only: the result does
+// not depend on scheduling, and it matches a host grouping byte for byte.
+//
+// [P1] "GLM-5.2 multi-GPU: expert-parallel sharding + the resident-fit
+// benchmark", "What landed": each rank contributes only the picks it owns;
+// its lever table: batched expert dispatch (one grouped call instead of a
+// loop over experts).  [P5] "GLM-5.3-Flash and full GLM-5.3 on the native
+// CUDA engine (tracker) #593": the device grouping plan is byte-equal to the
+// host routing.
+//
+// Method: rows are cut into blocks of 256 (four waves of 64 rows).  In each
+// wave, bit r of mask[e] is set when row r picked expert e (LDS integer
+// atomics: the result does not depend on their order).  A pick's slot is the
+// expert's offset + the picks of earlier blocks (scanned in block order) + the
+// picks of earlier waves of the block + popcount(mask[e] below row r).
+#include "common.h"
+
+namespace moe {
+
+__device__ __forceinline__ void build_masks(unsigned long long* masks, const int32_t* ids, int T,
+                                            int k, int lo, int nb) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 4 * nb; i += blockDim.x) masks[i] = 0ull;
+    __syncthreads();
+    const int t = blockIdx.x * kDispatchRows + tid;
+    const int wave = tid >> 6, lane = tid & 63;
+    if (t < T) {
+        for (int j = 0; j < k; ++j) {
+            int e = ids[(size_t)t * k + j] - lo;
+            if (e >= 0 && e < nb) atomicOr(&masks[wave * nb + e], 1ull << lane);
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ ids,
+                                                             int T, int k, int lo, int nb,
+                                                             int32_t* __restrict__ blkcnt) {
+    extern __shared__ unsigned long long masks[];
+    build_masks(masks, ids, T, k, lo, nb);
+    for (int e = threadIdx.x; e < nb; e += blockDim.x) {
+        int c = __popcll(masks[e]) + __popcll(masks[nb + e]) + __popcll(masks[2 * nb + e]) +
+                __popcll(masks[3 * nb + e]);
+        blkcnt[(size_t)blockIdx.x * nb + e] = c;
+    }
+}
+
+// Exclusive scan over the 1024 threads of a block (fixed order, deterministic).
+__device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int o = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) s_tmp[wave] = inc;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int w = 0; w < 16; ++w) {
+            int c = s_tmp[w];
+            s_tmp[w] = run;
+            run += c;
+        }
+        s_tmp[16] = run;
+    }
+    __syncthreads();
+    int res = s_tmp[wave] + inc - v;
+    *total = s_tmp[16];
+    __syncthreads();
+    return res;
+}
+
+// One block of 1024 threads; thread i owns groups 2i and 2i+1 (group nb is the
+// shared expert when present).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    int nblk, int nb, int T, bool has_shared, int32_t* __restrict__ blkcnt,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, Group* __restrict__ groups,
+    int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list,
+    int32_t* __restrict__ plan_counts, int lo) {
+    __shared__ int s_tmp[17];
+    const int tid = threadIdx.x;
+    int cnt[2], run[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        int r = 0;
+        if (e < nb) {
+            for (int b = 0; b < nblk; ++b) {
+                int c = blkcnt[(size_t)b * nb + e];
+                blkcnt[(size_t)b * nb + e] = r;
+                r += c;
+            }
+        }
+        cnt[q] = r;
+    }
+    int total;
+    int off0 = block_exclusive_scan(cnt[0] + cnt[1], s_tmp, &total);
+    run[0] = off0;
+    run[1] = off0 + cnt[0];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        if (e < nb) {
+            counts[e] = cnt[q];
+            offsets[e] = run[q];
+            for (int b = 0; b < nblk; ++b) blkcnt[(size_t)b * nb + e] += run[q];
+        }
+    }
+    if (tid == 0) offsets[nb] = total;
+
+    // Groups and work lists.
+    int n[2], gv[2], mt[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        n[q] = 0;
+        if (e < nb) {
+            n[q] = cnt[q];
+            groups[e] = Group{lo + e, run[q], cnt[q], 0};
+        } else if (e == nb && has_shared) {
+            n[q] = T;
+            groups[e] = Group{-1, 0, T, 0};
+        }
+        gv[q] = (n[q] >= 1 && n[q] <= kSmallRows) ? 1 : 0;
+        mt[q] = (n[q] > kSmallRows) ? (n[q] + kBM - 1) / kBM : 0;
+    }
+    int ngv, nmt;
+    int gv0 = block_exclusive_scan(gv[0] + gv[1], s_tmp, &ngv);
+    int mt0 = block_exclusive_scan(mt[0] + mt[1], s_tmp, &nmt);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        if (gv[q]) gemv_list[gv0] = e;
+        gv0 += gv[q];
+        for (int m = 0; m < mt[q]; ++m) {
+            mfma_list[2 * (mt0 + m)] = e;
+            mfma_list[2 * (mt0 + m) + 1] = m * kBM;
+        }
+        mt0 += mt[q];
+    }
+    if (tid == 0) {
+        plan_counts[0] = ngv;
+        plan_counts[1] = nmt;
+    }
+}
+
+__global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ ids,
+                                                             int T, int k, int lo, int nb,
+                                                             const int32_t* __restrict__ base,
+                                                             int32_t* __restrict__ perm,
+                                                             int32_t* __restrict__ pos) {
+    extern __shared__ unsigned long long masks[];
+    build_masks(masks, ids, T, k, lo, nb);
+    const int tid = threadIdx.x;
+    const int t = blockIdx.x * kDispatchRows + tid;
+    const int wave = tid >> 6, lane = tid & 63;
+    if (t >= T) return;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int j = 0; j < k; ++j) {
+        const int p = t * k + j;
+        int e = ids[p] - lo;
+        if (e >= 0 && e < nb) {
+            int slot = base[(size_t)blockIdx.x * nb + e];
+            for (int w = 0; w < wave; ++w) slot += __popcll(masks[w * nb + e]);
+            slot += __popcll(masks[wave * nb + e] & below);
+            perm[slot] = p;
+            pos[p] = slot;
+        } else {
+            pos[p] = -1;
+        }
+    }
+}
+
+void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_shared,
+                     int32_t* blkcnt, int32_t* counts, int32_t* offsets, int32_t* perm,
+                     int32_t* pos, Group* groups, int32_t* gemv_list, int32_t* mfma_list,
+                     int32_t* plan_counts, hipStream_t st) {
+    const int nb = hi - lo;
+    const int nblk = (T + kDispatchRows - 1) / kDispatchRows;
+    const size_t lds = sizeof(unsigned long long) * 4 * (size_t)nb;
+    dispatch_count_kernel<<<nblk, kDispatchRows, lds, st>>>(ids, T, k, lo, nb, blkcnt);
+    dispatch_scan_kernel<<<1, 1024, 0, st>>>(nblk, nb, T, has_shared, blkcnt, counts, offsets,
+                                             groups, gemv_list, mfma_list, plan_counts, lo);
+    dispatch_place_kernel<<<nblk, kDispatchRows, lds, st>>>(ids, T, k, lo, nb, blkcnt, perm, pos);
+}
+
+}  // namespace moe

@@ -1,0 +1,445 @@
+// gemv.hip -- bandwidth-bound expert projections for groups of 1..8 rows
+// (decode): gate/up with the SwiGLU epilogue fused, then the down projection.
+//
+// [P1] "GLM-5.2 multi-GPU: expert-parallel sharding + the resident-fit
+// benchmark", "Update (later 2026-06-29)": the per-expert expertSwiGLU;
+// [P5] "GLM-5.3-Flash and full GLM-5.3 on the native CUDA engine (tracker)
+// #593", "What exists now": fused gate/up rows are 2w wide (gate rows first
+// here); "The pieces, in order": W4A16 (4-bit weights, 16-bit activations).
+//
+// Layout of the work: a block of 8 waves owns one work item (16 intermediate
+// columns of one group for gate/up, 64 output columns for down) and keeps the
+// group's rows (at most 8) in LDS.  A wave streams whole weight rows (every
+// lane loads 16 contiguous bytes per step, so a step reads 1 KiB of one row),
+// multiplies them with all rows of the group, and reduces across lanes once
+// per weight row.  Blocks take contiguous runs of work items so the rows of a
+// group are staged once per block.
+//
+// 4-bit weights: (code - zero) * scale with (scale, zero) per 32 inputs.  One
+// lane step covers exactly one 32-input group: the codes are widened to the
+// bf16 values 128 + code with two bit operations per pair, dotted with the
+// rows (inputs stored pairwise-permuted in LDS to match the nibble order), and
+// the group contributes scale * (dot - (128 + zero) * sum(inputs)).
+#include "common.h"
+
+namespace moe {
+
+constexpr int kGemvThreads = 512;
+constexpr int kGemvWaves = kGemvThreads / 64;
+
+// Stage the rows of a group in LDS.  src_h: rows come from the intermediate
+// h (down projection), else from x (gate/up).  permute: store each 8 inputs as
+// (0,4),(1,5),(2,6),(3,7) pairs and the per-32 sums (4-bit path).
+__device__ void stage_rows(const ExpertArgs& a, const Group& g, bool src_h, int K, int nr,
+                           bool permute, uint16_t* xs, float* xsum) {
+    const bool shared = g.expert < 0;
+    const int c8n = K / 8;
+    for (int idx = threadIdx.x; idx < nr * c8n; idx += blockDim.x) {
+        const int r = idx / c8n, c8 = idx - r * c8n;
+        const uint16_t* src;
+        if (src_h)
+            src = shared ? a.h_s + (size_t)r * a.Is : a.h_r + (size_t)(g.row0 + r) * a.I;
+        else
+            src = a.x + (size_t)(shared ? r : a.perm[g.row0 + r] / a.topk) * a.H;
+        uint4 v = *reinterpret_cast<const uint4*>(src + 8 * c8);
+        if (permute) {
+            uint4 p;
+            p.x = (v.x & 0xffffu) | (v.z << 16);
+            p.y = (v.x >> 16) | (v.z & 0xffff0000u);
+            p.z = (v.y & 0xffffu) | (v.w << 16);
+            p.w = (v.y >> 16) | (v.w & 0xffff0000u);
+            v = p;
+        }
+        *reinterpret_cast<uint4*>(xs + (size_t)r * K + 8 * c8) = v;
+    }
+    if (permute) {
+        const int gn = K / 32;
+        for (int idx = threadIdx.x; idx < nr * gn; idx += blockDim.x) {
+            const int r = idx / gn, gi = idx - r * gn;
+            const uint16_t* src;
+            if (src_h)
+                src = shared ? a.h_s + (size_t)r * a.Is : a.h_r + (size_t)(g.row0 + r) * a.I;
+            else
+                src = a.x + (size_t)(shared ? r : a.perm[g.row0 + r] / a.topk) * a.H;
+            float s = 0.0f;
+            for (int q = 0; q < 32; ++q) s += bf16_bits_to_f32(src[32 * gi + q]);
+            xsum[r * gn + gi] = s;
+        }
+    }
+}
+
+// ---- dot helpers ---------------------------------------------------------
+
+// bf16 weights: 8 inputs per lane step.
+template <int NR>
+__device__ __forceinline__ void dot_step_bf16(const uint4& w, const uint16_t* xs, int K, int k,
+                                              float* acc) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k);
+        float s = acc[r];
+        s = dot2_bf16(w.x, xv.x, s);
+        s = dot2_bf16(w.y, xv.y, s);
+        s = dot2_bf16(w.z, xv.z, s);
+        s = dot2_bf16(w.w, xv.w, s);
+        acc[r] = s;
+    }
+}
+
+// 4-bit weights: 32 inputs (one group) per lane step.
+template <int NR>
+__device__ __forceinline__ void dot_step_w4(const uint4& q, float sc, float zz, const uint16_t* xs,
+                                            const float* xsum, int K, int k, float* acc) {
+    uint32_t qd[4] = {q.x, q.y, q.z, q.w};
+    float part[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) part[r] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t c = qd[d];
+        const uint32_t p0 = (c & 0x000f000fu) | 0x43004300u;
+        const uint32_t p1 = ((c >> 4) & 0x000f000fu) | 0x43004300u;
+        const uint32_t p2 = ((c >> 8) & 0x000f000fu) | 0x43004300u;
+        const uint32_t p3 = ((c >> 12) & 0x000f000fu) | 0x43004300u;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k + 8 * d);
+            float s = part[r];
+            s = dot2_bf16(p0, xv.x, s);
+            s = dot2_bf16(p1, xv.y, s);
+            s = dot2_bf16(p2, xv.z, s);
+            s = dot2_bf16(p3, xv.w, s);
+            part[r] = s;
+        }
+    }
+    const float z128 = 128.0f + zz;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r] += sc * (part[r] - z128 * xsum[r * (K / 32) + k / 32]);
+}
+
+// ---- gate/up ---------------------------------------------------------------
+
+// One work item: intermediate columns c0 .. c0+15 of group g; wave w owns
+// columns c0 + 2w and c0 + 2w + 1 (its gate row and its up row each).
+template <int W4, int NR>
+__device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const uint16_t* xs,
+                            const float* xsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool shared = g.expert < 0;
+    const int Ig = shared ? a.Is : a.I;
+    const int H = a.H;
+    for (int cc = 0; cc < 2; ++cc) {
+        const int c = c0 + 2 * wave + cc;
+        float ag[NR], au[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) ag[r] = au[r] = 0.0f;
+        if (!W4) {
+            const uint16_t* gr = shared ? a.swgu + (size_t)c * H
+                                        : a.wgu + ((size_t)g.expert * 2 * Ig + c) * H;
+            const uint16_t* ur = gr + (size_t)Ig * H;
+            constexpr int CB = 12;
+            const int nch = (H + 511) / 512;
+            for (int q0 = 0; q0 < nch; q0 += CB) {
+                uint4 wg[CB], wu[CB];
+#pragma unroll
+                for (int qq = 0; qq < CB; ++qq) {
+                    const int k = 512 * (q0 + qq) + 8 * lane;
+                    if (q0 + qq < nch && k < H) {
+                        wg[qq] = *reinterpret_cast<const uint4*>(gr + k);
+                        wu[qq] = *reinterpret_cast<const uint4*>(ur + k);
+                    }
+                }
+#pragma unroll
+                for (int qq = 0; qq < CB; ++qq) {
+                    const int k = 512 * (q0 + qq) + 8 * lane;
+                    if (q0 + qq < nch && k < H) {
+                        dot_step_bf16<NR>(wg[qq], xs, H, k, ag);
+                        dot_step_bf16<NR>(wu[qq], xs, H, k, au);
+                    }
+                }
+            }
+        } else {
+            const size_t grow = (size_t)g.expert * 2 * Ig + c, urow = grow + Ig;
+            const uint8_t* gq = a.qgu + grow * (H / 2);
+            const uint8_t* uq = a.qgu + urow * (H / 2);
+            const uint16_t* gs = a.sgu + grow * (H / 32);
+            const uint16_t* gz = a.zgu + grow * (H / 32);
+            const uint16_t* us = a.sgu + urow * (H / 32);
+            const uint16_t* uz = a.zgu + urow * (H / 32);
+            constexpr int CB = 4;
+            const int nch = (H + 2047) / 2048;
+            for (int q0 = 0; q0 < nch; q0 += CB) {
+                uint4 qg[CB], qu[CB];
+                uint32_t sg[CB], zg[CB], su[CB], zu[CB];
+#pragma unroll
+                for (int qq = 0; qq < CB; ++qq) {
+                    const int k = 2048 * (q0 + qq) + 32 * lane;
+                    if (q0 + qq < nch && k < H) {
+                        qg[qq] = *reinterpret_cast<const uint4*>(gq + k / 2);
+                        qu[qq] = *reinterpret_cast<const uint4*>(uq + k / 2);
+                        sg[qq] = gs[k / 32];
+                        zg[qq] = gz[k / 32];
+                        su[qq] = us[k / 32];
+                        zu[qq] = uz[k / 32];
+                    }
+                }
+#pragma unroll
+                for (int qq = 0; qq < CB; ++qq) {
+                    const int k = 2048 * (q0 + qq) + 32 * lane;
+                    if (q0 + qq < nch && k < H) {
+                        dot_step_w4<NR>(qg[qq], bf16_bits_to_f32(sg[qq]), bf16_bits_to_f32(zg[qq]),
+                                        xs, xsum, H, k, ag);
+                        dot_step_w4<NR>(qu[qq], bf16_bits_to_f32(su[qq]), bf16_bits_to_f32(zu[qq]),
+                                        xs, xsum, H, k, au);
+                    }
+                }
+            }
+        }
+        uint16_t* hout = shared ? a.h_s : a.h_r + (size_t)g.row0 * a.I;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float gs_ = wave_sum(ag[r]);
+            const float us_ = wave_sum(au[r]);
+            if (lane == r) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(gs_, us_));
+        }
+    }
+}
+
+template <int W4>
+__device__ __forceinline__ void gateup_dispatch_rows(const ExpertArgs& a, const Group& g, int c0,
+                                                     const uint16_t* xs, const float* xsum) {
+    switch (g.n) {
+        case 1: gateup_item<W4, 1>(a, g, c0, xs, xsum); break;
+        case 2: gateup_item<W4, 2>(a, g, c0, xs, xsum); break;
+        case 3: gateup_item<W4, 3>(a, g, c0, xs, xsum); break;
+        case 4: gateup_item<W4, 4>(a, g, c0, xs, xsum); break;
+        case 5: gateup_item<W4, 5>(a, g, c0, xs, xsum); break;
+        case 6: gateup_item<W4, 6>(a, g, c0, xs, xsum); break;
+        case 7: gateup_item<W4, 7>(a, g, c0, xs, xsum); break;
+        default: gateup_item<W4, 8>(a, g, c0, xs, xsum); break;
+    }
+}
+
+// Work items: every GEMV group (routed groups first, the shared expert last
+// when it is on this path) times its column tiles.
+__device__ __forceinline__ void item_of(const ExpertArgs& a, int it, int nrouted, int TR,
+                                        int* gi, int* tile) {
+    if (it < nrouted * TR) {
+        *gi = it / TR;
+        *tile = it - *gi * TR;
+    } else {
+        *gi = nrouted;
+        *tile = it - nrouted * TR;
+    }
+}
+
+template <int W4>
+__global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a, int max_rows) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+    float* xsum = reinterpret_cast<float*>(smem + (size_t)max_rows * a.H * 2);
+    const int ngv = a.plan_counts[0];
+    if (ngv == 0) return;
+    const bool sh_last = a.groups[a.gemv_list[ngv - 1]].expert < 0;
+    const int nrouted = ngv - (sh_last ? 1 : 0);
+    const int TR = a.I / kGuCols, TS = sh_last ? a.Is / kGuCols : 0;
+    const int total = nrouted * TR + TS;
+    const int per = (total + gridDim.x - 1) / gridDim.x;
+    const int beg = blockIdx.x * per, end = min(total, beg + per);
+    int cur = -1;
+    for (int it = beg; it < end; ++it) {
+        int gi, tile;
+        item_of(a, it, nrouted, TR, &gi, &tile);
+        const Group g = a.groups[a.gemv_list[gi]];
+        const bool w4 = W4 && g.expert >= 0;
+        if (gi != cur) {
+            __syncthreads();
+            stage_rows(a, g, false, a.H, g.n, w4, xs, xsum);
+            __syncthreads();
+            cur = gi;
+        }
+        if (w4)
+            gateup_dispatch_rows<1>(a, g, tile * kGuCols, xs, xsum);
+        else
+            gateup_dispatch_rows<0>(a, g, tile * kGuCols, xs, xsum);
+    }
+}
+
+// ---- down ------------------------------------------------------------------
+
+// One work item: output columns n0 .. n0+63 of group g; wave w owns 8 of them.
+template <int W4, int NR>
+__device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uint16_t* xs,
+                          const float* xsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const bool shared = g.expert < 0;
+    const int K = shared ? a.Is : a.I;
+    const int H = a.H;
+    constexpr int U = kDnCols / kGemvWaves;  // 8 columns per wave
+    const int cbase = n0 + U * wave;
+    float acc[U][NR];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[u][r] = 0.0f;
+    if (!W4) {
+        const uint16_t* wbase = shared ? a.swd : a.wd + (size_t)g.expert * H * K;
+        constexpr int CB = 4;
+        const int nch = (K + 511) / 512;
+        for (int q0 = 0; q0 < nch; q0 += CB) {
+            uint4 wv[U][CB];
+#pragma unroll
+            for (int qq = 0; qq < CB; ++qq) {
+                const int k = 512 * (q0 + qq) + 8 * lane;
+                if (q0 + qq < nch && k < K) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        wv[u][qq] = *reinterpret_cast<const uint4*>(wbase + (size_t)(cbase + u) * K + k);
+                }
+            }
+#pragma unroll
+            for (int qq = 0; qq < CB; ++qq) {
+                const int k = 512 * (q0 + qq) + 8 * lane;
+                if (q0 + qq < nch && k < K) {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k);
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            float s = acc[u][r];
+                            s = dot2_bf16(wv[u][qq].x, xv.x, s);
+                            s = dot2_bf16(wv[u][qq].y, xv.y, s);
+                            s = dot2_bf16(wv[u][qq].z, xv.z, s);
+                            s = dot2_bf16(wv[u][qq].w, xv.w, s);
+                            acc[u][r] = s;
+                        }
+                    }
+                }
+            }
+        }
+    } else {
+        const size_t rbase = (size_t)g.expert * H;
+        constexpr int CB = 1;
+        const int nch = (K + 2047) / 2048;
+        for (int q0 = 0; q0 < nch; q0 += CB) {
+            uint4 qv[U][CB];
+            uint32_t sv[U][CB], zv[U][CB];
+#pragma unroll
+            for (int qq = 0; qq < CB; ++qq) {
+                const int k = 2048 * (q0 + qq) + 32 * lane;
+                if (q0 + qq < nch && k < K) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const size_t row = rbase + cbase + u;
+                        qv[u][qq] = *reinterpret_cast<const uint4*>(a.qd + row * (K / 2) + k / 2);
+                        sv[u][qq] = a.sd[row * (K / 32) + k / 32];
+                        zv[u][qq] = a.zd[row * (K / 32) + k / 32];
+                    }
+                }
+            }
+#pragma unroll
+            for (int qq = 0; qq < CB; ++qq) {
+                const int k = 2048 * (q0 + qq) + 32 * lane;
+                if (q0 + qq < nch && k < K) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        dot_step_w4<NR>(qv[u][qq], bf16_bits_to_f32(sv[u][qq]),
+                                        bf16_bits_to_f32(zv[u][qq]), xs, xsum, K, k, acc[u]);
+                }
+            }
+        }
+    }
+    float* yout = shared ? a.y_s : a.y_r + (size_t)g.row0 * H;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float v = wave_sum(acc[u][r]);
+            if (lane == ((u * NR + r) & 63)) yout[(size_t)r * H + cbase + u] = v;
+        }
+}
+
+template <int W4>
+__device__ __forceinline__ void down_dispatch_rows(const ExpertArgs& a, const Group& g, int n0,
+                                                   const uint16_t* xs, const float* xsum) {
+    switch (g.n) {
+        case 1: down_item<W4, 1>(a, g, n0, xs, xsum); break;
+        case 2: down_item<W4, 2>(a, g, n0, xs, xsum); break;
+        case 3: down_item<W4, 3>(a, g, n0, xs, xsum); break;
+        case 4: down_item<W4, 4>(a, g, n0, xs, xsum); break;
+        case 5: down_item<W4, 5>(a, g, n0, xs, xsum); break;
+        case 6: down_item<W4, 6>(a, g, n0, xs, xsum); break;
+        case 7: down_item<W4, 7>(a, g, n0, xs, xsum); break;
+        default: down_item<W4, 8>(a, g, n0, xs, xsum); break;
+    }
+}
+
+template <int W4>
+__global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, int max_rows,
+                                                                 int kmax) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+    float* xsum = reinterpret_cast<float*>(smem + (size_t)max_rows * kmax * 2);
+    const int ngv = a.plan_counts[0];
+    if (ngv == 0) return;
+    const bool sh_last = a.groups[a.gemv_list[ngv - 1]].expert < 0;
+    const int nrouted = ngv - (sh_last ? 1 : 0);
+    const int TR = a.H / kDnCols;
+    const int total = (nrouted + (sh_last ? 1 : 0)) * TR;
+    const int per = (total + gridDim.x - 1) / gridDim.x;
+    const int beg = blockIdx.x * per, end = min(total, beg + per);
+    int cur = -1;
+    for (int it = beg; it < end; ++it) {
+        const int gi = it / TR, tile = it - gi * TR;
+        const Group g = a.groups[a.gemv_list[gi]];
+        const bool w4 = W4 && g.expert >= 0;
+        const int K = g.expert < 0 ? a.Is : a.I;
+        if (gi != cur) {
+            __syncthreads();
+            stage_rows(a, g, true, K, g.n, w4, xs, xsum);
+            __syncthreads();
+            cur = gi;
+        }
+        if (w4)
+            down_dispatch_rows<1>(a, g, tile * kDnCols, xs, xsum);
+        else
+            down_dispatch_rows<0>(a, g, tile * kDnCols, xs, xsum);
+    }
+}
+
+static int gemv_grid(size_t lds, int num_cu, long long ub) {
+    int occ = lds <= 64 * 1024 ? 2 : 1;
+    long long g = (long long)num_cu * occ;
+    if (ub < g) g = ub;
+    return (int)(g < 1 ? 1 : g);
+}
+
+void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st) {
+    const int max_rows = a.T < kSmallRows ? a.T : kSmallRows;
+    const size_t lds = (size_t)max_rows * a.H * 2 + (a.fmt ? (size_t)max_rows * (a.H / 32) * 4 : 0);
+    const int tiles = (a.I > a.Is ? a.I : a.Is) / kGuCols;
+    const int grid = gemv_grid(lds, num_cu, (long long)max_groups * tiles);
+    if (a.fmt) {
+        allow_lds(gateup_gemv_kernel<1>, lds);
+        gateup_gemv_kernel<1><<<grid, kGemvThreads, lds, st>>>(a, max_rows);
+    } else {
+        allow_lds(gateup_gemv_kernel<0>, lds);
+        gateup_gemv_kernel<0><<<grid, kGemvThreads, lds, st>>>(a, max_rows);
+    }
+}
+
+void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st) {
+    const int max_rows = a.T < kSmallRows ? a.T : kSmallRows;
+    const int kmax = a.I > a.Is ? a.I : a.Is;
+    const size_t lds = (size_t)max_rows * kmax * 2 + (a.fmt ? (size_t)max_rows * (kmax / 32) * 4 : 0);
+    const int grid = gemv_grid(lds, num_cu, (long long)max_groups * (a.H / kDnCols));
+    if (a.fmt) {
+        allow_lds(down_gemv_kernel<1>, lds);
+        down_gemv_kernel<1><<<grid, kGemvThreads, lds, st>>>(a, max_rows, kmax);
+    } else {
+        allow_lds(down_gemv_kernel<0>, lds);
+        down_gemv_kernel<0><<<grid, kGemvThreads, lds, st>>>(a, max_rows, kmax);
+    }
+}
+
+}  // namespace moe

@@ -1,0 +1,258 @@
+// moe_ffn.cpp -- the C ABI of libmoeffn.so: argument checks (all before the
+// first enqueue: [P1] "GLM-5.2 multi-GPU: expert-parallel sharding + the
+// resident-fit benchmark", gates table, fail-closed plans), workspace layout,
+// and the stage launches on the caller's stream.
+#include "../../include/moe_ffn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "common.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+// Byte offsets of the scratch buffers inside the workspace.
+struct Layout {
+    size_t logits, ids, w, counts, offsets, perm, pos, blkcnt, groups, gemv_list, mfma_list,
+        plan_counts, h_r, h_s, y_r, y_s, total;
+};
+
+int max_mfma_tiles(int T, int E, int k) {
+    // sum over groups of ceil(n / BM) <= (picks + shared rows) / BM + groups
+    return (int)(((long long)T * k + T) / moe::kBM) + E + 2;
+}
+
+Layout make_layout(int T, int H, int E, int I, int Is, int k) {
+    Layout L;
+    size_t o = 0;
+    const size_t Tk = (size_t)T * k;
+    const size_t nblk = ((size_t)T + moe::kDispatchRows - 1) / moe::kDispatchRows;
+    L.logits = o; o += align_up((size_t)T * E * 4);
+    L.ids = o; o += align_up(Tk * 4);
+    L.w = o; o += align_up(Tk * 4);
+    L.counts = o; o += align_up((size_t)E * 4);
+    L.offsets = o; o += align_up(((size_t)E + 1) * 4);
+    L.perm = o; o += align_up(Tk * 4);
+    L.pos = o; o += align_up(Tk * 4);
+    L.blkcnt = o; o += align_up(nblk * E * 4);
+    L.groups = o; o += align_up(((size_t)E + 1) * sizeof(moe::Group));
+    L.gemv_list = o; o += align_up(((size_t)E + 1) * 4);
+    L.mfma_list = o; o += align_up((size_t)max_mfma_tiles(T, E, k) * 8);
+    L.plan_counts = o; o += align_up(16);
+    L.h_r = o; o += align_up(Tk * I * 2);
+    L.h_s = o; o += align_up((size_t)T * (Is > 0 ? Is : 0) * 2);
+    L.y_r = o; o += align_up(Tk * H * 4);
+    L.y_s = o; o += align_up((size_t)T * H * 4);
+    L.total = o;
+    return L;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Size checks shared by moe_ffn and moe_ffn_workspace_bytes, in the order
+// the header documents: shapes, then top-k, then format.
+int32_t check_sizes(int32_t T, int32_t H, int32_t E, int32_t I, int32_t Is, int32_t topk,
+                    int32_t fmt) {
+    if (T < 1 || T > MOE_MAX_T || H < 256 || H % 256 != 0 || I < 64 || I % 64 != 0 ||
+        (Is != 0 && (Is < 64 || Is % 64 != 0)) || E < 1 || E > MOE_MAX_E)
+        return MOE_E_SHAPE;
+    if (topk < 1 || topk > E || topk > MOE_MAX_TOPK) return MOE_E_TOPK;
+    if (fmt != MOE_BF16 && fmt != MOE_W4A16) return MOE_E_FORMAT;
+    return MOE_OK;
+}
+
+struct DeviceInfo {
+    bool known = false;
+    bool gfx950 = false;
+    int num_cu = 0;
+};
+
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+// Per-device properties, queried once per device (a read-only cache).
+int32_t device_info(int* num_cu) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_E_HIP;
+    if (dev < 0 || dev >= 64) return MOE_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.known) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_E_HIP;
+        d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        d.num_cu = prop.multiProcessorCount;
+        d.known = true;
+    }
+    if (!d.gfx950) return MOE_E_DEVICE;
+    *num_cu = d.num_cu;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t I, int32_t Is,
+                                          int32_t topk, int32_t fmt) {
+    if (check_sizes(T, H, E, I, Is, topk, fmt) != MOE_OK) return 0;
+    return make_layout(T, H, E, I, Is, topk).total;
+}
+
+extern "C" const char* moe_ffn_strerror(int32_t code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_E_NULL: return "a required pointer is NULL";
+        case MOE_E_SHAPE: return "unsupported or inconsistent sizes";
+        case MOE_E_DIM: return "router expert count differs from the experts' count";
+        case MOE_E_BAND: return "expert band is empty or outside [0, E)";
+        case MOE_E_TOPK: return "topk must be in [1, min(E, 16)]";
+        case MOE_E_FORMAT: return "unknown expert weight format or group size";
+        case MOE_E_WORKSPACE: return "workspace missing or too small";
+        case MOE_E_ALIGN: return "a pointer is not 16-byte aligned";
+        case MOE_E_HIP: return "HIP runtime error while enqueuing";
+        case MOE_E_DEVICE: return "the current device is not a gfx950 GPU";
+        default: return "unknown error code";
+    }
+}
+
+extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
+                           const moe_shared* shared, int32_t band_lo, int32_t band_hi,
+                           int32_t topk, const moe_out* out, void* stream) {
+    // ---- argument checks: nothing is enqueued before all of them pass ----
+    if (!x || !router_w || !experts || !out) return MOE_E_NULL;
+    if (!x->ptr || !router_w->w || !out->y) return MOE_E_NULL;
+    const int fmt = experts->fmt;
+    if (fmt == MOE_BF16) {
+        if (!experts->w_gate_up || !experts->w_down) return MOE_E_NULL;
+    } else if (fmt == MOE_W4A16) {
+        if (!experts->q_gate_up || !experts->s_gate_up || !experts->z_gate_up || !experts->q_down ||
+            !experts->s_down || !experts->z_down)
+            return MOE_E_NULL;
+    } else {
+        return MOE_E_FORMAT;
+    }
+    if (shared && (!shared->w_gate_up || !shared->w_down)) return MOE_E_NULL;
+
+    const int T = x->T, H = x->H, E = experts->E, I = experts->I;
+    const int Is = shared ? shared->Is : 0;
+    if (router_w->H != H || experts->H != H || (shared && shared->H != H)) return MOE_E_SHAPE;
+    if (shared && Is <= 0) return MOE_E_SHAPE;
+    if (router_w->E != E) return MOE_E_DIM;
+    {
+        const int32_t rc = check_sizes(T, H, E, I, Is, topk, fmt);
+        if (rc != MOE_OK) return rc;
+    }
+    if (fmt == MOE_W4A16 && experts->group != 32) return MOE_E_FORMAT;
+    if (band_lo < 0 || band_hi > E || band_lo >= band_hi) return MOE_E_BAND;
+
+    const bool bf = fmt == MOE_BF16;
+    const void* ptrs[] = {x->ptr, router_w->w, router_w->bias,
+                          bf ? experts->w_gate_up : nullptr, bf ? experts->w_down : nullptr,
+                          bf ? nullptr : experts->q_gate_up, bf ? nullptr : experts->s_gate_up,
+                          bf ? nullptr : experts->z_gate_up, bf ? nullptr : experts->q_down,
+                          bf ? nullptr : experts->s_down, bf ? nullptr : experts->z_down,
+                          shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
+                          out->y, out->topk_ids, out->topk_w, out->counts, out->offsets,
+                          out->perm, out->pos, out->workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_E_ALIGN;
+
+    const Layout L = make_layout(T, H, E, I, Is, topk);
+    if (!out->workspace || out->workspace_bytes < L.total) return MOE_E_WORKSPACE;
+
+    int num_cu = 0;
+    {
+        int32_t rc = device_info(&num_cu);
+        if (rc != MOE_OK) return rc;
+    }
+
+    // ---- enqueue ----
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    unsigned char* ws = static_cast<unsigned char*>(out->workspace);
+    float* logits = reinterpret_cast<float*>(ws + L.logits);
+    int32_t* ids = out->topk_ids ? out->topk_ids : reinterpret_cast<int32_t*>(ws + L.ids);
+    float* wts = out->topk_w ? out->topk_w : reinterpret_cast<float*>(ws + L.w);
+    int32_t* counts = out->counts ? out->counts : reinterpret_cast<int32_t*>(ws + L.counts);
+    int32_t* offsets = out->offsets ? out->offsets : reinterpret_cast<int32_t*>(ws + L.offsets);
+    int32_t* perm = out->perm ? out->perm : reinterpret_cast<int32_t*>(ws + L.perm);
+    int32_t* pos = out->pos ? out->pos : reinterpret_cast<int32_t*>(ws + L.pos);
+    int32_t* blkcnt = reinterpret_cast<int32_t*>(ws + L.blkcnt);
+    moe::Group* groups = reinterpret_cast<moe::Group*>(ws + L.groups);
+    int32_t* gemv_list = reinterpret_cast<int32_t*>(ws + L.gemv_list);
+    int32_t* mfma_list = reinterpret_cast<int32_t*>(ws + L.mfma_list);
+    int32_t* plan_counts = reinterpret_cast<int32_t*>(ws + L.plan_counts);
+
+    void* const* ev = out->stage_events;
+    auto mark = [&](int slot) {
+        if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[slot]), st);
+    };
+
+    (void)hipGetLastError();  // clear a stale error so the check below sees only ours
+
+    const int nb = band_hi - band_lo;
+    const bool has_shared = shared != nullptr;
+    mark(MOE_EV_ROUTER);
+    moe::launch_router_logits(static_cast<const uint16_t*>(x->ptr), router_w->w, router_w->bias, T,
+                              H, E, logits, st);
+    mark(MOE_EV_TOPK);
+    moe::launch_router_topk(logits, T, E, topk, ids, wts, st);
+    mark(MOE_EV_DISPATCH);
+    moe::launch_dispatch(ids, T, topk, band_lo, band_hi, has_shared, blkcnt, counts, offsets, perm,
+                         pos, groups, gemv_list, mfma_list, plan_counts, st);
+
+    moe::ExpertArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = static_cast<const uint16_t*>(x->ptr);
+    a.T = T;
+    a.H = H;
+    a.topk = topk;
+    a.I = I;
+    a.fmt = fmt;
+    a.wgu = static_cast<const uint16_t*>(experts->w_gate_up);
+    a.wd = static_cast<const uint16_t*>(experts->w_down);
+    a.qgu = experts->q_gate_up;
+    a.sgu = static_cast<const uint16_t*>(experts->s_gate_up);
+    a.zgu = static_cast<const uint16_t*>(experts->z_gate_up);
+    a.qd = experts->q_down;
+    a.sd = static_cast<const uint16_t*>(experts->s_down);
+    a.zd = static_cast<const uint16_t*>(experts->z_down);
+    a.Is = Is;
+    a.swgu = shared ? static_cast<const uint16_t*>(shared->w_gate_up) : nullptr;
+    a.swd = shared ? static_cast<const uint16_t*>(shared->w_down) : nullptr;
+    a.groups = groups;
+    a.gemv_list = gemv_list;
+    a.mfma_list = mfma_list;
+    a.plan_counts = plan_counts;
+    a.perm = perm;
+    a.h_r = reinterpret_cast<uint16_t*>(ws + L.h_r);
+    a.h_s = reinterpret_cast<uint16_t*>(ws + L.h_s);
+    a.y_r = reinterpret_cast<float*>(ws + L.y_r);
+    a.y_s = reinterpret_cast<float*>(ws + L.y_s);
+
+    // Groups on each path: a group has at most T rows (a row picks an expert
+    // at most once), so with T <= 8 nothing reaches the MFMA path.
+    const long long picks = (long long)T * topk;
+    const int max_groups = (int)((picks < nb ? picks : nb) + (has_shared ? 1 : 0));
+    const bool mfma_possible = T > moe::kSmallRows;
+    const int max_tiles = max_mfma_tiles(T, nb, topk);
+
+    mark(MOE_EV_GU_GEMV);
+    moe::launch_gateup_gemv(a, max_groups, num_cu, st);
+    mark(MOE_EV_GU_MFMA);
+    if (mfma_possible) moe::launch_gateup_mfma(a, max_tiles, num_cu, st);
+    mark(MOE_EV_DN_GEMV);
+    moe::launch_down_gemv(a, max_groups, num_cu, st);
+    mark(MOE_EV_DN_MFMA);
+    if (mfma_possible) moe::launch_down_mfma(a, max_tiles, num_cu, st);
+    mark(MOE_EV_COMBINE);
+    moe::launch_combine(a.y_r, has_shared ? a.y_s : nullptr, pos, wts, T, H, topk, out->y, st);
+    mark(MOE_EV_END);
+
+    if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
+    return MOE_OK;
+}
