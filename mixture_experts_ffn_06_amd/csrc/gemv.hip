@@ -121,7 +121,11 @@ __device__ __forceinline__ void dot_step_w4(const uint4& q, float sc, float zz, 
 
 // One work item: intermediate columns c0 .. c0+15 of group g; wave w owns
 // columns c0 + 2w and c0 + 2w + 1 (its gate row and its up row each).
-template <int W4, int NR>
+// Loads are never predicated: a lane step past the end of the row reloads the
+// row's first chunk and its weights are zeroed, so every load of a block is in
+// flight at once (a predicated load would make the compiler wait for the
+// previous one).  CB = lane steps per block (bf16: 512 inputs per step).
+template <int W4, int NR, int CB>
 __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const uint16_t* xs,
                             const float* xsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -137,25 +141,24 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
             const uint16_t* gr = shared ? a.swgu + (size_t)c * H
                                         : a.wgu + ((size_t)g.expert * 2 * Ig + c) * H;
             const uint16_t* ur = gr + (size_t)Ig * H;
-            constexpr int CB = 12;
             const int nch = (H + 511) / 512;
             for (int q0 = 0; q0 < nch; q0 += CB) {
                 uint4 wg[CB], wu[CB];
+                int kk[CB];
+                bool ok[CB];
 #pragma unroll
                 for (int qq = 0; qq < CB; ++qq) {
                     const int k = 512 * (q0 + qq) + 8 * lane;
-                    if (q0 + qq < nch && k < H) {
-                        wg[qq] = *reinterpret_cast<const uint4*>(gr + k);
-                        wu[qq] = *reinterpret_cast<const uint4*>(ur + k);
-                    }
+                    ok[qq] = (q0 + qq < nch) && (k < H);
+                    kk[qq] = ok[qq] ? k : 0;
+                    wg[qq] = *reinterpret_cast<const uint4*>(gr + kk[qq]);
+                    wu[qq] = *reinterpret_cast<const uint4*>(ur + kk[qq]);
                 }
 #pragma unroll
                 for (int qq = 0; qq < CB; ++qq) {
-                    const int k = 512 * (q0 + qq) + 8 * lane;
-                    if (q0 + qq < nch && k < H) {
-                        dot_step_bf16<NR>(wg[qq], xs, H, k, ag);
-                        dot_step_bf16<NR>(wu[qq], xs, H, k, au);
-                    }
+                    const uint4 z = make_uint4(0, 0, 0, 0);
+                    dot_step_bf16<NR>(ok[qq] ? wg[qq] : z, xs, H, kk[qq], ag);
+                    dot_step_bf16<NR>(ok[qq] ? wu[qq] : z, xs, H, kk[qq], au);
                 }
             }
         } else {
@@ -166,32 +169,32 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
             const uint16_t* gz = a.zgu + grow * (H / 32);
             const uint16_t* us = a.sgu + urow * (H / 32);
             const uint16_t* uz = a.zgu + urow * (H / 32);
-            constexpr int CB = 4;
+            constexpr int CB4 = 3;
             const int nch = (H + 2047) / 2048;
-            for (int q0 = 0; q0 < nch; q0 += CB) {
-                uint4 qg[CB], qu[CB];
-                uint32_t sg[CB], zg[CB], su[CB], zu[CB];
+            for (int q0 = 0; q0 < nch; q0 += CB4) {
+                uint4 qg[CB4], qu[CB4];
+                uint32_t sg[CB4], zg[CB4], su[CB4], zu[CB4];
+                int kk[CB4];
+                bool ok[CB4];
 #pragma unroll
-                for (int qq = 0; qq < CB; ++qq) {
+                for (int qq = 0; qq < CB4; ++qq) {
                     const int k = 2048 * (q0 + qq) + 32 * lane;
-                    if (q0 + qq < nch && k < H) {
-                        qg[qq] = *reinterpret_cast<const uint4*>(gq + k / 2);
-                        qu[qq] = *reinterpret_cast<const uint4*>(uq + k / 2);
-                        sg[qq] = gs[k / 32];
-                        zg[qq] = gz[k / 32];
-                        su[qq] = us[k / 32];
-                        zu[qq] = uz[k / 32];
-                    }
+                    ok[qq] = (q0 + qq < nch) && (k < H);
+                    kk[qq] = ok[qq] ? k : 0;
+                    qg[qq] = *reinterpret_cast<const uint4*>(gq + kk[qq] / 2);
+                    qu[qq] = *reinterpret_cast<const uint4*>(uq + kk[qq] / 2);
+                    sg[qq] = gs[kk[qq] / 32];
+                    zg[qq] = gz[kk[qq] / 32];
+                    su[qq] = us[kk[qq] / 32];
+                    zu[qq] = uz[kk[qq] / 32];
                 }
 #pragma unroll
-                for (int qq = 0; qq < CB; ++qq) {
-                    const int k = 2048 * (q0 + qq) + 32 * lane;
-                    if (q0 + qq < nch && k < H) {
-                        dot_step_w4<NR>(qg[qq], bf16_bits_to_f32(sg[qq]), bf16_bits_to_f32(zg[qq]),
-                                        xs, xsum, H, k, ag);
-                        dot_step_w4<NR>(qu[qq], bf16_bits_to_f32(su[qq]), bf16_bits_to_f32(zu[qq]),
-                                        xs, xsum, H, k, au);
-                    }
+                for (int qq = 0; qq < CB4; ++qq) {
+                    // a zero scale removes the contribution of a step past the end
+                    const float sgv = ok[qq] ? bf16_bits_to_f32(sg[qq]) : 0.0f;
+                    const float suv = ok[qq] ? bf16_bits_to_f32(su[qq]) : 0.0f;
+                    dot_step_w4<NR>(qg[qq], sgv, bf16_bits_to_f32(zg[qq]), xs, xsum, H, kk[qq], ag);
+                    dot_step_w4<NR>(qu[qq], suv, bf16_bits_to_f32(zu[qq]), xs, xsum, H, kk[qq], au);
                 }
             }
         }
@@ -205,18 +208,18 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
     }
 }
 
-template <int W4>
+template <int W4, int CB>
 __device__ __forceinline__ void gateup_dispatch_rows(const ExpertArgs& a, const Group& g, int c0,
                                                      const uint16_t* xs, const float* xsum) {
     switch (g.n) {
-        case 1: gateup_item<W4, 1>(a, g, c0, xs, xsum); break;
-        case 2: gateup_item<W4, 2>(a, g, c0, xs, xsum); break;
-        case 3: gateup_item<W4, 3>(a, g, c0, xs, xsum); break;
-        case 4: gateup_item<W4, 4>(a, g, c0, xs, xsum); break;
-        case 5: gateup_item<W4, 5>(a, g, c0, xs, xsum); break;
-        case 6: gateup_item<W4, 6>(a, g, c0, xs, xsum); break;
-        case 7: gateup_item<W4, 7>(a, g, c0, xs, xsum); break;
-        default: gateup_item<W4, 8>(a, g, c0, xs, xsum); break;
+        case 1: gateup_item<W4, 1, CB>(a, g, c0, xs, xsum); break;
+        case 2: gateup_item<W4, 2, CB>(a, g, c0, xs, xsum); break;
+        case 3: gateup_item<W4, 3, CB>(a, g, c0, xs, xsum); break;
+        case 4: gateup_item<W4, 4, CB>(a, g, c0, xs, xsum); break;
+        case 5: gateup_item<W4, 5, CB>(a, g, c0, xs, xsum); break;
+        case 6: gateup_item<W4, 6, CB>(a, g, c0, xs, xsum); break;
+        case 7: gateup_item<W4, 7, CB>(a, g, c0, xs, xsum); break;
+        default: gateup_item<W4, 8, CB>(a, g, c0, xs, xsum); break;
     }
 }
 
@@ -233,7 +236,7 @@ __device__ __forceinline__ void item_of(const ExpertArgs& a, int it, int nrouted
     }
 }
 
-template <int W4>
+template <int W4, int CB>
 __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a, int max_rows) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -259,15 +262,16 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
             cur = gi;
         }
         if (w4)
-            gateup_dispatch_rows<1>(a, g, tile * kGuCols, xs, xsum);
+            gateup_dispatch_rows<1, CB>(a, g, tile * kGuCols, xs, xsum);
         else
-            gateup_dispatch_rows<0>(a, g, tile * kGuCols, xs, xsum);
+            gateup_dispatch_rows<0, CB>(a, g, tile * kGuCols, xs, xsum);
     }
 }
 
 // ---- down ------------------------------------------------------------------
 
-// One work item: output columns n0 .. n0+63 of group g; wave w owns 8 of them.
+// One work item: output columns n0 .. n0+63 of group g; wave w owns 8 of them,
+// streamed as two passes of 4 rows of the down weight (16 loads in flight).
 template <int W4, int NR>
 __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uint16_t* xs,
                           const float* xsum) {
@@ -275,8 +279,9 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
     const bool shared = g.expert < 0;
     const int K = shared ? a.Is : a.I;
     const int H = a.H;
-    constexpr int U = kDnCols / kGemvWaves;  // 8 columns per wave
-    const int cbase = n0 + U * wave;
+    constexpr int U = kDnCols / kGemvWaves / 2;  // 4 columns per pass, two passes
+    for (int pass = 0; pass < 2; ++pass) {
+    const int cbase = n0 + 2 * U * wave + U * pass;
     float acc[U][NR];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -288,65 +293,55 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
         const int nch = (K + 511) / 512;
         for (int q0 = 0; q0 < nch; q0 += CB) {
             uint4 wv[U][CB];
+            int kk[CB];
+            bool ok[CB];
 #pragma unroll
             for (int qq = 0; qq < CB; ++qq) {
                 const int k = 512 * (q0 + qq) + 8 * lane;
-                if (q0 + qq < nch && k < K) {
+                ok[qq] = (q0 + qq < nch) && (k < K);
+                kk[qq] = ok[qq] ? k : 0;
 #pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        wv[u][qq] = *reinterpret_cast<const uint4*>(wbase + (size_t)(cbase + u) * K + k);
-                }
+                for (int u = 0; u < U; ++u)
+                    wv[u][qq] = *reinterpret_cast<const uint4*>(wbase + (size_t)(cbase + u) * K + kk[qq]);
             }
 #pragma unroll
             for (int qq = 0; qq < CB; ++qq) {
-                const int k = 512 * (q0 + qq) + 8 * lane;
-                if (q0 + qq < nch && k < K) {
 #pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k);
+                for (int r = 0; r < NR; ++r) {
+                    uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + kk[qq]);
+                    if (!ok[qq]) xv = make_uint4(0, 0, 0, 0);
 #pragma unroll
-                        for (int u = 0; u < U; ++u) {
-                            float s = acc[u][r];
-                            s = dot2_bf16(wv[u][qq].x, xv.x, s);
-                            s = dot2_bf16(wv[u][qq].y, xv.y, s);
-                            s = dot2_bf16(wv[u][qq].z, xv.z, s);
-                            s = dot2_bf16(wv[u][qq].w, xv.w, s);
-                            acc[u][r] = s;
-                        }
+                    for (int u = 0; u < U; ++u) {
+                        float s = acc[u][r];
+                        s = dot2_bf16(wv[u][qq].x, xv.x, s);
+                        s = dot2_bf16(wv[u][qq].y, xv.y, s);
+                        s = dot2_bf16(wv[u][qq].z, xv.z, s);
+                        s = dot2_bf16(wv[u][qq].w, xv.w, s);
+                        acc[u][r] = s;
                     }
                 }
             }
         }
     } else {
         const size_t rbase = (size_t)g.expert * H;
-        constexpr int CB = 1;
         const int nch = (K + 2047) / 2048;
-        for (int q0 = 0; q0 < nch; q0 += CB) {
-            uint4 qv[U][CB];
-            uint32_t sv[U][CB], zv[U][CB];
+        for (int q = 0; q < nch; ++q) {
+            uint4 qv[U];
+            uint32_t sv[U], zv[U];
+            const int k = 2048 * q + 32 * lane;
+            const bool ok = k < K;
+            const int kq = ok ? k : 0;
 #pragma unroll
-            for (int qq = 0; qq < CB; ++qq) {
-                const int k = 2048 * (q0 + qq) + 32 * lane;
-                if (q0 + qq < nch && k < K) {
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const size_t row = rbase + cbase + u;
-                        qv[u][qq] = *reinterpret_cast<const uint4*>(a.qd + row * (K / 2) + k / 2);
-                        sv[u][qq] = a.sd[row * (K / 32) + k / 32];
-                        zv[u][qq] = a.zd[row * (K / 32) + k / 32];
-                    }
-                }
+            for (int u = 0; u < U; ++u) {
+                const size_t row = rbase + cbase + u;
+                qv[u] = *reinterpret_cast<const uint4*>(a.qd + row * (K / 2) + kq / 2);
+                sv[u] = a.sd[row * (K / 32) + kq / 32];
+                zv[u] = a.zd[row * (K / 32) + kq / 32];
             }
 #pragma unroll
-            for (int qq = 0; qq < CB; ++qq) {
-                const int k = 2048 * (q0 + qq) + 32 * lane;
-                if (q0 + qq < nch && k < K) {
-#pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        dot_step_w4<NR>(qv[u][qq], bf16_bits_to_f32(sv[u][qq]),
-                                        bf16_bits_to_f32(zv[u][qq]), xs, xsum, K, k, acc[u]);
-                }
-            }
+            for (int u = 0; u < U; ++u)
+                dot_step_w4<NR>(qv[u], ok ? bf16_bits_to_f32(sv[u]) : 0.0f, bf16_bits_to_f32(zv[u]),
+                                xs, xsum, K, kq, acc[u]);
         }
     }
     float* yout = shared ? a.y_s : a.y_r + (size_t)g.row0 * H;
@@ -357,6 +352,7 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
             const float v = wave_sum(acc[u][r]);
             if (lane == ((u * NR + r) & 63)) yout[(size_t)r * H + cbase + u] = v;
         }
+    }
 }
 
 template <int W4>
@@ -414,18 +410,32 @@ static int gemv_grid(size_t lds, int num_cu, long long ub) {
     return (int)(g < 1 ? 1 : g);
 }
 
+template <int CB>
+static void launch_gateup_cb(const ExpertArgs& a, int grid, size_t lds, int max_rows,
+                             hipStream_t st) {
+    if (a.fmt) {
+        allow_lds(gateup_gemv_kernel<1, CB>, lds);
+        gateup_gemv_kernel<1, CB><<<grid, kGemvThreads, lds, st>>>(a, max_rows);
+    } else {
+        allow_lds(gateup_gemv_kernel<0, CB>, lds);
+        gateup_gemv_kernel<0, CB><<<grid, kGemvThreads, lds, st>>>(a, max_rows);
+    }
+}
+
 void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st) {
     const int max_rows = a.T < kSmallRows ? a.T : kSmallRows;
     const size_t lds = (size_t)max_rows * a.H * 2 + (a.fmt ? (size_t)max_rows * (a.H / 32) * 4 : 0);
     const int tiles = (a.I > a.Is ? a.I : a.Is) / kGuCols;
     const int grid = gemv_grid(lds, num_cu, (long long)max_groups * tiles);
-    if (a.fmt) {
-        allow_lds(gateup_gemv_kernel<1>, lds);
-        gateup_gemv_kernel<1><<<grid, kGemvThreads, lds, st>>>(a, max_rows);
-    } else {
-        allow_lds(gateup_gemv_kernel<0>, lds);
-        gateup_gemv_kernel<0><<<grid, kGemvThreads, lds, st>>>(a, max_rows);
-    }
+    // lane steps per load block for bf16 rows: the whole row when it has at
+    // most 12 steps of 512 inputs (H <= 6144)
+    const int nch = (a.H + 511) / 512;
+    if (nch <= 4)
+        launch_gateup_cb<4>(a, grid, lds, max_rows, st);
+    else if (nch <= 8)
+        launch_gateup_cb<8>(a, grid, lds, max_rows, st);
+    else
+        launch_gateup_cb<12>(a, grid, lds, max_rows, st);
 }
 
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st) {
