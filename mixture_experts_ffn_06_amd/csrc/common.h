@@ -116,6 +116,8 @@ void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStre
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
 void launch_gateup_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
 void launch_down_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
+// bf16 experts: the four-stage direct-to-LDS pipeline (gate/up or down).
+void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int max_tiles, int num_cu, hipStream_t st);
 void launch_combine(const float* y_r, const float* y_s, const int32_t* pos, const float* w,
                     int T, int H, int k, float* out, hipStream_t st);
 

@@ -244,11 +244,21 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     mark(MOE_EV_GU_GEMV);
     moe::launch_gateup_gemv(a, max_groups, num_cu, st);
     mark(MOE_EV_GU_MFMA);
-    if (mfma_possible) moe::launch_gateup_mfma(a, max_tiles, num_cu, st);
+    if (mfma_possible) {
+        if (fmt == MOE_BF16)
+            moe::launch_mfma_pipe(a, true, max_tiles, num_cu, st);
+        else
+            moe::launch_gateup_mfma(a, max_tiles, num_cu, st);
+    }
     mark(MOE_EV_DN_GEMV);
     moe::launch_down_gemv(a, max_groups, num_cu, st);
     mark(MOE_EV_DN_MFMA);
-    if (mfma_possible) moe::launch_down_mfma(a, max_tiles, num_cu, st);
+    if (mfma_possible) {
+        if (fmt == MOE_BF16)
+            moe::launch_mfma_pipe(a, false, max_tiles, num_cu, st);
+        else
+            moe::launch_down_mfma(a, max_tiles, num_cu, st);
+    }
     mark(MOE_EV_COMBINE);
     moe::launch_combine(a.y_r, has_shared ? a.y_s : nullptr, pos, wts, T, H, topk, out->y, st);
     mark(MOE_EV_END);
