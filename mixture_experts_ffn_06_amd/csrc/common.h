@@ -54,8 +54,9 @@ struct ExpertArgs {
     // plan (device, written by the dispatch)
     const Group* groups;        // [nb + 1]
     const int32_t* gemv_list;   // group indices on the GEMV path
-    const int32_t* mfma_list;   // (group, m0) pairs on the MFMA path
-    const int32_t* plan_counts; // [0] = GEMV groups, [1] = MFMA tiles
+    const int32_t* mfma_list;   // three lists of (group, m0) pairs: 128-, 64- and 32-row tiles
+    int32_t mfma_cap;           // capacity of each of the three lists
+    const int32_t* plan_counts; // [0] GEMV groups, [1..3] tiles of 128, 64, 32 rows
     const int32_t* perm;        // [T*topk]
     // scratch
     uint16_t* h_r;  // bf16 [T*topk, I]  (perm order)
@@ -111,13 +112,14 @@ void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, 
 void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_shared,
                      int32_t* blkcnt, int32_t* counts, int32_t* offsets, int32_t* perm,
                      int32_t* pos, Group* groups, int32_t* gemv_list, int32_t* mfma_list,
-                     int32_t* plan_counts, hipStream_t st);
+                     int mfma_cap, int32_t* plan_counts, hipStream_t st);
 void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
 void launch_gateup_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
 void launch_down_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
-// bf16 experts: the four-stage direct-to-LDS pipeline (gate/up or down).
-void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int max_tiles, int num_cu, hipStream_t st);
+// bf16 experts: the direct-to-LDS pipelined tiles of 128, 64 and 32 rows
+// (gate/up or down), one launch per tile height.
+void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st);
 void launch_combine(const float* y_r, const float* y_s, const int32_t* pos, const float* w,
                     int T, int H, int k, float* out, hipStream_t st);
 

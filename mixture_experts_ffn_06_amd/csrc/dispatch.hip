@@ -79,7 +79,7 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     int nblk, int nb, int T, bool has_shared, int32_t* __restrict__ blkcnt,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, Group* __restrict__ groups,
-    int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list,
+    int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list, int mfma_cap,
     int32_t* __restrict__ plan_counts, int lo) {
     __shared__ int s_tmp[17];
     const int tid = threadIdx.x;
@@ -112,8 +112,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     }
     if (tid == 0) offsets[nb] = total;
 
-    // Groups and work lists.
-    int n[2], gv[2], mt[2];
+    // Groups and work lists.  A group of 1..8 rows goes to the GEMV path.  A
+    // larger group is cut into 128-row tiles; its last partial tile (if any)
+    // becomes a tile of 128, 64 or 32 rows by what it covers.
+    int n[2], gv[2], t128[2], t64[2], t32[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int e = 2 * tid + q;
@@ -126,25 +128,47 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
             groups[e] = Group{-1, 0, T, 0};
         }
         gv[q] = (n[q] >= 1 && n[q] <= kSmallRows) ? 1 : 0;
-        mt[q] = (n[q] > kSmallRows) ? (n[q] + kBM - 1) / kBM : 0;
+        const int big = n[q] > kSmallRows;
+        const int rem = n[q] % kBM;
+        t128[q] = big ? n[q] / kBM + (rem > 64 ? 1 : 0) : 0;
+        t64[q] = (big && rem > 32 && rem <= 64) ? 1 : 0;
+        t32[q] = (big && rem > 0 && rem <= 32) ? 1 : 0;
     }
-    int ngv, nmt;
+    int ngv, n128, n64, n32;
     int gv0 = block_exclusive_scan(gv[0] + gv[1], s_tmp, &ngv);
-    int mt0 = block_exclusive_scan(mt[0] + mt[1], s_tmp, &nmt);
+    int o128 = block_exclusive_scan(t128[0] + t128[1], s_tmp, &n128);
+    int o64 = block_exclusive_scan(t64[0] + t64[1], s_tmp, &n64);
+    int o32 = block_exclusive_scan(t32[0] + t32[1], s_tmp, &n32);
+    int32_t* l128 = mfma_list;
+    int32_t* l64 = mfma_list + 2 * (size_t)mfma_cap;
+    int32_t* l32 = mfma_list + 4 * (size_t)mfma_cap;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int e = 2 * tid + q;
         if (gv[q]) gemv_list[gv0] = e;
         gv0 += gv[q];
-        for (int m = 0; m < mt[q]; ++m) {
-            mfma_list[2 * (mt0 + m)] = e;
-            mfma_list[2 * (mt0 + m) + 1] = m * kBM;
+        for (int m = 0; m < t128[q]; ++m) {
+            l128[2 * (o128 + m)] = e;
+            l128[2 * (o128 + m) + 1] = m * kBM;
         }
-        mt0 += mt[q];
+        o128 += t128[q];
+        const int tail = (n[q] / kBM) * kBM;
+        if (t64[q]) {
+            l64[2 * o64] = e;
+            l64[2 * o64 + 1] = tail;
+        }
+        o64 += t64[q];
+        if (t32[q]) {
+            l32[2 * o32] = e;
+            l32[2 * o32 + 1] = tail;
+        }
+        o32 += t32[q];
     }
     if (tid == 0) {
         plan_counts[0] = ngv;
-        plan_counts[1] = nmt;
+        plan_counts[1] = n128;
+        plan_counts[2] = n64;
+        plan_counts[3] = n32;
     }
 }
 
@@ -178,13 +202,14 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
 void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_shared,
                      int32_t* blkcnt, int32_t* counts, int32_t* offsets, int32_t* perm,
                      int32_t* pos, Group* groups, int32_t* gemv_list, int32_t* mfma_list,
-                     int32_t* plan_counts, hipStream_t st) {
+                     int mfma_cap, int32_t* plan_counts, hipStream_t st) {
     const int nb = hi - lo;
     const int nblk = (T + kDispatchRows - 1) / kDispatchRows;
     const size_t lds = sizeof(unsigned long long) * 4 * (size_t)nb;
     dispatch_count_kernel<<<nblk, kDispatchRows, lds, st>>>(ids, T, k, lo, nb, blkcnt);
     dispatch_scan_kernel<<<1, 1024, 0, st>>>(nblk, nb, T, has_shared, blkcnt, counts, offsets,
-                                             groups, gemv_list, mfma_list, plan_counts, lo);
+                                             groups, gemv_list, mfma_list, mfma_cap, plan_counts,
+                                             lo);
     dispatch_place_kernel<<<nblk, kDispatchRows, lds, st>>>(ids, T, k, lo, nb, blkcnt, perm, pos);
 }
 

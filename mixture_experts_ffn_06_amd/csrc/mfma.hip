@@ -225,31 +225,34 @@ __device__ void mfma_tile(const ExpertArgs& a, TileSmem& sm, const Group& g, int
     }
 }
 
+// Walks the three tile lists of the dispatch (tiles of 128, 64 and 32 rows)
+// with 128-row tiles; a shorter tile's missing rows are zero and never stored.
 template <int W4, bool GATEUP>
-__global__ __launch_bounds__(kMfmaThreads) void expert_mfma_kernel(ExpertArgs a, int sh_tiles) {
+__global__ __launch_bounds__(kMfmaThreads) void expert_mfma_kernel(ExpertArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     TileSmem& sm = *reinterpret_cast<TileSmem*>(smem_raw);
-    const int ntiles = a.plan_counts[1];
-    if (ntiles == 0) return;
-    // The shared expert's tiles (if any on this path) are the last entries.
-    const int last_group = a.mfma_list[2 * (ntiles - 1)];
-    const int shn = a.groups[last_group].expert < 0 ? sh_tiles : 0;
-    const int rt = ntiles - shn;
+    const int n0 = a.plan_counts[1], n1 = a.plan_counts[2], n2 = a.plan_counts[3];
+    const int ntiles = n0 + n1 + n2;
     const int NTr = GATEUP ? a.I / 64 : a.H / kBN;
     const int NTs = GATEUP ? a.Is / 64 : a.H / kBN;
-    const int total = rt * NTr + shn * NTs;
+    const int NT = NTr > NTs ? NTr : NTs;
+    const int total = ntiles * NT;
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        int tile, nt;
-        if (item < rt * NTr) {
-            tile = item / NTr;
-            nt = item - tile * NTr;
-        } else {
-            const int it2 = item - rt * NTr;
-            tile = rt + it2 / NTs;
-            nt = it2 - (it2 / NTs) * NTs;
+        int tile = item / NT;
+        const int nt = item - tile * NT;
+        int list = 0;
+        if (tile >= n0) {
+            tile -= n0;
+            list = 1;
+            if (tile >= n1) {
+                tile -= n1;
+                list = 2;
+            }
         }
-        const Group g = a.groups[a.mfma_list[2 * tile]];
-        const int m0 = a.mfma_list[2 * tile + 1];
+        const int32_t* tl = a.mfma_list + 2 * (size_t)list * a.mfma_cap;
+        const Group g = a.groups[tl[2 * tile]];
+        if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
+        const int m0 = tl[2 * tile + 1];
         if (W4 && g.expert >= 0)
             mfma_tile<1, GATEUP>(a, sm, g, m0, nt);
         else
@@ -264,30 +267,28 @@ static int mfma_grid(int num_cu, long long ub) {
 }
 
 void launch_gateup_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st) {
-    const int sh_tiles = (a.T + kBM - 1) / kBM;
     const int nt = (a.I > a.Is ? a.I : a.Is) / 64;
-    const int grid = mfma_grid(num_cu, (long long)max_tiles * nt);
+    const int grid = mfma_grid(num_cu, 3LL * max_tiles * nt);
     const size_t lds = sizeof(TileSmem);
     if (a.fmt) {
         allow_lds(expert_mfma_kernel<1, true>, lds);
-        expert_mfma_kernel<1, true><<<grid, kMfmaThreads, lds, st>>>(a, sh_tiles);
+        expert_mfma_kernel<1, true><<<grid, kMfmaThreads, lds, st>>>(a);
     } else {
         allow_lds(expert_mfma_kernel<0, true>, lds);
-        expert_mfma_kernel<0, true><<<grid, kMfmaThreads, lds, st>>>(a, sh_tiles);
+        expert_mfma_kernel<0, true><<<grid, kMfmaThreads, lds, st>>>(a);
     }
 }
 
 void launch_down_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st) {
-    const int sh_tiles = (a.T + kBM - 1) / kBM;
     const int nt = a.H / kBN;
-    const int grid = mfma_grid(num_cu, (long long)max_tiles * nt);
+    const int grid = mfma_grid(num_cu, 3LL * max_tiles * nt);
     const size_t lds = sizeof(TileSmem);
     if (a.fmt) {
         allow_lds(expert_mfma_kernel<1, false>, lds);
-        expert_mfma_kernel<1, false><<<grid, kMfmaThreads, lds, st>>>(a, sh_tiles);
+        expert_mfma_kernel<1, false><<<grid, kMfmaThreads, lds, st>>>(a);
     } else {
         allow_lds(expert_mfma_kernel<0, false>, lds);
-        expert_mfma_kernel<0, false><<<grid, kMfmaThreads, lds, st>>>(a, sh_tiles);
+        expert_mfma_kernel<0, false><<<grid, kMfmaThreads, lds, st>>>(a);
     }
 }
 

@@ -24,7 +24,7 @@ struct Layout {
 };
 
 int max_mfma_tiles(int T, int E, int k) {
-    // sum over groups of ceil(n / BM) <= (picks + shared rows) / BM + groups
+    // tiles of one height over all groups <= (picks + shared rows) / 128 + groups
     return (int)(((long long)T * k + T) / moe::kBM) + E + 2;
 }
 
@@ -43,7 +43,7 @@ Layout make_layout(int T, int H, int E, int I, int Is, int k) {
     L.blkcnt = o; o += align_up(nblk * E * 4);
     L.groups = o; o += align_up(((size_t)E + 1) * sizeof(moe::Group));
     L.gemv_list = o; o += align_up(((size_t)E + 1) * 4);
-    L.mfma_list = o; o += align_up((size_t)max_mfma_tiles(T, E, k) * 8);
+    L.mfma_list = o; o += align_up(3 * (size_t)max_mfma_tiles(T, E, k) * 8);
     L.plan_counts = o; o += align_up(16);
     L.h_r = o; o += align_up(Tk * I * 2);
     L.h_s = o; o += align_up((size_t)T * (Is > 0 ? Is : 0) * 2);
@@ -202,8 +202,9 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     mark(MOE_EV_TOPK);
     moe::launch_router_topk(logits, T, E, topk, ids, wts, st);
     mark(MOE_EV_DISPATCH);
+    const int mfma_cap = max_mfma_tiles(T, E, topk);
     moe::launch_dispatch(ids, T, topk, band_lo, band_hi, has_shared, blkcnt, counts, offsets, perm,
-                         pos, groups, gemv_list, mfma_list, plan_counts, st);
+                         pos, groups, gemv_list, mfma_list, mfma_cap, plan_counts, st);
 
     moe::ExpertArgs a;
     memset(&a, 0, sizeof a);
@@ -227,6 +228,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     a.groups = groups;
     a.gemv_list = gemv_list;
     a.mfma_list = mfma_list;
+    a.mfma_cap = mfma_cap;
     a.plan_counts = plan_counts;
     a.perm = perm;
     a.h_r = reinterpret_cast<uint16_t*>(ws + L.h_r);
@@ -246,7 +248,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     mark(MOE_EV_GU_MFMA);
     if (mfma_possible) {
         if (fmt == MOE_BF16)
-            moe::launch_mfma_pipe(a, true, max_tiles, num_cu, st);
+            moe::launch_mfma_pipe(a, true, num_cu, st);
         else
             moe::launch_gateup_mfma(a, max_tiles, num_cu, st);
     }
@@ -255,7 +257,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     mark(MOE_EV_DN_MFMA);
     if (mfma_possible) {
         if (fmt == MOE_BF16)
-            moe::launch_mfma_pipe(a, false, max_tiles, num_cu, st);
+            moe::launch_mfma_pipe(a, false, num_cu, st);
         else
             moe::launch_down_mfma(a, max_tiles, num_cu, st);
     }
