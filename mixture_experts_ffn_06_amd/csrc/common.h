@@ -89,11 +89,24 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                            __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 
-// Sum over the 64 lanes of a wave (fixed butterfly; every lane gets the sum).
+// Sum over the 64 lanes of a wave, in a fixed order: four DPP steps sum each
+// row of 16 lanes (pairs, quads, halves, rows: every lane of a row ends with
+// the row's sum), then (row0 + row1) + (row2 + row3) from lanes 0, 16, 32, 48.
+// Every lane gets the sum.  DPP moves stay in the VALU, so the chain is short.
+template <int CTRL>
+__device__ __forceinline__ float dpp_term(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) v += __shfl_xor(v, s, 64);
-    return v;
+    v += dpp_term<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_term<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_term<0x141>(v);  // row_half_mirror
+    v += dpp_term<0x140>(v);  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Allow a kernel more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).

@@ -12,8 +12,7 @@
 // group's rows (at most 8) in LDS.  A wave streams whole weight rows (every
 // lane loads 16 contiguous bytes per step, so a step reads 1 KiB of one row),
 // multiplies them with all rows of the group, and reduces across lanes once
-// per weight row.  Blocks take contiguous runs of work items so the rows of a
-// group are staged once per block.
+// per weight row.  Work items are dealt to the blocks round-robin.
 //
 // 4-bit weights: (code - zero) * scale with (scale, zero) per 32 inputs.  One
 // lane step covers exactly one 32-input group: the codes are widened to the
@@ -247,10 +246,11 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
     const int nrouted = ngv - (sh_last ? 1 : 0);
     const int TR = a.I / kGuCols, TS = sh_last ? a.Is / kGuCols : 0;
     const int total = nrouted * TR + TS;
-    const int per = (total + gridDim.x - 1) / gridDim.x;
-    const int beg = blockIdx.x * per, end = min(total, beg + per);
+    // Items are dealt round-robin: at any moment the blocks stream neighbouring
+    // column tiles of the same experts, so HBM sees a few long sequential runs
+    // rather than one run per block.
     int cur = -1;
-    for (int it = beg; it < end; ++it) {
+    for (int it = blockIdx.x; it < total; it += gridDim.x) {
         int gi, tile;
         item_of(a, it, nrouted, TR, &gi, &tile);
         const Group g = a.groups[a.gemv_list[gi]];
@@ -382,10 +382,8 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, i
     const int nrouted = ngv - (sh_last ? 1 : 0);
     const int TR = a.H / kDnCols;
     const int total = (nrouted + (sh_last ? 1 : 0)) * TR;
-    const int per = (total + gridDim.x - 1) / gridDim.x;
-    const int beg = blockIdx.x * per, end = min(total, beg + per);
     int cur = -1;
-    for (int it = beg; it < end; ++it) {
+    for (int it = blockIdx.x; it < total; it += gridDim.x) {
         const int gi = it / TR, tile = it - gi * TR;
         const Group g = a.groups[a.gemv_list[gi]];
         const bool w4 = W4 && g.expert >= 0;
