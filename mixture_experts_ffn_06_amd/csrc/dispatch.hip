@@ -74,47 +74,16 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
     return res;
 }
 
-// One block of 1024 threads; thread i owns groups 2i and 2i+1 (group nb is the
-// shared expert when present).
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
-    int nblk, int nb, int T, bool has_shared, int32_t* __restrict__ blkcnt,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, Group* __restrict__ groups,
-    int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list, int mfma_cap,
-    int32_t* __restrict__ plan_counts, int lo) {
-    __shared__ int s_tmp[17];
+// Groups and work lists.  Thread i owns groups 2i and 2i+1 with row counts
+// cnt[] and first rows run[]; group nb is the shared expert when present.
+__device__ void build_plan(const int cnt[2], const int run[2], int nb, int T, int lo,
+                           bool has_shared, Group* __restrict__ groups,
+                           int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list,
+                           int mfma_cap, int32_t* __restrict__ plan_counts, int* s_tmp) {
     const int tid = threadIdx.x;
-    int cnt[2], run[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int e = 2 * tid + q;
-        int r = 0;
-        if (e < nb) {
-            for (int b = 0; b < nblk; ++b) {
-                int c = blkcnt[(size_t)b * nb + e];
-                blkcnt[(size_t)b * nb + e] = r;
-                r += c;
-            }
-        }
-        cnt[q] = r;
-    }
-    int total;
-    int off0 = block_exclusive_scan(cnt[0] + cnt[1], s_tmp, &total);
-    run[0] = off0;
-    run[1] = off0 + cnt[0];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int e = 2 * tid + q;
-        if (e < nb) {
-            counts[e] = cnt[q];
-            offsets[e] = run[q];
-            for (int b = 0; b < nblk; ++b) blkcnt[(size_t)b * nb + e] += run[q];
-        }
-    }
-    if (tid == 0) offsets[nb] = total;
-
-    // Groups and work lists.  A group of 1..8 rows goes to the GEMV path.  A
-    // larger group is cut into 128-row tiles; its last partial tile (if any)
-    // becomes a tile of 128, 64 or 32 rows by what it covers.
+    // A group of 1..8 rows goes to the GEMV path.  A larger group is cut into
+    // 128-row tiles; its last partial tile (if any) becomes a tile of 128, 64
+    // or 32 rows by what it covers.
     int n[2], gv[2], t128[2], t64[2], t32[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -172,6 +141,49 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     }
 }
 
+
+// One block of 1024 threads; thread i owns groups 2i and 2i+1 (group nb is the
+// shared expert when present).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    int nblk, int nb, int T, bool has_shared, int32_t* __restrict__ blkcnt,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, Group* __restrict__ groups,
+    int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list, int mfma_cap,
+    int32_t* __restrict__ plan_counts, int lo) {
+    __shared__ int s_tmp[17];
+    const int tid = threadIdx.x;
+    int cnt[2], run[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        int r = 0;
+        if (e < nb) {
+            for (int b = 0; b < nblk; ++b) {
+                int c = blkcnt[(size_t)b * nb + e];
+                blkcnt[(size_t)b * nb + e] = r;
+                r += c;
+            }
+        }
+        cnt[q] = r;
+    }
+    int total;
+    int off0 = block_exclusive_scan(cnt[0] + cnt[1], s_tmp, &total);
+    run[0] = off0;
+    run[1] = off0 + cnt[0];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        if (e < nb) {
+            counts[e] = cnt[q];
+            offsets[e] = run[q];
+            for (int b = 0; b < nblk; ++b) blkcnt[(size_t)b * nb + e] += run[q];
+        }
+    }
+    if (tid == 0) offsets[nb] = total;
+
+    build_plan(cnt, run, nb, T, lo, has_shared, groups, gemv_list, mfma_list, mfma_cap,
+               plan_counts, s_tmp);
+}
+
 __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ ids,
                                                              int T, int k, int lo, int nb,
                                                              const int32_t* __restrict__ base,
@@ -199,6 +211,62 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
     }
 }
 
+// All of the dispatch in one block when every row fits in one block of 256
+// rows (decode): masks, counts, scan, plan and placement without a kernel
+// boundary in between.  1024 threads; threads 0..255 own the rows.
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int lo, int nb, bool has_shared,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ pos, Group* __restrict__ groups, int32_t* __restrict__ gemv_list,
+    int32_t* __restrict__ mfma_list, int mfma_cap, int32_t* __restrict__ plan_counts) {
+    extern __shared__ unsigned long long masks[];  // [4][nb], then int offsets[nb + 1]
+    int* s_off = reinterpret_cast<int*>(masks + 4 * nb);
+    __shared__ int s_tmp[17];
+    build_masks(masks, ids, T, k, lo, nb);
+    const int tid = threadIdx.x;
+    int cnt[2], run[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        cnt[q] = e < nb ? __popcll(masks[e]) + __popcll(masks[nb + e]) + __popcll(masks[2 * nb + e]) +
+                              __popcll(masks[3 * nb + e])
+                        : 0;
+    }
+    int total;
+    const int off0 = block_exclusive_scan(cnt[0] + cnt[1], s_tmp, &total);
+    run[0] = off0;
+    run[1] = off0 + cnt[0];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int e = 2 * tid + q;
+        if (e < nb) {
+            counts[e] = cnt[q];
+            offsets[e] = run[q];
+            s_off[e] = run[q];
+        }
+    }
+    if (tid == 0) offsets[nb] = total;
+    build_plan(cnt, run, nb, T, lo, has_shared, groups, gemv_list, mfma_list, mfma_cap,
+               plan_counts, s_tmp);  // its scans hold barriers: s_off is visible
+    const int t = tid;
+    if (t >= T) return;
+    const int wave = tid >> 6, lane = tid & 63;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int j = 0; j < k; ++j) {
+        const int p = t * k + j;
+        const int e = ids[p] - lo;
+        if (e >= 0 && e < nb) {
+            int slot = s_off[e];
+            for (int w = 0; w < wave; ++w) slot += __popcll(masks[w * nb + e]);
+            slot += __popcll(masks[wave * nb + e] & below);
+            perm[slot] = p;
+            pos[p] = slot;
+        } else {
+            pos[p] = -1;
+        }
+    }
+}
+
 void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_shared,
                      int32_t* blkcnt, int32_t* counts, int32_t* offsets, int32_t* perm,
                      int32_t* pos, Group* groups, int32_t* gemv_list, int32_t* mfma_list,
@@ -206,6 +274,12 @@ void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_
     const int nb = hi - lo;
     const int nblk = (T + kDispatchRows - 1) / kDispatchRows;
     const size_t lds = sizeof(unsigned long long) * 4 * (size_t)nb;
+    if (nblk == 1) {
+        dispatch_small_kernel<<<1, 1024, lds + sizeof(int) * ((size_t)nb + 1), st>>>(
+            ids, T, k, lo, nb, has_shared, counts, offsets, perm, pos, groups, gemv_list, mfma_list,
+            mfma_cap, plan_counts);
+        return;
+    }
     dispatch_count_kernel<<<nblk, kDispatchRows, lds, st>>>(ids, T, k, lo, nb, blkcnt);
     dispatch_scan_kernel<<<1, 1024, 0, st>>>(nblk, nb, T, has_shared, blkcnt, counts, offsets,
                                              groups, gemv_list, mfma_list, mfma_cap, plan_counts,

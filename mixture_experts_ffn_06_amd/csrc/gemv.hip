@@ -52,16 +52,21 @@ __device__ void stage_rows(const ExpertArgs& a, const Group& g, bool src_h, int 
         *reinterpret_cast<uint4*>(xs + (size_t)r * K + 8 * c8) = v;
     }
     if (permute) {
+        // per-32 sums, from the staged copy (a fixed order over its 32 values)
+        __syncthreads();
         const int gn = K / 32;
         for (int idx = threadIdx.x; idx < nr * gn; idx += blockDim.x) {
             const int r = idx / gn, gi = idx - r * gn;
-            const uint16_t* src;
-            if (src_h)
-                src = shared ? a.h_s + (size_t)r * a.Is : a.h_r + (size_t)(g.row0 + r) * a.I;
-            else
-                src = a.x + (size_t)(shared ? r : a.perm[g.row0 + r] / a.topk) * a.H;
+            const uint4* src = reinterpret_cast<const uint4*>(xs + (size_t)r * K + 32 * gi);
             float s = 0.0f;
-            for (int q = 0; q < 32; ++q) s += bf16_bits_to_f32(src[32 * gi + q]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 v = src[q];
+                s += bf16_lo(v.x) + bf16_hi(v.x);
+                s += bf16_lo(v.y) + bf16_hi(v.y);
+                s += bf16_lo(v.z) + bf16_hi(v.z);
+                s += bf16_lo(v.w) + bf16_hi(v.w);
+            }
             xsum[r * gn + gi] = s;
         }
     }

@@ -17,7 +17,9 @@
 namespace moe {
 
 // One wave computes a tile of RB rows x EB experts; four waves per block.
-template <int RB, int EB>
+// One wave computes a tile of RB rows x EB experts; four waves per block.
+// The loads of BATCH steps of i are issued before any of them is used.
+template <int RB, int EB, int BATCH>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const float* __restrict__ wr,
                                                             const float* __restrict__ bias,
@@ -50,30 +52,46 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
         for (int e = 0; e < EB; ++e) acc[r][e] = 0.0f;
 
-    for (int i = 0; i < H / 256; ++i) {
-        float xv[RB][4], wv[EB][4];
+    const int nI = H / 256;
+    for (int i0 = 0; i0 < nI; i0 += BATCH) {
+        uint2 xu[BATCH][RB];
+        float4 wf[BATCH][EB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            uint2 u = *reinterpret_cast<const uint2*>(xp[r] + 256 * i + 4 * lane);
-            xv[r][0] = bf16_lo(u.x);
-            xv[r][1] = bf16_hi(u.x);
-            xv[r][2] = bf16_lo(u.y);
-            xv[r][3] = bf16_hi(u.y);
-        }
-#pragma unroll
-        for (int e = 0; e < EB; ++e) {
-            float4 f = *reinterpret_cast<const float4*>(wp[e] + 256 * i + 4 * lane);
-            wv[e][0] = f.x;
-            wv[e][1] = f.y;
-            wv[e][2] = f.z;
-            wv[e][3] = f.w;
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int b = 0; b < BATCH; ++b) {
+            const int i = min(i0 + b, nI - 1);  // steps past the end reload the last one, unused
 #pragma unroll
             for (int r = 0; r < RB; ++r)
+                xu[b][r] = *reinterpret_cast<const uint2*>(xp[r] + 256 * i + 4 * lane);
 #pragma unroll
-                for (int e = 0; e < EB; ++e) acc[r][e] = __builtin_fmaf(xv[r][c], wv[e][c], acc[r][e]);
+            for (int e = 0; e < EB; ++e)
+                wf[b][e] = *reinterpret_cast<const float4*>(wp[e] + 256 * i + 4 * lane);
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            if (i0 + b < nI) {  // wave-uniform
+            float xv[RB][4], wv[EB][4];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                xv[r][0] = bf16_lo(xu[b][r].x);
+                xv[r][1] = bf16_hi(xu[b][r].x);
+                xv[r][2] = bf16_lo(xu[b][r].y);
+                xv[r][3] = bf16_hi(xu[b][r].y);
+            }
+#pragma unroll
+            for (int e = 0; e < EB; ++e) {
+                wv[e][0] = wf[b][e].x;
+                wv[e][1] = wf[b][e].y;
+                wv[e][2] = wf[b][e].z;
+                wv[e][3] = wf[b][e].w;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+#pragma unroll
+                    for (int e = 0; e < EB; ++e) acc[r][e] = __builtin_fmaf(xv[r][c], wv[e][c], acc[r][e]);
+            }
+        }
     }
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1)
@@ -102,24 +120,67 @@ void launch_router_logits(const uint16_t* x, const float* wr, const float* bias,
     if (T <= 1) {
         waves = E;
         blocks = (waves + 3) / 4;
-        router_logits_kernel<1, 1><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<1, 1, 12><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else if (T <= 2) {
         waves = E;
         blocks = (waves + 3) / 4;
-        router_logits_kernel<2, 1><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<2, 1, 12><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else if (T <= 4) {
         waves = E;
         blocks = (waves + 3) / 4;
-        router_logits_kernel<4, 1><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<4, 1, 8><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else if (T <= 64) {
         waves = ((T + 7) / 8) * E;
         blocks = (waves + 3) / 4;
-        router_logits_kernel<8, 1><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<8, 1, 6><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else {
         waves = ((T + 7) / 8) * ((E + 7) / 8);
         blocks = (waves + 3) / 4;
-        router_logits_kernel<8, 8><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<8, 8, 2><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
     }
+}
+
+// Top-k of one row per wave: experts ordered by (logit descending, id
+// ascending); the first k in that order are the picks, in pick order.  The
+// weights are the softmax over the picks ([P2] "GLM-5.3-Flash on CUDA:
+// attention on one GPU, routed experts on the Sparks (proposal) #214", "Per
+// MoE layer": rows travel with their top-k ids and weights).
+// (value, id) keys: a larger value wins, equal values go to the lower id;
+// id 0x7fffffff marks "nothing left" and always loses.
+__device__ __forceinline__ bool key_better(float v2, int i2, float v1, int i1) {
+    return i2 != 0x7fffffff && (i1 == 0x7fffffff || v2 > v1 || (v2 == v1 && i2 < i1));
+}
+
+template <int CTRL>
+__device__ __forceinline__ void key_step(float& v, int& i) {
+    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+    const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
+    if (key_better(ov, oi, v, i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+// Best key of the wave: four DPP steps give every lane its row's best, then
+// the four row winners are combined.  Every lane gets the result.
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+    key_step<0xB1>(v, i);   // quad_perm [1,0,3,2]
+    key_step<0x4E>(v, i);   // quad_perm [2,3,0,1]
+    key_step<0x141>(v, i);  // row_half_mirror
+    key_step<0x140>(v, i);  // row_mirror
+    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+        if (key_better(rv, ri, bv, bi)) {
+            bv = rv;
+            bi = ri;
+        }
+    }
+    v = bv;
+    i = bi;
 }
 
 // Top-k of one row per wave: experts ordered by (logit descending, id
@@ -163,15 +224,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                 bid = lane + 64 * m;
             }
         }
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) {
-            float ov = __shfl_xor(bv, s, 64);
-            int oid = __shfl_xor(bid, s, 64);
-            if (oid != 0x7fffffff && (bid == 0x7fffffff || ov > bv || (ov == bv && oid < bid))) {
-                bv = ov;
-                bid = oid;
-            }
-        }
+        wave_best(bv, bid);
         if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
         sel_v[j] = bv;
         sel_id[j] = bid;
