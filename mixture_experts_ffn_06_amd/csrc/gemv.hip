@@ -227,6 +227,124 @@ __device__ __forceinline__ void gateup_dispatch_rows(const ExpertArgs& a, const 
     }
 }
 
+// ---- overlapped path: bf16 groups of 1 or 2 rows (the decode case) --------
+//
+// A work item's critical path used to be: group descriptor -> row tokens ->
+// rows into LDS -> barrier -> weight loads.  Here the next item's descriptor
+// and tokens are fetched during the current item, and the rows of a new group
+// are loaded into registers before the item's weight loads are issued and
+// written to one of two LDS buffers while those loads are in flight (a plain
+// s_barrier, not __syncthreads, whose fence would wait for them).  The two
+// buffers alternate per staging, so a block needs no barrier before writing
+// the next group's rows: the previous staging's barrier already ordered every
+// read of the buffer being replaced.
+
+struct ItemMeta {
+    Group g;
+    int gi, tile, tok0, tok1;
+};
+
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ ItemMeta load_meta(const ExpertArgs& a, int it, int nrouted, int TR);
+
+// Returns the next item's descriptor (fetched once this item's first loads are
+// in flight), or this item's when there is no next one.
+template <int NR, int CB>
+__device__ ItemMeta gateup_fast(const ExpertArgs& a, const ItemMeta& m, bool restage, uint16_t* xb,
+                                bool has_next, int itn, int nrouted, int TR) {
+    ItemMeta mn = m;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Group& g = m.g;
+    const bool shared = g.expert < 0;
+    const int Ig = shared ? a.Is : a.I;
+    const int H = a.H;
+    const int c8n = H / 8;
+    const int nchunk = NR * c8n;  // <= 4 * kGemvThreads (checked by the caller)
+    // up to four 16-byte chunks of the rows per thread, in named registers
+    auto xchunk = [&](int i) -> uint4 {
+        const int idx = min(tid + kGemvThreads * i, nchunk - 1);
+        const int r = idx / c8n, c8 = idx - r * c8n;
+        return *reinterpret_cast<const uint4*>(a.x + (size_t)(r ? m.tok1 : m.tok0) * H + 8 * c8);
+    };
+    auto xput = [&](int i, const uint4& v) {
+        const int idx = tid + kGemvThreads * i;
+        if (idx < nchunk) {
+            const int r = idx / c8n, c8 = idx - r * c8n;
+            *reinterpret_cast<uint4*>(xb + (size_t)r * H + 8 * c8) = v;
+        }
+    };
+    uint4 x0, x1, x2, x3;
+    if (restage) {
+        x0 = xchunk(0);
+        x1 = xchunk(1);
+        x2 = xchunk(2);
+        x3 = xchunk(3);
+    }
+    const int nch = (H + 511) / 512;  // <= CB (checked by the caller): one block of loads
+    uint16_t* hout = shared ? a.h_s : a.h_r + (size_t)g.row0 * a.I;
+#pragma nounroll
+    for (int cc = 0; cc < 2; ++cc) {
+        const int c = m.tile * kGuCols + 2 * wave + cc;
+        const uint16_t* gr = shared ? a.swgu + (size_t)c * H : a.wgu + ((size_t)g.expert * 2 * Ig + c) * H;
+        const uint16_t* ur = gr + (size_t)Ig * H;
+        float ag[NR], au[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) ag[r] = au[r] = 0.0f;
+        uint4 wg[CB], wu[CB];
+        int kk[CB];
+        bool ok[CB];
+#pragma unroll
+        for (int qq = 0; qq < CB; ++qq) {
+            const int k = 512 * qq + 8 * lane;
+            ok[qq] = (qq < nch) && (k < H);
+            kk[qq] = ok[qq] ? k : 0;
+            wg[qq] = *reinterpret_cast<const uint4*>(gr + kk[qq]);
+            wu[qq] = *reinterpret_cast<const uint4*>(ur + kk[qq]);
+        }
+        if (cc == 0) {
+            if (has_next) mn = load_meta(a, itn, nrouted, TR);
+            if (restage) {
+                xput(0, x0);
+                xput(1, x1);
+                xput(2, x2);
+                xput(3, x3);
+                wait_lgkm0();
+                __builtin_amdgcn_s_barrier();
+            }
+        }
+#pragma unroll
+        for (int qq = 0; qq < CB; ++qq) {
+            const uint4 z = make_uint4(0, 0, 0, 0);
+            dot_step_bf16<NR>(ok[qq] ? wg[qq] : z, xb, H, kk[qq], ag);
+            dot_step_bf16<NR>(ok[qq] ? wu[qq] : z, xb, H, kk[qq], au);
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float gs_ = wave_sum(ag[r]);
+            const float us_ = wave_sum(au[r]);
+            if (lane == r) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(gs_, us_));
+        }
+    }
+    return mn;
+}
+
+__device__ __forceinline__ ItemMeta load_meta(const ExpertArgs& a, int it, int nrouted, int TR) {
+    ItemMeta m;
+    if (it < nrouted * TR) {
+        m.gi = it / TR;
+        m.tile = it - m.gi * TR;
+    } else {
+        m.gi = nrouted;
+        m.tile = it - nrouted * TR;
+    }
+    m.g = a.groups[a.gemv_list[m.gi]];
+    const bool sh = m.g.expert < 0;
+    m.tok0 = sh ? 0 : a.perm[m.g.row0] / a.topk;
+    m.tok1 = sh ? 1 : (m.g.n > 1 ? a.perm[m.g.row0 + 1] / a.topk : m.tok0);
+    return m;
+}
+
 // Work items: every GEMV group (routed groups first, the shared expert last
 // when it is on this path) times its column tiles.
 __device__ __forceinline__ void item_of(const ExpertArgs& a, int it, int nrouted, int TR,
@@ -241,10 +359,10 @@ __device__ __forceinline__ void item_of(const ExpertArgs& a, int it, int nrouted
 }
 
 template <int W4, int CB>
-__global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a, int max_rows) {
+__global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a, int lds_rows) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    float* xsum = reinterpret_cast<float*>(smem + (size_t)max_rows * a.H * 2);
+    float* xsum = reinterpret_cast<float*>(smem + (size_t)lds_rows * a.H * 2);
     const int ngv = a.plan_counts[0];
     if (ngv == 0) return;
     const bool sh_last = a.groups[a.gemv_list[ngv - 1]].expert < 0;
@@ -254,22 +372,42 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
     // Items are dealt round-robin: at any moment the blocks stream neighbouring
     // column tiles of the same experts, so HBM sees a few long sequential runs
     // rather than one run per block.
-    int cur = -1;
-    for (int it = blockIdx.x; it < total; it += gridDim.x) {
-        int gi, tile;
-        item_of(a, it, nrouted, TR, &gi, &tile);
-        const Group g = a.groups[a.gemv_list[gi]];
+    int it = blockIdx.x;
+    if (it >= total) return;
+    const bool fast_ok = 2 * (a.H / 8) <= 4 * kGemvThreads && a.H <= 512 * CB;
+    ItemMeta m = load_meta(a, it, nrouted, TR);
+    int cur = -1, buf = 0;
+    for (;;) {
+        const int itn = it + gridDim.x;
+        const bool has_next = itn < total;
+        ItemMeta mn = m;
+        const Group& g = m.g;
         const bool w4 = W4 && g.expert >= 0;
-        if (gi != cur) {
+        if (!w4 && g.n <= 2 && fast_ok) {
+            const bool restage = m.gi != cur;
+            if (restage) buf ^= 1;
+            uint16_t* xb = xs + (size_t)buf * 2 * a.H;
+            if (g.n == 1)
+                mn = gateup_fast<1, CB>(a, m, restage, xb, has_next, itn, nrouted, TR);
+            else
+                mn = gateup_fast<2, CB>(a, m, restage, xb, has_next, itn, nrouted, TR);
+            cur = m.gi;
+        } else {
+            // rows staged synchronously across the whole LDS area
             __syncthreads();
             stage_rows(a, g, false, a.H, g.n, w4, xs, xsum);
             __syncthreads();
-            cur = gi;
+            if (has_next) mn = load_meta(a, itn, nrouted, TR);
+            if (w4)
+                gateup_dispatch_rows<1, CB>(a, g, m.tile * kGuCols, xs, xsum);
+            else
+                gateup_dispatch_rows<0, CB>(a, g, m.tile * kGuCols, xs, xsum);
+            __syncthreads();  // the next staging may overwrite these rows
+            cur = -1;
         }
-        if (w4)
-            gateup_dispatch_rows<1, CB>(a, g, tile * kGuCols, xs, xsum);
-        else
-            gateup_dispatch_rows<0, CB>(a, g, tile * kGuCols, xs, xsum);
+        if (!has_next) break;
+        it = itn;
+        m = mn;
     }
 }
 
@@ -414,31 +552,33 @@ static int gemv_grid(size_t lds, int num_cu, long long ub) {
 }
 
 template <int CB>
-static void launch_gateup_cb(const ExpertArgs& a, int grid, size_t lds, int max_rows,
+static void launch_gateup_cb(const ExpertArgs& a, int grid, size_t lds, int lds_rows,
                              hipStream_t st) {
     if (a.fmt) {
         allow_lds(gateup_gemv_kernel<1, CB>, lds);
-        gateup_gemv_kernel<1, CB><<<grid, kGemvThreads, lds, st>>>(a, max_rows);
+        gateup_gemv_kernel<1, CB><<<grid, kGemvThreads, lds, st>>>(a, lds_rows);
     } else {
         allow_lds(gateup_gemv_kernel<0, CB>, lds);
-        gateup_gemv_kernel<0, CB><<<grid, kGemvThreads, lds, st>>>(a, max_rows);
+        gateup_gemv_kernel<0, CB><<<grid, kGemvThreads, lds, st>>>(a, lds_rows);
     }
 }
 
 void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st) {
     const int max_rows = a.T < kSmallRows ? a.T : kSmallRows;
-    const size_t lds = (size_t)max_rows * a.H * 2 + (a.fmt ? (size_t)max_rows * (a.H / 32) * 4 : 0);
+    // rows of LDS: the largest group, and at least two buffers of two rows
+    const int lds_rows = max_rows > 4 ? max_rows : 4;
+    const size_t lds = (size_t)lds_rows * a.H * 2 + (a.fmt ? (size_t)max_rows * (a.H / 32) * 4 : 0);
     const int tiles = (a.I > a.Is ? a.I : a.Is) / kGuCols;
     const int grid = gemv_grid(lds, num_cu, (long long)max_groups * tiles);
     // lane steps per load block for bf16 rows: the whole row when it has at
     // most 12 steps of 512 inputs (H <= 6144)
     const int nch = (a.H + 511) / 512;
     if (nch <= 4)
-        launch_gateup_cb<4>(a, grid, lds, max_rows, st);
+        launch_gateup_cb<4>(a, grid, lds, lds_rows, st);
     else if (nch <= 8)
-        launch_gateup_cb<8>(a, grid, lds, max_rows, st);
+        launch_gateup_cb<8>(a, grid, lds, lds_rows, st);
     else
-        launch_gateup_cb<12>(a, grid, lds, max_rows, st);
+        launch_gateup_cb<12>(a, grid, lds, lds_rows, st);
 }
 
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st) {
