@@ -281,26 +281,20 @@ __device__ ItemMeta gateup_fast(const ExpertArgs& a, const ItemMeta& m, bool res
         x2 = xchunk(2);
         x3 = xchunk(3);
     }
-    const int nch = (H + 511) / 512;  // <= CB (checked by the caller): one block of loads
+    // H = 512 CB exactly (checked by the caller): whole rows in one block of
+    // loads, no clamping, no selects
     uint16_t* hout = shared ? a.h_s : a.h_r + (size_t)g.row0 * a.I;
+    const uint16_t* xl = xb + 8 * lane;
 #pragma nounroll
     for (int cc = 0; cc < 2; ++cc) {
         const int c = m.tile * kGuCols + 2 * wave + cc;
-        const uint16_t* gr = shared ? a.swgu + (size_t)c * H : a.wgu + ((size_t)g.expert * 2 * Ig + c) * H;
+        const uint16_t* gr = (shared ? a.swgu + (size_t)c * H : a.wgu + ((size_t)g.expert * 2 * Ig + c) * H) + 8 * lane;
         const uint16_t* ur = gr + (size_t)Ig * H;
-        float ag[NR], au[NR];
-#pragma unroll
-        for (int r = 0; r < NR; ++r) ag[r] = au[r] = 0.0f;
         uint4 wg[CB], wu[CB];
-        int kk[CB];
-        bool ok[CB];
 #pragma unroll
-        for (int qq = 0; qq < CB; ++qq) {
-            const int k = 512 * qq + 8 * lane;
-            ok[qq] = (qq < nch) && (k < H);
-            kk[qq] = ok[qq] ? k : 0;
-            wg[qq] = *reinterpret_cast<const uint4*>(gr + kk[qq]);
-            wu[qq] = *reinterpret_cast<const uint4*>(ur + kk[qq]);
+        for (int q = 0; q < CB; ++q) {
+            wg[q] = *reinterpret_cast<const uint4*>(gr + 512 * q);
+            wu[q] = *reinterpret_cast<const uint4*>(ur + 512 * q);
         }
         if (cc == 0) {
             if (has_next) mn = load_meta(a, itn, nrouted, TR);
@@ -313,11 +307,26 @@ __device__ ItemMeta gateup_fast(const ExpertArgs& a, const ItemMeta& m, bool res
                 __builtin_amdgcn_s_barrier();
             }
         }
+        float ag[NR], au[NR];
 #pragma unroll
-        for (int qq = 0; qq < CB; ++qq) {
-            const uint4 z = make_uint4(0, 0, 0, 0);
-            dot_step_bf16<NR>(ok[qq] ? wg[qq] : z, xb, H, kk[qq], ag);
-            dot_step_bf16<NR>(ok[qq] ? wu[qq] : z, xb, H, kk[qq], au);
+        for (int r = 0; r < NR; ++r) ag[r] = au[r] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < CB; ++q) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(xl + r * H + 512 * q);
+                float sg = ag[r], su = au[r];
+                sg = dot2_bf16(wg[q].x, xv.x, sg);
+                sg = dot2_bf16(wg[q].y, xv.y, sg);
+                sg = dot2_bf16(wg[q].z, xv.z, sg);
+                sg = dot2_bf16(wg[q].w, xv.w, sg);
+                su = dot2_bf16(wu[q].x, xv.x, su);
+                su = dot2_bf16(wu[q].y, xv.y, su);
+                su = dot2_bf16(wu[q].z, xv.z, su);
+                su = dot2_bf16(wu[q].w, xv.w, su);
+                ag[r] = sg;
+                au[r] = su;
+            }
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
     // rather than one run per block.
     int it = blockIdx.x;
     if (it >= total) return;
-    const bool fast_ok = 2 * (a.H / 8) <= 4 * kGemvThreads && a.H <= 512 * CB;
+    const bool fast_ok = 2 * (a.H / 8) <= 4 * kGemvThreads && a.H == 512 * CB;
     ItemMeta m = load_meta(a, it, nrouted, TR);
     int cur = -1, buf = 0;
     for (;;) {
@@ -430,7 +439,31 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc[u][r] = 0.0f;
-    if (!W4) {
+    if (!W4 && K == 512 * 4) {
+        // rows of exactly 4 lane steps (K = 2048): no clamping, no selects
+        const uint16_t* wrow = (shared ? a.swd : a.wd + (size_t)g.expert * H * K) + (size_t)cbase * K + 8 * lane;
+        const uint16_t* xl = xs + 8 * lane;
+        uint4 wv[U][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < U; ++u) wv[u][q] = *reinterpret_cast<const uint4*>(wrow + (size_t)u * K + 512 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(xl + r * K + 512 * q);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float t = acc[u][r];
+                    t = dot2_bf16(wv[u][q].x, xv.x, t);
+                    t = dot2_bf16(wv[u][q].y, xv.y, t);
+                    t = dot2_bf16(wv[u][q].z, xv.z, t);
+                    t = dot2_bf16(wv[u][q].w, xv.w, t);
+                    acc[u][r] = t;
+                }
+            }
+    } else if (!W4) {
         const uint16_t* wbase = shared ? a.swd : a.wd + (size_t)g.expert * H * K;
         constexpr int CB = 4;
         const int nch = (K + 511) / 512;
