@@ -3,9 +3,12 @@
 A step is one call of the whole layer (router, top-k, dispatch, gate/up +
 SwiGLU, down, combine + shared expert) over one batch of synthetic rows whose
 inputs and weights are already resident in HBM.  Before every step a 1 GiB
-scratch write evicts the L2 and the MALL, so every step reads its weights from
-HBM; the layer's own time per step is measured with HIP events recorded by
-the library on the launch stream (the eviction is outside it).
+scratch read evicts the L2 and the MALL (256 MB), so every step reads its
+weights from HBM; the layer's own time per step is measured with HIP events on
+the launch stream (the eviction is outside them).  A read leaves the caches
+clean, as the weight reads of a model's other layers would; a 1 GiB write
+(--flush write) instead leaves them full of dirty lines whose write-back lands
+in the next kernel's time (about 10% of a decode-sized layer).
 
 Prints one JSON line: rows/s, us per layer, the dominant kernel's roofline
 fraction (measured live with the same events) and the oracle timed on the
@@ -55,38 +58,63 @@ class Hip:
         return float(ms.value)
 
 
-def roofline_for(w, counts, stage_ms, synth):
-    """Dominant kernel and its algorithmic bytes or flops per launch.
+def _expert_gu_bytes(w):
+    if w.fmt == "bf16":
+        return 2 * w.I * w.H * 2
+    return 2 * w.I * (w.H // 2) + 2 * 2 * w.I * (w.H // 32) * 2  # codes + bf16 scales and zeros
 
-    Decode-sized batches (every group on the GEMV path): the gate/up GEMV
-    launch, which streams each touched expert's fused gate/up weights once
-    (2*I*H*2 bytes per bf16 expert; codes + scales + zeros for 4-bit) plus the
-    shared expert's, the rows of x and the bf16 intermediate it writes.
-    Prefill-sized batches: the gate/up MFMA launch, 2*(2I)*H flops per row of
-    each group on that path."""
+
+def roofline_for(w, counts, stage_ms):
+    """Dominant kernel and its algorithmic bytes and flops per launch.
+
+    The gate/up projection dominates every workload.  Its algorithmic bytes:
+    each touched expert's fused gate/up weights once (2*I*H bf16 values, or
+    4-bit codes plus a bf16 scale and zero per 32 inputs), the shared
+    expert's, the routed and shared rows of x it reads and the bf16
+    intermediate it writes.  Its flops: 2*(2I)*H per routed row and
+    2*(2Is)*H per shared row.  Decode-sized batches (every group on the GEMV
+    path) take the GEMV launch; larger ones the MFMA launches (one per tile
+    height), whose time is summed.  The bound is whichever of HBM bytes at
+    8 TB/s and flops at the bf16 dense MFMA peak takes longer; the MFMA
+    fraction is reported beside it for every workload."""
     n_touched = int((counts > 0).sum())
+    routed = int(counts.sum())
+    sh_rows = w.T if w.Is else 0
+    wbytes = n_touched * _expert_gu_bytes(w) + (2 * w.Is * w.H * 2 if w.Is else 0)
+    act = (routed + sh_rows) * w.H * 2 + routed * w.I * 2 + sh_rows * w.Is * 2
+    nbytes = wbytes + act
+    flops = 2.0 * routed * 2 * w.I * w.H + 2.0 * sh_rows * 2 * w.Is * w.H
     if w.T <= 8:
-        if w.fmt == "bf16":
-            per_expert = 2 * w.I * w.H * 2
-        else:
-            per_expert = 2 * w.I * (w.H // 2) + 2 * 2 * w.I * (w.H // 32) * 2
-        sh = 2 * w.Is * w.H * 2 if w.Is else 0
-        act = w.T * w.H * 2 + int(counts.sum()) * w.I * 2 + (w.T * w.Is * 2 if w.Is else 0)
-        traffic = n_touched * per_expert + sh + act
-        ms = stage_ms["gu_gemv"]
-        achieved = traffic / (ms * 1e-3) / 1e9
-        return {"bound": "hbm", "kernel": "gateup_gemv_kernel", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "algorithmic_bytes": traffic, "touched_experts": n_touched,
-                "kernel_us": round(ms * 1e3, 2)}
-    rows_mfma = int(counts[counts > 8].sum()) + (w.T if w.Is else 0)
-    flops = 2.0 * rows_mfma * 2 * w.I * w.H
-    ms = stage_ms["gu_mfma"]
-    achieved = flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "kernel": "expert_mfma_kernel<gate/up>", "achieved": round(achieved, 1),
-            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-            "algorithmic_flops": flops, "kernel_us": round(ms * 1e3, 2)}
+        kernel, ms = f"gateup_gemv_kernel<{0 if w.fmt == 'bf16' else 1},12>", stage_ms["gu_gemv"]
+    else:
+        kernel = ("expert_mfma_pipe_kernel<true,256|128|64|32>" if w.fmt == "bf16"
+                  else "expert_mfma_kernel<1,true>")
+        ms = stage_ms["gu_mfma"]
+        # rows on the GEMV path (groups of 1..8 rows) are not in this launch
+        small = counts[(counts > 0) & (counts <= 8)]
+        n_touched -= int(small.numel())
+        routed_m = routed - int(small.sum())
+        wbytes = n_touched * _expert_gu_bytes(w) + (2 * w.Is * w.H * 2 if w.Is else 0)
+        act = (routed_m + sh_rows) * w.H * 2 + routed_m * w.I * 2 + sh_rows * w.Is * 2
+        nbytes = wbytes + act
+        flops = 2.0 * routed_m * 2 * w.I * w.H + 2.0 * sh_rows * 2 * w.Is * w.H
+    sec = ms * 1e-3
+    gbs = nbytes / sec / 1e9
+    tfs = flops / sec / 1e12
+    t_bytes = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_flops = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    mfma = {"achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if t_bytes >= t_flops:
+        out = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        out = {"bound": "mfma", **mfma}
+    out.update({"traffic": None, "kernel": kernel, "kernel_us": round(ms * 1e3, 2),
+                "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                "touched_experts": n_touched, "mfma": mfma,
+                "floor_us": round(max(t_bytes, t_flops) * 1e6, 2)})
+    return out
 
 
 def cpu_baseline(w, d, ex, rows_budget):
@@ -124,7 +152,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode")
-    ap.add_argument("--no-flush", action="store_true", help="do not evict L2/MALL between steps")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="how L2 and MALL are evicted before each step (1 GiB scratch read or write)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8)
     args = ap.parse_args()
@@ -152,13 +181,18 @@ def main():
     out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
     ws = torch.empty((moe.workspace_bytes(w.T, w.H, w.E, w.I, w.Is, w.topk,
                                           0 if w.fmt == "bf16" else 1),), dtype=torch.uint8, device=dev)
-    flush = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    flush = torch.ones((1 << 28,), dtype=torch.int32, device=dev)  # 1 GiB
+
+    def evict():
+        if args.flush == "read":
+            flush.sum()  # reads 1 GiB, writes one scalar
+        elif args.flush == "write":
+            flush.fill_(1)
     ev = [hip.events(moe.MOE_NUM_EVENTS) for _ in range(min(args.steps, 10))]
     ex = {}
 
     def step(events=None, exports=None):
-        if not args.no_flush:
-            flush.fill_(1)
+        evict()
         moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
                     w.band_hi, w.topk, out=out, workspace=ws, events=events, exports=exports)
 
@@ -173,8 +207,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(1)
+        evict()
         starts[i].record(stream)
         moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
                     w.band_hi, w.topk, out=out, workspace=ws)
@@ -195,7 +228,7 @@ def main():
         for s_ in range(len(names) - 1):
             stage[names[s_]] += hip.elapsed_ms(ev[i][s_], ev[i][s_ + 1]) / nstage
     counts = ex["counts"].cpu()
-    roof = roofline_for(w, counts, stage, synth)
+    roof = roofline_for(w, counts, stage)
 
     line = {
         "metric": METRIC,
@@ -207,7 +240,7 @@ def main():
         "ms_per_step": round(ms, 4),
         "ms_per_step_min": round(min(layer_ms), 4),
         "us_per_layer": round(ms * 1e3, 2),
-        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "wall_ms_per_step_incl_eviction": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -215,7 +248,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "topk": w.topk, "I": w.I,
                    "Is": w.Is, "fmt": w.fmt, "band": [w.band_lo, w.band_hi],
-                   "l2_mall_evicted_each_step": not args.no_flush},
+                   "l2_mall_eviction": {"read": "1 GiB read", "write": "1 GiB write",
+                                        "none": None}[args.flush]},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "roofline": roof,
     }

@@ -54,9 +54,9 @@ struct ExpertArgs {
     // plan (device, written by the dispatch)
     const Group* groups;        // [nb + 1]
     const int32_t* gemv_list;   // group indices on the GEMV path
-    const int32_t* mfma_list;   // three lists of (group, m0) pairs: 128-, 64- and 32-row tiles
-    int32_t mfma_cap;           // capacity of each of the three lists
-    const int32_t* plan_counts; // [0] GEMV groups, [1..3] tiles of 128, 64, 32 rows
+    const int32_t* mfma_list;   // four lists of (group, m0) pairs: 128-, 64-, 32- and 256-row tiles
+    int32_t mfma_cap;           // capacity of each list
+    const int32_t* plan_counts; // [0] GEMV groups, [1..4] tiles of 128, 64, 32, 256 rows
     const int32_t* perm;        // [T*topk]
     // scratch
     uint16_t* h_r;  // bf16 [T*topk, I]  (perm order)

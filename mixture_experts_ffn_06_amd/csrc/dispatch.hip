@@ -82,9 +82,10 @@ __device__ void build_plan(const int cnt[2], const int run[2], int nb, int T, in
                            int mfma_cap, int32_t* __restrict__ plan_counts, int* s_tmp) {
     const int tid = threadIdx.x;
     // A group of 1..8 rows goes to the GEMV path.  A larger group is cut into
-    // 128-row tiles; its last partial tile (if any) becomes a tile of 128, 64
-    // or 32 rows by what it covers.
-    int n[2], gv[2], t128[2], t64[2], t32[2];
+    // 256-row tiles; the rest (r rows) becomes a 128-row tile when r > 128
+    // plus one tile of 128, 64 or 32 rows for what is left, by its size.
+    int n[2], gv[2], t256[2], t128[2], t64[2], t32[2];
+    int m128a[2], m128b[2], mlast[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int e = 2 * tid + q;
@@ -98,38 +99,67 @@ __device__ void build_plan(const int cnt[2], const int run[2], int nb, int T, in
         }
         gv[q] = (n[q] >= 1 && n[q] <= kSmallRows) ? 1 : 0;
         const int big = n[q] > kSmallRows;
-        const int rem = n[q] % kBM;
-        t128[q] = big ? n[q] / kBM + (rem > 64 ? 1 : 0) : 0;
-        t64[q] = (big && rem > 32 && rem <= 64) ? 1 : 0;
-        t32[q] = (big && rem > 0 && rem <= 32) ? 1 : 0;
+        const int full = big ? n[q] / 256 : 0;
+        int rem = big ? n[q] % 256 : 0;
+        int m0 = full * 256;
+        t256[q] = full;
+        t128[q] = 0;
+        t64[q] = 0;
+        t32[q] = 0;
+        m128a[q] = m128b[q] = mlast[q] = 0;
+        if (rem > 128) {
+            m128a[q] = m0;
+            t128[q] = 1;
+            m0 += 128;
+            rem -= 128;
+        }
+        mlast[q] = m0;
+        if (rem > 64) {
+            if (t128[q]) m128b[q] = m0; else m128a[q] = m0;
+            t128[q] += 1;
+        } else if (rem > 32) {
+            t64[q] = 1;
+        } else if (rem > 0) {
+            t32[q] = 1;
+        }
     }
-    int ngv, n128, n64, n32;
+    int ngv, n256, n128, n64, n32;
     int gv0 = block_exclusive_scan(gv[0] + gv[1], s_tmp, &ngv);
+    int o256 = block_exclusive_scan(t256[0] + t256[1], s_tmp, &n256);
     int o128 = block_exclusive_scan(t128[0] + t128[1], s_tmp, &n128);
     int o64 = block_exclusive_scan(t64[0] + t64[1], s_tmp, &n64);
     int o32 = block_exclusive_scan(t32[0] + t32[1], s_tmp, &n32);
     int32_t* l128 = mfma_list;
     int32_t* l64 = mfma_list + 2 * (size_t)mfma_cap;
     int32_t* l32 = mfma_list + 4 * (size_t)mfma_cap;
+    int32_t* l256 = mfma_list + 6 * (size_t)mfma_cap;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int e = 2 * tid + q;
         if (gv[q]) gemv_list[gv0] = e;
         gv0 += gv[q];
-        for (int m = 0; m < t128[q]; ++m) {
-            l128[2 * (o128 + m)] = e;
-            l128[2 * (o128 + m) + 1] = m * kBM;
+        for (int m = 0; m < t256[q]; ++m) {
+            l256[2 * (o256 + m)] = e;
+            l256[2 * (o256 + m) + 1] = m * 256;
+        }
+        o256 += t256[q];
+        if (t128[q] >= 1) {
+            l128[2 * o128] = e;
+            l128[2 * o128 + 1] = m128a[q];
+        }
+        if (t128[q] == 2) {
+            l128[2 * o128 + 2] = e;
+            l128[2 * o128 + 3] = m128b[q];
         }
         o128 += t128[q];
-        const int tail = (n[q] / kBM) * kBM;
         if (t64[q]) {
             l64[2 * o64] = e;
-            l64[2 * o64 + 1] = tail;
+            l64[2 * o64 + 1] = mlast[q];
         }
         o64 += t64[q];
         if (t32[q]) {
             l32[2 * o32] = e;
-            l32[2 * o32 + 1] = tail;
+            l32[2 * o32 + 1] = mlast[q];
         }
         o32 += t32[q];
     }
@@ -138,6 +168,7 @@ __device__ void build_plan(const int cnt[2], const int run[2], int nb, int T, in
         plan_counts[1] = n128;
         plan_counts[2] = n64;
         plan_counts[3] = n32;
+        plan_counts[4] = n256;
     }
 }
 

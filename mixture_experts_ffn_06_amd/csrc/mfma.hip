@@ -225,14 +225,15 @@ __device__ void mfma_tile(const ExpertArgs& a, TileSmem& sm, const Group& g, int
     }
 }
 
-// Walks the three tile lists of the dispatch (tiles of 128, 64 and 32 rows)
-// with 128-row tiles; a shorter tile's missing rows are zero and never stored.
+// Walks the tile lists of the dispatch with 128-row tiles: a 256-row tile is
+// two of them; a shorter tile's missing rows are zero and never stored.
 template <int W4, bool GATEUP>
 __global__ __launch_bounds__(kMfmaThreads) void expert_mfma_kernel(ExpertArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     TileSmem& sm = *reinterpret_cast<TileSmem*>(smem_raw);
     const int n0 = a.plan_counts[1], n1 = a.plan_counts[2], n2 = a.plan_counts[3];
-    const int ntiles = n0 + n1 + n2;
+    const int n3 = 2 * a.plan_counts[4];  // 256-row tiles as pairs of 128-row tiles
+    const int ntiles = n0 + n1 + n2 + n3;
     const int NTr = GATEUP ? a.I / 64 : a.H / kBN;
     const int NTs = GATEUP ? a.Is / 64 : a.H / kBN;
     const int NT = NTr > NTs ? NTr : NTs;
@@ -240,19 +241,26 @@ __global__ __launch_bounds__(kMfmaThreads) void expert_mfma_kernel(ExpertArgs a)
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
         int tile = item / NT;
         const int nt = item - tile * NT;
-        int list = 0;
+        int list = 0, half = 0;
         if (tile >= n0) {
             tile -= n0;
             list = 1;
             if (tile >= n1) {
                 tile -= n1;
                 list = 2;
+                if (tile >= n2) {
+                    tile -= n2;
+                    list = 3;
+                    half = tile & 1;
+                    tile >>= 1;
+                }
             }
         }
         const int32_t* tl = a.mfma_list + 2 * (size_t)list * a.mfma_cap;
         const Group g = a.groups[tl[2 * tile]];
         if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
-        const int m0 = tl[2 * tile + 1];
+        const int m0 = tl[2 * tile + 1] + 128 * half;
+        if (m0 >= g.n) continue;
         if (W4 && g.expert >= 0)
             mfma_tile<1, GATEUP>(a, sm, g, m0, nt);
         else
@@ -268,7 +276,7 @@ static int mfma_grid(int num_cu, long long ub) {
 
 void launch_gateup_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st) {
     const int nt = (a.I > a.Is ? a.I : a.Is) / 64;
-    const int grid = mfma_grid(num_cu, 3LL * max_tiles * nt);
+    const int grid = mfma_grid(num_cu, 5LL * max_tiles * nt);
     const size_t lds = sizeof(TileSmem);
     if (a.fmt) {
         allow_lds(expert_mfma_kernel<1, true>, lds);
@@ -281,7 +289,7 @@ void launch_gateup_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStrea
 
 void launch_down_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st) {
     const int nt = a.H / kBN;
-    const int grid = mfma_grid(num_cu, 3LL * max_tiles * nt);
+    const int grid = mfma_grid(num_cu, 5LL * max_tiles * nt);
     const size_t lds = sizeof(TileSmem);
     if (a.fmt) {
         allow_lds(expert_mfma_kernel<1, false>, lds);

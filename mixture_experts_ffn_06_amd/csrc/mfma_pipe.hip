@@ -7,9 +7,10 @@
 // engine (tracker) #593": fused gate/up rows 2w wide; grouped experts on
 // prompt rows.
 //
-// A block of 4 waves owns a BM x 128 output tile of one group (BM = 128, 64
-// or 32, chosen per tile from the rows it covers, so a small group does not
-// pay for 128 rows of matrix work) and walks K in steps of 64.  Tiles of A
+// A block owns a BM x 128 output tile of one group (BM = 256 with 8 waves, or
+// 128, 64, 32 with 4 waves; chosen per tile from the rows it covers, so a
+// small group does not pay for 256 rows of matrix work and a large one reads
+// each weight tile once per 256 rows) and walks K in steps of 64.  Tiles of A
 // (the group's rows) and B (weight rows) go straight from global memory into
 // LDS with global_load_lds_dwordx4 (16 bytes per lane, a wave filling 1 KiB =
 // 8 rows of 128 bytes), S steps in flight.  In LDS a row's eight 16-byte
@@ -29,22 +30,24 @@ typedef float f32x4_p __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) const bf16x8_p lds_bf16x8;
 
-constexpr int kPipeThreads = 256;
 constexpr int kBTileBytes = kBN * kBK * 2;  // 16 KiB of weight rows per stage
 
 template <int BM>
 struct PipeCfg {
-    static constexpr int WM = BM == 128 ? 2 : 1;  // waves along M
-    static constexpr int WN = 4 / WM;             // waves along N
-    static constexpr int MT = BM / WM / 16;       // 16-row subtiles per wave
-    static constexpr int NT = kBN / WN / 16;      // 16-column subtiles per wave
-    static constexpr int S = BM == 64 ? 3 : 4;    // stages in flight
-    static constexpr int LA = BM / 32;            // A loads per wave per stage
-    static constexpr int L = LA + 4;              // all loads per wave per stage
+    static constexpr int NW = BM == 256 ? 8 : 4;                  // waves per block
+    static constexpr int WM = BM == 256 ? 4 : (BM == 128 ? 2 : 1);  // waves along M
+    static constexpr int WN = NW / WM;                            // waves along N
+    static constexpr int MT = BM / WM / 16;                       // 16-row subtiles per wave
+    static constexpr int NT = kBN / WN / 16;                      // 16-column subtiles per wave
+    static constexpr int S = BM == 256 ? 3 : (BM == 128 ? 2 : (BM == 64 ? 3 : 4));  // stages
+    static constexpr int LA = BM / 8 / NW;                        // A loads per wave per stage
+    static constexpr int LB = kBN / 8 / NW;                       // B loads per wave per stage
+    static constexpr int L = LA + LB;                             // all loads per wave per stage
     static constexpr int ATile = BM * kBK * 2;
     static constexpr int Stage = ATile + kBTileBytes;
     static constexpr int Lds = S * Stage;
     static constexpr int PerCU = Lds <= 80 * 1024 ? 2 : 1;
+    static constexpr int Threads = 64 * NW;
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -67,16 +70,16 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
     const int rows = min(BM, g.n - m0);
     const int KT = K / kBK;
 
-    // Load sources.  Load j of this wave fills tile rows 8 (wave + 4 j) .. +7;
-    // lane l writes physical chunk l % 8 of row 8 (wave + 4 j) + l / 8, which
+    // Load sources.  Load j of this wave fills tile rows 8 (wave + NW j) .. +7;
+    // lane l writes physical chunk l % 8 of row 8 (wave + NW j) + l / 8, which
     // holds logical chunk (l % 8) ^ (row % 8).
     const uint16_t* asrc[C::LA];
-    const uint16_t* bsrc[4];
+    const uint16_t* bsrc[C::LB];
     const uint16_t* wbase = GATEUP ? (shared ? a.swgu : a.wgu + (size_t)g.expert * 2 * Ig * H)
                                    : (shared ? a.swd : a.wd + (size_t)g.expert * H * Ig);
 #pragma unroll
     for (int j = 0; j < C::LA; ++j) {
-        const int r = 8 * (wave + 4 * j) + (lane >> 3);
+        const int r = 8 * (wave + C::NW * j) + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
         const int rr = r < rows ? r : 0;  // rows past the group reload row 0 (never stored)
         const uint16_t* arow;
@@ -89,8 +92,8 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         asrc[j] = arow + 8 * c;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 8 * (wave + 4 * j) + (lane >> 3);
+    for (int j = 0; j < C::LB; ++j) {
+        const int r = 8 * (wave + C::NW * j) + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
         int brow;
         if (GATEUP)
@@ -105,11 +108,11 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         const int k0 = kt * kBK;
 #pragma unroll
         for (int j = 0; j < C::LA; ++j)
-            __builtin_amdgcn_global_load_lds(asrc[j] + k0, st + (wave + 4 * j) * 1024, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(asrc[j] + k0, st + (wave + C::NW * j) * 1024, 16, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_global_load_lds(bsrc[j] + k0, st + C::ATile + (wave + 4 * j) * 1024, 16,
-                                             0, 0);
+        for (int j = 0; j < C::LB; ++j)
+            __builtin_amdgcn_global_load_lds(bsrc[j] + k0, st + C::ATile + (wave + C::NW * j) * 1024,
+                                             16, 0, 0);
     };
 
     f32x4_p acc[C::MT][C::NT];
@@ -214,11 +217,11 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
 }
 
 template <bool GATEUP, int BM>
-__global__ __launch_bounds__(kPipeThreads) void expert_mfma_pipe_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(PipeCfg<BM>::Threads) void expert_mfma_pipe_kernel(ExpertArgs a) {
     using C = PipeCfg<BM>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::Lds];
     lds_u8* smem = (lds_u8*)smem_raw;
-    constexpr int list = BM == 128 ? 0 : (BM == 64 ? 1 : 2);
+    constexpr int list = BM == 256 ? 3 : (BM == 128 ? 0 : (BM == 64 ? 1 : 2));
     const int ntiles = a.plan_counts[1 + list];
     const int32_t* tl = a.mfma_list + 2 * (size_t)list * a.mfma_cap;
     // Every tile gets the same number of column tiles (the larger of the
@@ -243,15 +246,17 @@ static void launch_pipe_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
     const long long ub = (long long)a.mfma_cap * NT;
     if (ub < grid) grid = ub;
     if (grid < 1) grid = 1;
-    expert_mfma_pipe_kernel<GATEUP, BM><<<(int)grid, kPipeThreads, 0, st>>>(a);
+    expert_mfma_pipe_kernel<GATEUP, BM><<<(int)grid, C::Threads, 0, st>>>(a);
 }
 
 void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st) {
     if (gateup) {
+        launch_pipe_bm<true, 256>(a, num_cu, st);
         launch_pipe_bm<true, 128>(a, num_cu, st);
         launch_pipe_bm<true, 64>(a, num_cu, st);
         launch_pipe_bm<true, 32>(a, num_cu, st);
     } else {
+        launch_pipe_bm<false, 256>(a, num_cu, st);
         launch_pipe_bm<false, 128>(a, num_cu, st);
         launch_pipe_bm<false, 64>(a, num_cu, st);
         launch_pipe_bm<false, 32>(a, num_cu, st);

@@ -43,8 +43,8 @@ Layout make_layout(int T, int H, int E, int I, int Is, int k) {
     L.blkcnt = o; o += align_up(nblk * E * 4);
     L.groups = o; o += align_up(((size_t)E + 1) * sizeof(moe::Group));
     L.gemv_list = o; o += align_up(((size_t)E + 1) * 4);
-    L.mfma_list = o; o += align_up(3 * (size_t)max_mfma_tiles(T, E, k) * 8);
-    L.plan_counts = o; o += align_up(16);
+    L.mfma_list = o; o += align_up(4 * (size_t)max_mfma_tiles(T, E, k) * 8);
+    L.plan_counts = o; o += align_up(32);
     L.h_r = o; o += align_up(Tk * I * 2);
     L.h_s = o; o += align_up((size_t)T * (Is > 0 ? Is : 0) * 2);
     L.y_r = o; o += align_up(Tk * H * 4);
