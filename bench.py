@@ -58,6 +58,48 @@ class Hip:
         return float(ms.value)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_prefill.txt")
+KERNEL_SOURCES = {
+    "gemv": ["mixture_experts_ffn_06_amd/csrc/gemv.hip", "mixture_experts_ffn_06_amd/csrc/common.h"],
+    "pipe": ["mixture_experts_ffn_06_amd/csrc/mfma_pipe.hip", "mixture_experts_ffn_06_amd/csrc/common.h"],
+}
+
+
+def _source_hash(files):
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernels):
+    """HBM bytes per launch of `kernels` (summed) from the committed counter
+    summary: FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain
+    copy of known size.  None when a kernel has no line for this workload or
+    its sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    table = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) == 5 and f[0] == "traffic":
+                table[(f[1], f[2])] = (int(f[3]), f[4])
+    total = 0
+    for k in kernels:
+        hit = table.get((workload, k))
+        if hit is None:
+            return None
+        fam = "gemv" if "gemv" in k else "pipe"
+        if hit[1] != _source_hash(KERNEL_SOURCES[fam]):
+            return None
+        total += hit[0]
+    return total
+
+
 def _expert_gu_bytes(w):
     if w.fmt == "bf16":
         return 2 * w.I * w.H * 2
@@ -86,10 +128,15 @@ def roofline_for(w, counts, stage_ms):
     flops = 2.0 * routed * 2 * w.I * w.H + 2.0 * sh_rows * 2 * w.Is * w.H
     if w.T <= 8:
         kernel, ms = f"gateup_gemv_kernel<{0 if w.fmt == 'bf16' else 1},12>", stage_ms["gu_gemv"]
+        traffic = measured_traffic(w.name, [f"moe::{kernel}"])
     else:
         kernel = ("expert_mfma_pipe_kernel<true,256|128|64|32>" if w.fmt == "bf16"
                   else "expert_mfma_kernel<1,true>")
         ms = stage_ms["gu_mfma"]
+        traffic = None
+        if w.fmt == "bf16":
+            traffic = measured_traffic(
+                w.name, [f"moe::expert_mfma_pipe_kernel<true,{bm}>" for bm in (256, 128, 64, 32)])
         # rows on the GEMV path (groups of 1..8 rows) are not in this launch
         small = counts[(counts > 0) & (counts <= 8)]
         n_touched -= int(small.numel())
@@ -110,14 +157,14 @@ def roofline_for(w, counts, stage_ms):
                "frac": round(gbs / HBM_PEAK_GBS, 4)}
     else:
         out = {"bound": "mfma", **mfma}
-    out.update({"traffic": None, "kernel": kernel, "kernel_us": round(ms * 1e3, 2),
+    out.update({"traffic": traffic, "kernel": kernel, "kernel_us": round(ms * 1e3, 2),
                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                 "touched_experts": n_touched, "mfma": mfma,
                 "floor_us": round(max(t_bytes, t_flops) * 1e6, 2)})
     return out
 
 
-def cpu_baseline(w, d, ex, rows_budget):
+def cpu_baseline(w, d, ex, rows_budget, min_seconds=10.0):
     """The oracle, as it stands, on a bounded sample of rows of the workload."""
     import torch
 
@@ -136,14 +183,19 @@ def cpu_baseline(w, d, ex, rows_budget):
               "shared": None if d["shared"] is None else {k: v.cpu() for k, v in d["shared"].items()}}
     ex_o = orc.Experts(experts, w.E, w.H, w.I)
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    t0 = time.perf_counter()
-    orc.moe_ffn(inputs, w.E, w.I, w.Is, w.band_lo, w.band_hi, w.topk,
-                rows=torch.tensor(rows, dtype=torch.int32), experts=ex_o)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(rows) / dt, 3), "unit": "rows/s", "cores": min(threads, len(rows)),
+    rows_t = torch.tensor(rows, dtype=torch.int32)
+    # the sample is run again until about min_seconds of host time are spent
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.moe_ffn(inputs, w.E, w.I, w.Is, w.band_lo, w.band_hi, w.topk, rows=rows_t, experts=ex_o)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(reps * len(rows) / dt, 3), "unit": "rows/s", "cores": min(threads, len(rows)),
             "threads_available": threads, "kind": "oracle",
-            "sample": f"rows 0..{len(rows) - 1} of the {w.name} workload (fp64 per-row oracle, "
-                      f"OpenMP over rows), {dt:.2f} s"}
+            "sample": f"rows 0..{len(rows) - 1} of the {w.name} workload, run {reps} times "
+                      f"(fp64 per-row oracle, OpenMP over rows), {dt:.2f} s"}
 
 
 def main():
@@ -156,6 +208,9 @@ def main():
                     help="how L2 and MALL are evicted before each step (1 GiB scratch read or write)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB five times (a known byte "
+                         "count for calibrating HBM byte counters), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -164,6 +219,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones((n,), dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)  # reads and writes n*4 bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                          "launches": 5}), flush=True)
+        return
 
     import mixture_experts_ffn_06_amd as moe
     import synth
