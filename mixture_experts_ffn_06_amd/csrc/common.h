@@ -130,9 +130,13 @@ void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStre
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
 void launch_gateup_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
 void launch_down_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
-// bf16 experts: the direct-to-LDS pipelined tiles of 128, 64 and 32 rows
-// (gate/up or down), one launch per tile height.
+// bf16 experts: the direct-to-LDS pipelined tiles of 256, 128, 64 and 32
+// rows (gate/up or down), one launch per tile height.  With 4-bit experts
+// these launches run the (bf16) shared expert's tiles only.
 void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st);
+// 4-bit experts: the same pipeline with the codes dequantized in LDS, tiles
+// of 128 (and 256 as two halves), 64 and 32 rows; then the shared expert.
+void launch_mfma_w4(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st);
 void launch_combine(const float* y_r, const float* y_s, const int32_t* pos, const float* w,
                     int T, int H, int k, float* out, hipStream_t st);
 

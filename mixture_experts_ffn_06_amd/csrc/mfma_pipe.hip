@@ -27,6 +27,7 @@ namespace moe {
 
 typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
 typedef float f32x4_p __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_p __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) const bf16x8_p lds_bf16x8;
 
@@ -56,6 +57,31 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
 }
+
+// Walk of (tile, column tile) items for tile lists whose tiles mostly belong
+// to different experts.  Workgroups are dealt to the 8 XCDs round-robin by
+// index; here XCD x takes tiles x, x + 8, ... with all their column tiles, in
+// tile-major order over its own blocks, so a tile's A rows are fetched into
+// one XCD's L2 once and then served to every column tile from there (the
+// weights, read once per item either way, are not shared across tiles).
+struct XcdWalk {
+    int x, l, g8, NT, ntiles, j;
+    __device__ XcdWalk(int ntiles_, int NT_) : NT(NT_), ntiles(ntiles_) {
+        x = blockIdx.x & 7;
+        l = blockIdx.x >> 3;
+        g8 = gridDim.x >> 3;
+        j = l;
+    }
+    // next item of this block: false when its XCD has none left
+    __device__ bool next(int* tile, int* nt) {
+        const int t = x + 8 * (j / NT);
+        if (t >= ntiles) return false;
+        *tile = t;
+        *nt = j % NT;
+        j += g8;
+        return true;
+    }
+};
 
 template <bool GATEUP, int BM>
 __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int m0, int nt) {
@@ -166,20 +192,23 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         __builtin_amdgcn_s_barrier();  // stage kt visible to all waves; stage kt-1 free
         if (kt + C::S - 1 < KT) issue(kt + C::S - 1);
         const lds_u8* st = smem + (kt % C::S) * C::Stage;
+        // the step's operand reads first, then its MFMAs
+        bf16x8_p af[2][C::MT], bfr[2][C::NT];
 #pragma unroll
         for (int ks = 0; ks < kBK / 32; ++ks) {
             const int q = ks * 4 + (lane >> 4);  // logical 16-byte chunk of the operand
-            bf16x8_p af[C::MT], bfr[C::NT];
 #pragma unroll
-            for (int i = 0; i < C::MT; ++i) af[i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
+            for (int i = 0; i < C::MT; ++i) af[ks][i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j) bfr[j] = *(lds_bf16x8*)(st + boff[j] + ((q ^ bx[j]) << 4));
+            for (int j = 0; j < C::NT; ++j) bfr[ks][j] = *(lds_bf16x8*)(st + boff[j] + ((q ^ bx[j]) << 4));
+        }
+#pragma unroll
+        for (int ks = 0; ks < kBK / 32; ++ks)
 #pragma unroll
             for (int i = 0; i < C::MT; ++i)
 #pragma unroll
                 for (int j = 0; j < C::NT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
     }
 
     // Epilogue.  Lane holds D[4 (lane >> 4) + v][lane & 15] of each 16x16 subtile.
@@ -229,12 +258,22 @@ __global__ __launch_bounds__(PipeCfg<BM>::Threads) void expert_mfma_pipe_kernel(
     const int NTr = GATEUP ? a.I / 64 : a.H / kBN;
     const int NTs = GATEUP ? a.Is / 64 : a.H / kBN;
     const int NT = NTr > NTs ? NTr : NTs;
-    const int total = ntiles * NT;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int tile = item / NT, nt = item - tile * NT;
+    auto run = [&](int tile, int nt) {
         const Group g = a.groups[tl[2 * tile]];
-        if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
+        if (nt >= (g.expert < 0 ? NTs : NTr)) return;
+        if (a.fmt != 0 && g.expert >= 0) return;  // 4-bit experts: expert_mfma_w4_kernel
         pipe_tile<GATEUP, BM>(a, smem, g, tl[2 * tile + 1], nt);
+    };
+    if (BM == 256) {
+        // Large groups have several 256-row tiles: column tile nt of all of
+        // them runs on XCD nt mod 8 (NT and the grid are multiples of 8 at
+        // the usual widths), whose L2 then serves the shared weight rows.
+        const int total = ntiles * NT;
+        for (int item = blockIdx.x; item < total; item += gridDim.x) run(item / NT, item % NT);
+    } else {
+        XcdWalk w(ntiles, NT);
+        int tile, nt;
+        while (w.next(&tile, &nt)) run(tile, nt);
     }
 }
 
@@ -245,7 +284,7 @@ static void launch_pipe_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
     long long grid = (long long)num_cu * C::PerCU;
     const long long ub = (long long)a.mfma_cap * NT;
     if (ub < grid) grid = ub;
-    if (grid < 1) grid = 1;
+    grid = grid < 8 ? 8 : grid & ~7LL;  // the XCD walk deals blocks in groups of 8
     expert_mfma_pipe_kernel<GATEUP, BM><<<(int)grid, C::Threads, 0, st>>>(a);
 }
 
@@ -261,6 +300,263 @@ void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t 
         launch_pipe_bm<false, 64>(a, num_cu, st);
         launch_pipe_bm<false, 32>(a, num_cu, st);
     }
+}
+
+// ---- 4-bit experts ---------------------------------------------------------
+//
+// Blocks of 4 waves for BM = 128, 64, 32 (a 256-row tile runs as two 128-row
+// halves); wave w owns all BM rows and 32 columns (16 gate and the matching 16
+// up columns, or 32 down columns), so no two waves expand the same weights.
+// Per K step of 64 a stage holds the A rows (bf16, as above), the weight codes
+// (128 rows x 32 bytes) and each row's scale and zero for the step's two
+// 32-input groups, all loaded straight into LDS.  A wave expands its own B
+// operand in registers just before the MFMAs that use it:
+// (1024 + q) as an fp16 pair per two codes (one AND and one OR), then
+// v_fma_mix ((1024 + q) s - (1024 + z) s, exact in fp32: both products fit in
+// 24 bits) and v_cvt_pk_bf16_f32 (round to nearest even) -- the bf16 weight
+// RNE((q - z) s).
+
+template <int BM>
+struct W4Cfg {
+    static constexpr int NW = 4;
+    static constexpr int WN = 4;                         // waves along N (each 32 columns)
+    static constexpr int MT = BM / 16;                   // 16-row subtiles per wave
+    static constexpr int NT = 2;                         // 16-column subtiles per wave
+    static constexpr int S = BM == 128 ? 3 : (BM == 64 ? 4 : 6);  // stages
+    static constexpr int LA = BM / 32;                   // A loads per wave per stage
+    static constexpr int L = LA + 2;                     // + codes + scales or zeros
+    static constexpr int ATile = BM * kBK * 2;
+    static constexpr int QOff = ATile;                   // 128 rows x 32 bytes of codes
+    static constexpr int SOff = QOff + 4096;             // 128 rows x 2 bf16 scales
+    static constexpr int ZOff = SOff + 512;              // 128 rows x 2 bf16 zeros
+    static constexpr int Stage = ZOff + 512;
+    static constexpr int Lds = S * Stage;
+    static constexpr int PerCU = Lds <= 80 * 1024 ? 2 : 1;
+    static constexpr int Threads = 64 * NW;
+};
+
+typedef _Float16 f16x2_p __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_p __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    const bf16x2_p v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight codes (one word, k = 0..7 in nibbles 0..7) -> eight bf16 weights.
+__device__ __forceinline__ bf16x8_p dequant8(uint32_t c, float s, float n) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // fp16 pair (1024 + q_j, 1024 + q_{j+4})
+        const f16x2_p h = __builtin_bit_cast(f16x2_p, ((c >> (4 * j)) & 0x000f000fu) | 0x64006400u);
+        v[j] = fmaf((float)h.x, s, n);
+        v[j + 4] = fmaf((float)h.y, s, n);
+    }
+    const u32x4_p o = {pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]),
+                       pack2_bf16(v[6], v[7])};
+    return __builtin_bit_cast(bf16x8_p, o);
+}
+
+template <bool GATEUP, int BM>
+__device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, int m0, int nt) {
+    using C = W4Cfg<BM>;
+    typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Ig = a.I;
+    const int H = a.H;
+    const int K = GATEUP ? H : Ig;
+    const int rows = min(BM, g.n - m0);
+    const int KT = K / kBK;
+
+    const uint16_t* asrc[C::LA];
+#pragma unroll
+    for (int j = 0; j < C::LA; ++j) {
+        const int r = 8 * (wave + C::NW * j) + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const int rr = r < rows ? r : 0;
+        const uint16_t* arow;
+        if (GATEUP)
+            arow = a.x + (size_t)(a.perm[g.row0 + m0 + rr] / a.topk) * H;
+        else
+            arow = a.h_r + (size_t)(g.row0 + m0 + rr) * a.I;
+        asrc[j] = arow + 8 * c;
+    }
+    // Wave w loads the codes of rows 32 w .. 32 w + 31 (lane: row 32 w + l / 2,
+    // half l % 2, 16 bytes), and waves 0-1 the scales, 2-3 the zeros of
+    // 64 rows each (4 bytes a lane: both groups of the step).
+    auto wrow = [&](int r) -> size_t {
+        const int row = GATEUP ? (r < 64 ? nt * 64 + r : Ig + nt * 64 + (r - 64)) : nt * kBN + r;
+        return (size_t)g.expert * (GATEUP ? 2 * (size_t)Ig : (size_t)H) + row;
+    };
+    const unsigned char* qsrc =
+        (GATEUP ? a.qgu : a.qd) + wrow(32 * wave + (lane >> 1)) * (K / 2) + 16 * (lane & 1);
+    const uint16_t* szbase = wave < 2 ? (GATEUP ? a.sgu : a.sd) : (GATEUP ? a.zgu : a.zd);
+    const unsigned char* szsrc = (const unsigned char*)(szbase + wrow(64 * (wave & 1) + lane) * (K / 32));
+    const int szdst = (wave < 2 ? C::SOff : C::ZOff) + (wave & 1) * 256;
+
+    auto issue = [&](int kt) {
+        lds_u8* st = smem + (kt % C::S) * C::Stage;
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int j = 0; j < C::LA; ++j)
+            __builtin_amdgcn_global_load_lds(asrc[j] + k0, st + (wave + C::NW * j) * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(qsrc + (size_t)kt * 32, st + C::QOff + wave * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(szsrc + (size_t)kt * 4, st + szdst, 4, 0, 0);
+    };
+
+    f32x4_p acc[C::MT][C::NT];
+#pragma unroll
+    for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) acc[i][j] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+    int aoff[C::MT], ax[C::MT], brow[C::NT];
+#pragma unroll
+    for (int i = 0; i < C::MT; ++i) {
+        const int r = 16 * i + (lane & 15);
+        aoff[i] = r * 128;
+        ax[i] = r & 7;
+    }
+#pragma unroll
+    for (int j = 0; j < C::NT; ++j)
+        brow[j] = (GATEUP ? (j == 0 ? 0 : 64) + 16 * wave : 32 * wave + 16 * j) + (lane & 15);
+
+    __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
+#pragma unroll
+    for (int s = 0; s < C::S - 1; ++s)
+        if (s < KT) issue(s);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int after = min(C::S - 2, KT - 1 - kt);
+        if (after >= 4)
+            wait_vmcnt<4 * C::L>();
+        else if (after == 3)
+            wait_vmcnt<3 * C::L>();
+        else if (after == 2)
+            wait_vmcnt<2 * C::L>();
+        else if (after == 1)
+            wait_vmcnt<C::L>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // stage kt visible to all waves; stage kt-1 free
+        if (kt + C::S - 1 < KT) issue(kt + C::S - 1);
+        const lds_u8* st = smem + (kt % C::S) * C::Stage;
+        // Every LDS read of the step first (one wait), then the expansion,
+        // then the MFMAs.
+        uint32_t sw[C::NT], zw[C::NT], codes[2][C::NT];
+        bf16x8_p af[2][C::MT];
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) {
+            sw[j] = *(lds_u32*)(st + C::SOff + brow[j] * 4);
+            zw[j] = *(lds_u32*)(st + C::ZOff + brow[j] * 4);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int q = ks * 4 + (lane >> 4);  // logical 16-byte chunk = 8 codes of k
+#pragma unroll
+            for (int j = 0; j < C::NT; ++j) codes[ks][j] = *(lds_u32*)(st + C::QOff + brow[j] * 32 + 4 * q);
+#pragma unroll
+            for (int i = 0; i < C::MT; ++i) af[ks][i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
+        }
+        bf16x8_p bfr[2][C::NT];
+#pragma unroll
+        for (int j = 0; j < C::NT; ++j) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                // scale and zero of this lane's column for group ks of the step
+                const float sc = __uint_as_float(ks ? (sw[j] & 0xffff0000u) : (sw[j] << 16));
+                const float zz = __uint_as_float(ks ? (zw[j] & 0xffff0000u) : (zw[j] << 16));
+                bfr[ks][j] = dequant8(codes[ks][j], sc, -((1024.0f + zz) * sc));
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+    }
+
+    if (GATEUP) {
+        uint16_t* hout = a.h_r + (size_t)(g.row0 + m0) * a.I;
+        const int c = nt * 64 + 16 * wave + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * i + 4 * (lane >> 4) + v;
+                if (r < rows) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(acc[i][0][v], acc[i][1][v]));
+            }
+    } else {
+        float* yout = a.y_r + (size_t)(g.row0 + m0) * H;
+#pragma unroll
+        for (int i = 0; i < C::MT; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * i + 4 * (lane >> 4) + v;
+                if (r >= rows) continue;
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j)
+                    yout[(size_t)r * H + nt * kBN + 32 * wave + 16 * j + (lane & 15)] = acc[i][j][v];
+            }
+    }
+}
+
+// Routed 4-bit groups only (the shared expert is bf16 and runs in
+// expert_mfma_pipe_kernel).  BM = 128 also takes the 256-row list, each tile
+// as two 128-row halves.
+template <bool GATEUP, int BM>
+__global__ __launch_bounds__(W4Cfg<BM>::Threads) void expert_mfma_w4_kernel(ExpertArgs a) {
+    using C = W4Cfg<BM>;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::Lds];
+    lds_u8* smem = (lds_u8*)smem_raw;
+    constexpr int list = BM == 128 ? 0 : (BM == 64 ? 1 : 2);
+    const int n0 = a.plan_counts[1 + list];
+    const int n3 = BM == 128 ? 2 * a.plan_counts[4] : 0;
+    const int NT = GATEUP ? a.I / 64 : a.H / kBN;
+    XcdWalk w(n0 + n3, NT);
+    int tile, nt;
+    while (w.next(&tile, &nt)) {
+        int l = list, half = 0;
+        if (tile >= n0) {
+            tile -= n0;
+            l = 3;
+            half = tile & 1;
+            tile >>= 1;
+        }
+        const int32_t* tl = a.mfma_list + 2 * (size_t)l * a.mfma_cap;
+        const Group g = a.groups[tl[2 * tile]];
+        if (g.expert < 0) continue;  // the shared expert is bf16
+        const int m0 = tl[2 * tile + 1] + 128 * half;
+        if (m0 >= g.n) continue;
+        pipe_tile_w4<GATEUP, BM>(a, smem, g, m0, nt);
+    }
+}
+
+template <bool GATEUP, int BM>
+static void launch_w4_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
+    using C = W4Cfg<BM>;
+    const int NT = GATEUP ? a.I / 64 : a.H / kBN;
+    long long grid = (long long)num_cu * C::PerCU;
+    const long long ub = (long long)(BM == 128 ? 3 : 1) * a.mfma_cap * NT;
+    if (ub < grid) grid = ub;
+    grid = grid < 8 ? 8 : grid & ~7LL;  // the XCD walk deals blocks in groups of 8
+    expert_mfma_w4_kernel<GATEUP, BM><<<(int)grid, C::Threads, 0, st>>>(a);
+}
+
+void launch_mfma_w4(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st) {
+    if (gateup) {
+        launch_w4_bm<true, 128>(a, num_cu, st);
+        launch_w4_bm<true, 64>(a, num_cu, st);
+        launch_w4_bm<true, 32>(a, num_cu, st);
+    } else {
+        launch_w4_bm<false, 128>(a, num_cu, st);
+        launch_w4_bm<false, 64>(a, num_cu, st);
+        launch_w4_bm<false, 32>(a, num_cu, st);
+    }
+    if (a.Is > 0) launch_mfma_pipe(a, gateup, num_cu, st);  // the bf16 shared expert
 }
 
 }  // namespace moe

@@ -250,7 +250,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
         if (fmt == MOE_BF16)
             moe::launch_mfma_pipe(a, true, num_cu, st);
         else
-            moe::launch_gateup_mfma(a, max_tiles, num_cu, st);
+            moe::launch_mfma_w4(a, true, num_cu, st);
     }
     mark(MOE_EV_DN_GEMV);
     moe::launch_down_gemv(a, max_groups, num_cu, st);
@@ -259,7 +259,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
         if (fmt == MOE_BF16)
             moe::launch_mfma_pipe(a, false, num_cu, st);
         else
-            moe::launch_down_mfma(a, max_tiles, num_cu, st);
+            moe::launch_mfma_w4(a, false, num_cu, st);
     }
     mark(MOE_EV_COMBINE);
     moe::launch_combine(a.y_r, has_shared ? a.y_s : nullptr, pos, wts, T, H, topk, out->y, st);
