@@ -131,7 +131,7 @@ def roofline_for(w, counts, stage_ms):
         traffic = measured_traffic(w.name, [f"moe::{kernel}"])
     else:
         kernel = ("expert_mfma_pipe_kernel<true,256|128|64|32>" if w.fmt == "bf16"
-                  else "expert_mfma_kernel<1,true>")
+                  else "expert_mfma_w4_kernel<true,128|64|32> + shared expert_mfma_pipe_kernel")
         ms = stage_ms["gu_mfma"]
         traffic = None
         if w.fmt == "bf16":

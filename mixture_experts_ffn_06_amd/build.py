@@ -16,8 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoeffn.so")
 
-SOURCES = ["router.hip", "dispatch.hip", "gemv.hip", "mfma.hip", "mfma_pipe.hip", "combine.hip",
-           "moe_ffn.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "gemv.hip", "mfma_pipe.hip", "combine.hip", "moe_ffn.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -128,8 +128,6 @@ void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_
                      int mfma_cap, int32_t* plan_counts, hipStream_t st);
 void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
-void launch_gateup_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
-void launch_down_mfma(const ExpertArgs& a, int max_tiles, int num_cu, hipStream_t st);
 // bf16 experts: the direct-to-LDS pipelined tiles of 256, 128, 64 and 32
 // rows (gate/up or down), one launch per tile height.  With 4-bit experts
 // these launches run the (bf16) shared expert's tiles only.

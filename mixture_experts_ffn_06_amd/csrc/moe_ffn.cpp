@@ -241,7 +241,6 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     const long long picks = (long long)T * topk;
     const int max_groups = (int)((picks < nb ? picks : nb) + (has_shared ? 1 : 0));
     const bool mfma_possible = T > moe::kSmallRows;
-    const int max_tiles = max_mfma_tiles(T, nb, topk);
 
     mark(MOE_EV_GU_GEMV);
     moe::launch_gateup_gemv(a, max_groups, num_cu, st);
