@@ -81,11 +81,11 @@ __device__ void build_plan(const int cnt[2], const int run[2], int nb, int T, in
                            int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list,
                            int mfma_cap, int32_t* __restrict__ plan_counts, int* s_tmp) {
     const int tid = threadIdx.x;
-    // A group of 1..8 rows goes to the GEMV path.  A larger group is cut into
-    // 256-row tiles; the rest (r rows) becomes a 128-row tile when r > 128
-    // plus one tile of 128, 64 or 32 rows for what is left, by its size.
+    // A group of 1..8 rows goes to the GEMV path; one of 9..32, 33..64 or
+    // 65..128 rows is one tile of 32, 64 or 128 rows; a larger one is cut into
+    // 256-row tiles, the last one partial.  Every group is in exactly one
+    // list, so one launch reads each expert's weights.
     int n[2], gv[2], t256[2], t128[2], t64[2], t32[2];
-    int m128a[2], m128b[2], mlast[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int e = 2 * tid + q;
@@ -97,31 +97,12 @@ __device__ void build_plan(const int cnt[2], const int run[2], int nb, int T, in
             n[q] = T;
             groups[e] = Group{-1, 0, T, 0};
         }
-        gv[q] = (n[q] >= 1 && n[q] <= kSmallRows) ? 1 : 0;
-        const int big = n[q] > kSmallRows;
-        const int full = big ? n[q] / 256 : 0;
-        int rem = big ? n[q] % 256 : 0;
-        int m0 = full * 256;
-        t256[q] = full;
-        t128[q] = 0;
-        t64[q] = 0;
-        t32[q] = 0;
-        m128a[q] = m128b[q] = mlast[q] = 0;
-        if (rem > 128) {
-            m128a[q] = m0;
-            t128[q] = 1;
-            m0 += 128;
-            rem -= 128;
-        }
-        mlast[q] = m0;
-        if (rem > 64) {
-            if (t128[q]) m128b[q] = m0; else m128a[q] = m0;
-            t128[q] += 1;
-        } else if (rem > 32) {
-            t64[q] = 1;
-        } else if (rem > 0) {
-            t32[q] = 1;
-        }
+        const int nn = n[q];
+        gv[q] = (nn >= 1 && nn <= kSmallRows) ? 1 : 0;
+        t32[q] = (nn > kSmallRows && nn <= 32) ? 1 : 0;
+        t64[q] = (nn > 32 && nn <= 64) ? 1 : 0;
+        t128[q] = (nn > 64 && nn <= 128) ? 1 : 0;
+        t256[q] = nn > 128 ? (nn + 255) / 256 : 0;
     }
     int ngv, n256, n128, n64, n32;
     int gv0 = block_exclusive_scan(gv[0] + gv[1], s_tmp, &ngv);
@@ -143,23 +124,19 @@ __device__ void build_plan(const int cnt[2], const int run[2], int nb, int T, in
             l256[2 * (o256 + m) + 1] = m * 256;
         }
         o256 += t256[q];
-        if (t128[q] >= 1) {
+        if (t128[q]) {
             l128[2 * o128] = e;
-            l128[2 * o128 + 1] = m128a[q];
-        }
-        if (t128[q] == 2) {
-            l128[2 * o128 + 2] = e;
-            l128[2 * o128 + 3] = m128b[q];
+            l128[2 * o128 + 1] = 0;
         }
         o128 += t128[q];
         if (t64[q]) {
             l64[2 * o64] = e;
-            l64[2 * o64 + 1] = mlast[q];
+            l64[2 * o64 + 1] = 0;
         }
         o64 += t64[q];
         if (t32[q]) {
             l32[2 * o32] = e;
-            l32[2 * o32 + 1] = mlast[q];
+            l32[2 * o32 + 1] = 0;
         }
         o32 += t32[q];
     }

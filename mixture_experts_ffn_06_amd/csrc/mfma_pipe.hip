@@ -7,10 +7,10 @@
 // engine (tracker) #593": fused gate/up rows 2w wide; grouped experts on
 // prompt rows.
 //
-// A block owns a BM x 128 output tile of one group (BM = 256 with 8 waves, or
-// 128, 64, 32 with 4 waves; chosen per tile from the rows it covers, so a
-// small group does not pay for 256 rows of matrix work and a large one reads
-// each weight tile once per 256 rows) and walks K in steps of 64.  Tiles of A
+// A block owns a BM x BN output tile of one group (256 x 256 with 8 waves for
+// groups of more than 128 rows, the last tile partial; 128, 64 or 32 x 128
+// with 4 waves for a group that one such tile covers) and walks K in steps of
+// 64.  Tiles of A
 // (the group's rows) and B (weight rows) go straight from global memory into
 // LDS with global_load_lds_dwordx4 (16 bytes per lane, a wave filling 1 KiB =
 // 8 rows of 128 bytes), S steps in flight.  In LDS a row's eight 16-byte
@@ -31,24 +31,37 @@ typedef uint32_t u32x4_p __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) const bf16x8_p lds_bf16x8;
 
-constexpr int kBTileBytes = kBN * kBK * 2;  // 16 KiB of weight rows per stage
+constexpr int kBTileBytes = kBN * kBK * 2;  // 16 KiB of 128 weight rows per stage
 
-template <int BM>
+// BM x BN tiles.  256 x 256: 8 waves of 128 x 64 (fewer LDS operand bytes
+// per MFMA than 64 x 64 wave tiles; LDS bandwidth bounds the 64 x 64 layout
+// at full MFMA rate), two 64 KiB stages, one block per CU.  256 x 128 (when
+// there are too few 256 x 256 items to fill the chip): 8 waves of 64 x 64,
+// three stages.  128, 64, 32 x 128: 4 waves, two blocks per CU.
+template <int BM, int BN_ = (BM == 256 ? 256 : 128)>
 struct PipeCfg {
+    static constexpr int BN = BN_;                                // columns per tile
     static constexpr int NW = BM == 256 ? 8 : 4;                  // waves per block
-    static constexpr int WM = BM == 256 ? 4 : (BM == 128 ? 2 : 1);  // waves along M
+    static constexpr int WM = BM == 256 ? (BN == 256 ? 2 : 4) : (BM == 128 ? 2 : 1);  // waves along M
     static constexpr int WN = NW / WM;                            // waves along N
     static constexpr int MT = BM / WM / 16;                       // 16-row subtiles per wave
-    static constexpr int NT = kBN / WN / 16;                      // 16-column subtiles per wave
-    static constexpr int S = BM == 256 ? 3 : (BM == 128 ? 2 : (BM == 64 ? 3 : 4));  // stages
-    static constexpr int LA = BM / 8 / NW;                        // A loads per wave per stage
-    static constexpr int LB = kBN / 8 / NW;                       // B loads per wave per stage
+    static constexpr int NT = BN / WN / 16;                       // 16-column subtiles per wave
+    static constexpr int S = BM == 256 ? (BN == 256 ? 2 : 3) : (BM == 128 ? 2 : (BM == 64 ? 3 : 4));  // stages
+    static constexpr int ALoads = BM / 8;                         // A wave-loads per stage
+    static constexpr int LA = ALoads / NW;                        // A loads per wave per stage
+    static constexpr int LB = BN / 8 / NW;                        // B loads per wave per stage
     static constexpr int L = LA + LB;                             // all loads per wave per stage
     static constexpr int ATile = BM * kBK * 2;
-    static constexpr int Stage = ATile + kBTileBytes;
+    static constexpr int Stage = ATile + BN * kBK * 2;
     static constexpr int Lds = S * Stage;
     static constexpr int PerCU = Lds <= 80 * 1024 ? 2 : 1;
     static constexpr int Threads = 64 * NW;
+    static_assert(ALoads % NW == 0, "A loads per wave");
+    // column tiles of a gate/up (width w: BN / 2 gate + BN / 2 up columns) or
+    // down projection
+    static __host__ __device__ int col_tiles(bool gateup, int w, int H) {
+        return gateup ? (w + BN / 2 - 1) / (BN / 2) : H / BN;
+    }
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
@@ -83,9 +96,9 @@ struct XcdWalk {
     }
 };
 
-template <bool GATEUP, int BM>
+template <bool GATEUP, int BM, int BN>
 __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int m0, int nt) {
-    using C = PipeCfg<BM>;
+    using C = PipeCfg<BM, BN>;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -122,10 +135,15 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         const int r = 8 * (wave + C::NW * j) + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
         int brow;
-        if (GATEUP)
-            brow = r < 64 ? nt * 64 + r : Ig + nt * 64 + (r - 64);
-        else
-            brow = nt * kBN + r;
+        if (GATEUP) {
+            constexpr int hb = C::BN / 2;
+            const int col = nt * hb + (r < hb ? r : r - hb);
+            // columns past the width (I not a multiple of BN / 2) reload
+            // column 0 and are never stored
+            brow = (col < Ig ? col : 0) + (r < hb ? 0 : Ig);
+        } else {
+            brow = nt * C::BN + r;
+        }
         bsrc[j] = wbase + (size_t)brow * K + 8 * c;
     }
 
@@ -162,9 +180,9 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         int rb;
         if (GATEUP) {
             constexpr int half = C::NT / 2;
-            rb = (j < half ? 0 : 64) + wn * (64 / C::WN) + 16 * (j % half);
+            rb = (j < half ? 0 : C::BN / 2) + wn * (C::BN / 2 / C::WN) + 16 * (j % half);
         } else {
-            rb = wn * (kBN / C::WN) + 16 * j;
+            rb = wn * (C::BN / C::WN) + 16 * j;
         }
         rb += lane & 15;
         boff[j] = C::ATile + rb * 128;
@@ -183,7 +201,11 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         // Stage kt is complete once at most (stages issued after it) x L of
         // this wave's loads are still in flight.
         const int after = min(C::S - 2, KT - 1 - kt);
-        if (after >= 2)
+        if (after >= 4)
+            wait_vmcnt<4 * C::L>();
+        else if (after == 3)
+            wait_vmcnt<3 * C::L>();
+        else if (after == 2)
             wait_vmcnt<2 * C::L>();
         else if (after == 1)
             wait_vmcnt<C::L>();
@@ -192,23 +214,37 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         __builtin_amdgcn_s_barrier();  // stage kt visible to all waves; stage kt-1 free
         if (kt + C::S - 1 < KT) issue(kt + C::S - 1);
         const lds_u8* st = smem + (kt % C::S) * C::Stage;
-        // the step's operand reads first, then its MFMAs
-        bf16x8_p af[2][C::MT], bfr[2][C::NT];
+        // 16-row subtiles wholly past the group's rows do no MFMA work
+        // (wave-uniform: a partial last tile of a large group)
+        bool live[C::MT];
 #pragma unroll
-        for (int ks = 0; ks < kBK / 32; ++ks) {
-            const int q = ks * 4 + (lane >> 4);  // logical 16-byte chunk of the operand
+        for (int i = 0; i < C::MT; ++i) live[i] = wm * (BM / C::WM) + 16 * i < rows;
+        // the operand reads of both halves of the step first, then their
+        // MFMAs (one half at a time for the 128 x 64 wave tile: registers)
+        constexpr int KH = C::MT + C::NT <= 8 ? 2 : 1;
 #pragma unroll
-            for (int i = 0; i < C::MT; ++i) af[ks][i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
+        for (int k0 = 0; k0 < kBK / 32; k0 += KH) {
+            bf16x8_p af[KH][C::MT], bfr[KH][C::NT];
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j) bfr[ks][j] = *(lds_bf16x8*)(st + boff[j] + ((q ^ bx[j]) << 4));
+            for (int kh = 0; kh < KH; ++kh) {
+                const int q = (k0 + kh) * 4 + (lane >> 4);  // logical 16-byte chunk of the operand
+#pragma unroll
+                for (int i = 0; i < C::MT; ++i)
+                    if (live[i]) af[kh][i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) bfr[kh][j] = *(lds_bf16x8*)(st + boff[j] + ((q ^ bx[j]) << 4));
+            }
+#pragma unroll
+            for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+                for (int i = 0; i < C::MT; ++i)
+                    if (live[i]) {
+#pragma unroll
+                        for (int j = 0; j < C::NT; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kh][i], bfr[kh][j], acc[i][j], 0,
+                                                                                0, 0);
+                    }
         }
-#pragma unroll
-        for (int ks = 0; ks < kBK / 32; ++ks)
-#pragma unroll
-            for (int i = 0; i < C::MT; ++i)
-#pragma unroll
-                for (int j = 0; j < C::NT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
     }
 
     // Epilogue.  Lane holds D[4 (lane >> 4) + v][lane & 15] of each 16x16 subtile.
@@ -223,9 +259,10 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
                 if (r >= rows) continue;
 #pragma unroll
                 for (int j = 0; j < half; ++j) {
-                    const int c = nt * 64 + wn * (64 / C::WN) + 16 * j + (lane & 15);
-                    hout[(size_t)r * Ig + c] =
-                        f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + half][v]));
+                    const int c = nt * (C::BN / 2) + wn * (C::BN / 2 / C::WN) + 16 * j + (lane & 15);
+                    if (c < Ig)
+                        hout[(size_t)r * Ig + c] =
+                            f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + half][v]));
                 }
             }
     } else {
@@ -238,7 +275,7 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
                 if (r >= rows) continue;
 #pragma unroll
                 for (int j = 0; j < C::NT; ++j) {
-                    const int c = nt * kBN + wn * (kBN / C::WN) + 16 * j + (lane & 15);
+                    const int c = nt * C::BN + wn * (C::BN / C::WN) + 16 * j + (lane & 15);
                     yout[(size_t)r * H + c] = acc[i][j][v];
                 }
             }
@@ -248,39 +285,53 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
 template <bool GATEUP, int BM>
 __global__ __launch_bounds__(PipeCfg<BM>::Threads) void expert_mfma_pipe_kernel(ExpertArgs a) {
     using C = PipeCfg<BM>;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::Lds];
+    using CN = PipeCfg<BM, 128>;  // 256 x 128 items when 256 x 256 ones are too few
+    constexpr int kLds = C::Lds > CN::Lds ? C::Lds : CN::Lds;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kLds];
     lds_u8* smem = (lds_u8*)smem_raw;
     constexpr int list = BM == 256 ? 3 : (BM == 128 ? 0 : (BM == 64 ? 1 : 2));
     const int ntiles = a.plan_counts[1 + list];
     const int32_t* tl = a.mfma_list + 2 * (size_t)list * a.mfma_cap;
-    // Every tile gets the same number of column tiles (the larger of the
-    // routed and shared widths); items past a group's width are skipped.
-    const int NTr = GATEUP ? a.I / 64 : a.H / kBN;
-    const int NTs = GATEUP ? a.Is / 64 : a.H / kBN;
-    const int NT = NTr > NTs ? NTr : NTs;
-    auto run = [&](int tile, int nt) {
-        const Group g = a.groups[tl[2 * tile]];
-        if (nt >= (g.expert < 0 ? NTs : NTr)) return;
-        if (a.fmt != 0 && g.expert >= 0) return;  // 4-bit experts: expert_mfma_w4_kernel
-        pipe_tile<GATEUP, BM>(a, smem, g, tl[2 * tile + 1], nt);
-    };
     if (BM == 256) {
-        // Large groups have several 256-row tiles: column tile nt of all of
+        // A large group has several 256-row tiles: column tile nt of all of
         // them runs on XCD nt mod 8 (NT and the grid are multiples of 8 at
         // the usual widths), whose L2 then serves the shared weight rows.
+        // Every tile gets the same number of column tiles (the larger of the
+        // routed and shared widths); items past a group's width are skipped.
+        const bool narrow = (long long)ntiles * C::col_tiles(GATEUP, a.I > a.Is ? a.I : a.Is, a.H) < gridDim.x;
+        const int NTr = narrow ? CN::col_tiles(GATEUP, a.I, a.H) : C::col_tiles(GATEUP, a.I, a.H);
+        const int NTs = narrow ? CN::col_tiles(GATEUP, a.Is, a.H) : C::col_tiles(GATEUP, a.Is, a.H);
+        const int NT = NTr > NTs ? NTr : NTs;
         const int total = ntiles * NT;
-        for (int item = blockIdx.x; item < total; item += gridDim.x) run(item / NT, item % NT);
+        for (int item = blockIdx.x; item < total; item += gridDim.x) {
+            const int tile = item / NT, nt = item % NT;
+            const Group g = a.groups[tl[2 * tile]];
+            if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
+            if (a.fmt != 0 && g.expert >= 0) continue;  // 4-bit experts: expert_mfma_w4_kernel
+            if (narrow)
+                pipe_tile<GATEUP, BM, 128>(a, smem, g, tl[2 * tile + 1], nt);
+            else
+                pipe_tile<GATEUP, BM, C::BN>(a, smem, g, tl[2 * tile + 1], nt);
+        }
     } else {
+        const int NTr = C::col_tiles(GATEUP, a.I, a.H);
+        const int NTs = C::col_tiles(GATEUP, a.Is, a.H);
+        const int NT = NTr > NTs ? NTr : NTs;
         XcdWalk w(ntiles, NT);
         int tile, nt;
-        while (w.next(&tile, &nt)) run(tile, nt);
+        while (w.next(&tile, &nt)) {
+            const Group g = a.groups[tl[2 * tile]];
+            if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
+            if (a.fmt != 0 && g.expert >= 0) continue;  // 4-bit experts: expert_mfma_w4_kernel
+            pipe_tile<GATEUP, BM, C::BN>(a, smem, g, tl[2 * tile + 1], nt);
+        }
     }
 }
 
 template <bool GATEUP, int BM>
 static void launch_pipe_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
     using C = PipeCfg<BM>;
-    const int NT = GATEUP ? (a.I > a.Is ? a.I : a.Is) / 64 : a.H / kBN;
+    const int NT = PipeCfg<BM, 128>::col_tiles(GATEUP, a.I > a.Is ? a.I : a.Is, a.H);
     long long grid = (long long)num_cu * C::PerCU;
     const long long ub = (long long)a.mfma_cap * NT;
     if (ub < grid) grid = ub;
