@@ -122,6 +122,11 @@ void launch_router_logits(const uint16_t* x, const float* wr, const float* bias,
                           int E, float* logits, hipStream_t st);
 void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         hipStream_t st);
+// Batches of at most 16 rows: top-k and the dispatch in one block.
+void launch_topk_dispatch_small(const float* logits, int E, float* wts, int32_t* ids, int T, int k,
+                                int lo, int hi, bool has_shared, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* pos, Group* groups, int32_t* gemv_list,
+                                int32_t* mfma_list, int mfma_cap, int32_t* plan_counts, hipStream_t st);
 void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_shared,
                      int32_t* blkcnt, int32_t* counts, int32_t* offsets, int32_t* perm,
                      int32_t* pos, Group* groups, int32_t* gemv_list, int32_t* mfma_list,

@@ -16,6 +16,7 @@
 // expert's offset + the picks of earlier blocks (scanned in block order) + the
 // picks of earlier waves of the block + popcount(mask[e] below row r).
 #include "common.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
 // All of the dispatch in one block when every row fits in one block of 256
 // rows (decode): masks, counts, scan, plan and placement without a kernel
 // boundary in between.  1024 threads; threads 0..255 own the rows.
-__global__ __launch_bounds__(1024) void dispatch_small_kernel(
+__device__ __forceinline__ void dispatch_small_body(
     const int32_t* __restrict__ ids, int T, int k, int lo, int nb, bool has_shared,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
     int32_t* __restrict__ pos, Group* __restrict__ groups, int32_t* __restrict__ gemv_list,
@@ -273,6 +274,57 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
             pos[p] = -1;
         }
     }
+}
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int lo, int nb, bool has_shared,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ pos, Group* __restrict__ groups, int32_t* __restrict__ gemv_list,
+    int32_t* __restrict__ mfma_list, int mfma_cap, int32_t* __restrict__ plan_counts) {
+    dispatch_small_body(ids, T, k, lo, nb, has_shared, counts, offsets, perm, pos, groups, gemv_list,
+                        mfma_list, mfma_cap, plan_counts);
+}
+
+// Batches of at most 16 rows: top-k (wave t takes row t) and the dispatch in
+// one block; the picks go to the outputs and to LDS, where the dispatch reads
+// them.
+template <int PER>
+__global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(
+    const float* __restrict__ logits, int E, float* __restrict__ wts, int32_t* __restrict__ ids,
+    int T, int k, int lo, int nb, bool has_shared, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+    Group* __restrict__ groups, int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list,
+    int mfma_cap, int32_t* __restrict__ plan_counts) {
+    __shared__ int32_t s_ids[16 * 16];  // rows x picks (at most 16 each)
+    const int wave = threadIdx.x >> 6;
+    if (wave < T) topk_row<PER>(logits, wave, E, k, ids, wts, s_ids);
+    __syncthreads();
+    dispatch_small_body(s_ids, T, k, lo, nb, has_shared, counts, offsets, perm, pos, groups, gemv_list,
+                        mfma_list, mfma_cap, plan_counts);
+}
+
+void launch_topk_dispatch_small(const float* logits, int E, float* wts, int32_t* ids, int T, int k,
+                                int lo, int hi, bool has_shared, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* pos, Group* groups, int32_t* gemv_list,
+                                int32_t* mfma_list, int mfma_cap, int32_t* plan_counts, hipStream_t st) {
+    const int nb = hi - lo;
+    const size_t lds = sizeof(unsigned long long) * 4 * (size_t)nb + sizeof(int) * ((size_t)nb + 1);
+    const int per = (E + 63) / 64;
+#define MOE_TOPK_DISPATCH(P)                                                                          \
+    topk_dispatch_small_kernel<P><<<1, 1024, lds, st>>>(logits, E, wts, ids, T, k, lo, nb, has_shared, \
+                                                         counts, offsets, perm, pos, groups, gemv_list, \
+                                                         mfma_list, mfma_cap, plan_counts)
+    if (per <= 1)
+        MOE_TOPK_DISPATCH(1);
+    else if (per <= 2)
+        MOE_TOPK_DISPATCH(2);
+    else if (per <= 4)
+        MOE_TOPK_DISPATCH(4);
+    else if (per <= 8)
+        MOE_TOPK_DISPATCH(8);
+    else
+        MOE_TOPK_DISPATCH(16);
+#undef MOE_TOPK_DISPATCH
 }
 
 void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_shared,

@@ -200,11 +200,19 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     moe::launch_router_logits(static_cast<const uint16_t*>(x->ptr), router_w->w, router_w->bias, T,
                               H, E, logits, st);
     mark(MOE_EV_TOPK);
-    moe::launch_router_topk(logits, T, E, topk, ids, wts, st);
-    mark(MOE_EV_DISPATCH);
     const int mfma_cap = max_mfma_tiles(T, E, topk);
-    moe::launch_dispatch(ids, T, topk, band_lo, band_hi, has_shared, blkcnt, counts, offsets, perm,
-                         pos, groups, gemv_list, mfma_list, mfma_cap, plan_counts, st);
+    if (T <= 16) {
+        // one block: top-k (a wave per row) and the dispatch
+        mark(MOE_EV_DISPATCH);
+        moe::launch_topk_dispatch_small(logits, E, wts, ids, T, topk, band_lo, band_hi, has_shared, counts,
+                                        offsets, perm, pos, groups, gemv_list, mfma_list, mfma_cap,
+                                        plan_counts, st);
+    } else {
+        moe::launch_router_topk(logits, T, E, topk, ids, wts, st);
+        mark(MOE_EV_DISPATCH);
+        moe::launch_dispatch(ids, T, topk, band_lo, band_hi, has_shared, blkcnt, counts, offsets, perm,
+                             pos, groups, gemv_list, mfma_list, mfma_cap, plan_counts, st);
+    }
 
     moe::ExpertArgs a;
     memset(&a, 0, sizeof a);

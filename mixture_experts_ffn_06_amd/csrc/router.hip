@@ -11,13 +11,14 @@
 // with lane l xor 1, 2, 4, 8, 16, 32.  Every lane of a wave plays one lane of
 // that order, so a wave computes a dot in exactly that order.
 #include "common.h"
+#include "topk.h"
 
 #pragma clang fp contract(off)
 
 namespace moe {
 
-// One wave computes a tile of RB rows x EB experts; four waves per block.
-// One wave computes a tile of RB rows x EB experts; four waves per block.
+// One wave computes a tile of RB rows x EB experts.
+// One wave computes a tile of RB rows x EB experts.
 // The loads of BATCH steps of i are issued before any of them is used.
 template <int RB, int EB, int BATCH>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
                                                             float* __restrict__ logits) {
     const int lane = threadIdx.x & 63;
     // wave-uniform values live in scalar registers
-    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    const int wave = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
     const int ET = (E + EB - 1) / EB;
     const int RT = (T + RB - 1) / RB;
     if (wave >= RT * ET) return;
@@ -116,138 +117,31 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 
 void launch_router_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H,
                           int E, float* logits, hipStream_t st) {
-    int waves, blocks;
+    // Up to 64 rows: one wave per block, so the E (or a few times E) waves
+    // spread over every CU; larger batches: four waves per block.
     if (T <= 1) {
-        waves = E;
-        blocks = (waves + 3) / 4;
-        router_logits_kernel<1, 1, 12><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<1, 1, 12><<<E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else if (T <= 2) {
-        waves = E;
-        blocks = (waves + 3) / 4;
-        router_logits_kernel<2, 1, 12><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<2, 1, 12><<<E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else if (T <= 4) {
-        waves = E;
-        blocks = (waves + 3) / 4;
-        router_logits_kernel<4, 1, 8><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<4, 1, 8><<<E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else if (T <= 64) {
-        waves = ((T + 7) / 8) * E;
-        blocks = (waves + 3) / 4;
-        router_logits_kernel<8, 1, 6><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<8, 1, 6><<<((T + 7) / 8) * E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else {
-        waves = ((T + 7) / 8) * ((E + 7) / 8);
-        blocks = (waves + 3) / 4;
-        router_logits_kernel<8, 8, 2><<<blocks, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
+        const int waves = ((T + 7) / 8) * ((E + 7) / 8);
+        router_logits_kernel<8, 8, 2><<<(waves + 3) / 4, 256, 0, st>>>(x, wr, bias, T, H, E, logits);
     }
 }
 
-// Top-k of one row per wave: experts ordered by (logit descending, id
-// ascending); the first k in that order are the picks, in pick order.  The
-// weights are the softmax over the picks ([P2] "GLM-5.3-Flash on CUDA:
-// attention on one GPU, routed experts on the Sparks (proposal) #214", "Per
-// MoE layer": rows travel with their top-k ids and weights).
-// (value, id) keys: a larger value wins, equal values go to the lower id;
-// id 0x7fffffff marks "nothing left" and always loses.
-__device__ __forceinline__ bool key_better(float v2, int i2, float v1, int i1) {
-    return i2 != 0x7fffffff && (i1 == 0x7fffffff || v2 > v1 || (v2 == v1 && i2 < i1));
-}
-
-template <int CTRL>
-__device__ __forceinline__ void key_step(float& v, int& i) {
-    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-    const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
-    if (key_better(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-    }
-}
-
-// Best key of the wave: four DPP steps give every lane its row's best, then
-// the four row winners are combined.  Every lane gets the result.
-__device__ __forceinline__ void wave_best(float& v, int& i) {
-    key_step<0xB1>(v, i);   // quad_perm [1,0,3,2]
-    key_step<0x4E>(v, i);   // quad_perm [2,3,0,1]
-    key_step<0x141>(v, i);  // row_half_mirror
-    key_step<0x140>(v, i);  // row_mirror
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-        if (key_better(rv, ri, bv, bi)) {
-            bv = rv;
-            bi = ri;
-        }
-    }
-    v = bv;
-    i = bi;
-}
-
-// Top-k of one row per wave: experts ordered by (logit descending, id
-// ascending); the first k in that order are the picks, in pick order.  The
-// weights are the softmax over the picks ([P2] "GLM-5.3-Flash on CUDA:
-// attention on one GPU, routed experts on the Sparks (proposal) #214", "Per
-// MoE layer": rows travel with their top-k ids and weights).
+// Top-k of one row per wave (topk.h).
 template <int PER>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T,
                                                           int E, int k, int32_t* __restrict__ ids,
                                                           float* __restrict__ w) {
-    const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    float v[PER];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-        int e = lane + 64 * m;
-        v[m] = (e < E) ? logits[(size_t)t * E + e] : -INFINITY;
-        if (e >= E) taken |= 1u << m;
-    }
-    float sel_v[16];
-    int sel_id[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        sel_v[j] = 0.0f;
-        sel_id[j] = 0;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j >= k) break;
-        float bv = -INFINITY;
-        int bid = 0x7fffffff;
-#pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            if (taken >> m & 1u) continue;
-            // ids grow with m inside a lane, so a strict compare keeps the lower id on ties
-            if (bid == 0x7fffffff || v[m] > bv) {
-                bv = v[m];
-                bid = lane + 64 * m;
-            }
-        }
-        wave_best(bv, bid);
-        if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
-        sel_v[j] = bv;
-        sel_id[j] = bid;
-    }
-    const float m0 = sel_v[0];
-    float a[16];
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j >= k) break;
-        a[j] = expf(sel_v[j] - m0);
-        s = s + a[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j >= k) break;
-        if (lane == j) {
-            ids[(size_t)t * k + j] = sel_id[j];
-            w[(size_t)t * k + j] = a[j] / s;
-        }
-    }
+    topk_row<PER>(logits, t, E, k, ids, w, nullptr);
 }
-
 void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                         hipStream_t st) {
     int blocks = (T + 3) / 4;
