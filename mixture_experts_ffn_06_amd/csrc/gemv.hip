@@ -90,6 +90,14 @@ __device__ __forceinline__ void dot_step_bf16(const uint4& w, const uint16_t* xs
     }
 }
 
+// (x & m) | k in one instruction (the compiler emits an AND and an OR: a
+// VOP3 takes no literal, and only one scalar operand, so k sits in a VGPR).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t k) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(k));
+    return r;
+}
+
 // 4-bit weights: 32 inputs (one group) per lane step.
 template <int NR>
 __device__ __forceinline__ void dot_step_w4(const uint4& q, float sc, float zz, const uint16_t* xs,
@@ -101,10 +109,10 @@ __device__ __forceinline__ void dot_step_w4(const uint4& q, float sc, float zz, 
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         const uint32_t c = qd[d];
-        const uint32_t p0 = (c & 0x000f000fu) | 0x43004300u;
-        const uint32_t p1 = ((c >> 4) & 0x000f000fu) | 0x43004300u;
-        const uint32_t p2 = ((c >> 8) & 0x000f000fu) | 0x43004300u;
-        const uint32_t p3 = ((c >> 12) & 0x000f000fu) | 0x43004300u;
+        const uint32_t p0 = and_or(c, 0x000f000fu, 0x43004300u);
+        const uint32_t p1 = and_or(c >> 4, 0x000f000fu, 0x43004300u);
+        const uint32_t p2 = and_or(c >> 8, 0x000f000fu, 0x43004300u);
+        const uint32_t p3 = and_or(c >> 12, 0x000f000fu, 0x43004300u);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k + 8 * d);
