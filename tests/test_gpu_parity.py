@@ -230,3 +230,22 @@ def test_empty_band_gives_zero_or_shared():
     assert int(ex["offsets"][-1]) == 0
     assert float(y.abs().max()) == 0.0
     assert (ex["pos"].cpu() == -1).all()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "w4"])
+@pytest.mark.parametrize("T", [16, 17])
+def test_small_batch_topk_dispatch_boundary(T, fmt):
+    # Up to 16 rows the top-k and the dispatch run in one block, with the
+    # picks of every row (up to 16 x 16) kept in LDS; 17 rows take the
+    # separate kernels.  topk = 16 fills that buffer.
+    w = synth.Workload("boundary", T=T, H=256, E=64, topk=16, I=128, Is=64, fmt=fmt)
+    log(f"case {w}")
+    d = gpu_inputs(w)
+    side = OracleSide(w, d)
+    y, ex = run_gpu(w, d)
+    check_routing(ex, side, 0, w.E)
+    compare(y, side.layer(list(range(w.T)), 0, w.E), f"boundary T={T}/{fmt}")
+    # a band in the middle: picks outside it are marked -1 in pos
+    y, ex = run_gpu(w, d, 16, 40, shared=False)
+    check_routing(ex, side, 16, 40)
+    compare(y, side.layer(list(range(w.T)), 16, 40, shared=False), f"boundary T={T}/{fmt} band")
