@@ -394,6 +394,9 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
     const bool fast_ok = 2 * (a.H / 8) <= 4 * kGemvThreads && a.H == 512 * CB;
     ItemMeta m = load_meta(a, it, nrouted, TR);
     int cur = -1, buf = 0;
+    // the one row staged by the synchronous path (2 token + 4-bit layout), or
+    // -1: one-row groups of the same token (every group when T = 1) reuse it
+    int staged = -1;
     for (;;) {
         const int itn = it + gridDim.x;
         const bool has_next = itn < total;
@@ -409,11 +412,16 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
             else
                 mn = gateup_fast<2, CB>(a, m, restage, xb, has_next, itn, nrouted, TR);
             cur = m.gi;
+            staged = -1;  // its buffers overlap the synchronous staging area
         } else {
             // rows staged synchronously across the whole LDS area
-            __syncthreads();
-            stage_rows(a, g, false, a.H, g.n, w4, xs, xsum);
-            __syncthreads();
+            const int key = g.n == 1 ? 2 * m.tok0 + (w4 ? 1 : 0) : -1;
+            if (key < 0 || key != staged) {
+                __syncthreads();  // a fast-path item before may still read its buffer
+                stage_rows(a, g, false, a.H, g.n, w4, xs, xsum);
+                __syncthreads();
+                staged = key;
+            }
             if (has_next) mn = load_meta(a, itn, nrouted, TR);
             if (w4)
                 gateup_dispatch_rows<1, CB>(a, g, m.tile * kGuCols, xs, xsum);
