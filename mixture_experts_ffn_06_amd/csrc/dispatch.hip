@@ -48,31 +48,57 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
     }
 }
 
-// Exclusive scan over the 1024 threads of a block (fixed order, deterministic).
-__device__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+// Exclusive scans of N values over the 1024 threads of a block at once (fixed
+// order, deterministic): wave scans by shuffles, then wave 0 scans the 16
+// wave totals the same way.  s_tmp holds 17 N ints.
+template <int N>
+__device__ void block_exclusive_scan_n(const int (&v)[N], int (&res)[N], int (&total)[N], int* s_tmp) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int inc = v;
+    int inc[N];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int o = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += o;
-    }
-    if (lane == 63) s_tmp[wave] = inc;
-    __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int w = 0; w < 16; ++w) {
-            int c = s_tmp[w];
-            s_tmp[w] = run;
-            run += c;
+    for (int i = 0; i < N; ++i) inc[i] = v[i];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int o = __shfl_up(inc[i], d, 64);
+            if (lane >= d) inc[i] += o;
         }
-        s_tmp[16] = run;
+    if (lane == 63)
+#pragma unroll
+        for (int i = 0; i < N; ++i) s_tmp[wave * N + i] = inc[i];
+    __syncthreads();
+    if (wave == 0) {
+        int w[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) w[i] = lane < 16 ? s_tmp[lane * N + i] : 0;
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int o = __shfl_up(w[i], d, 64);
+                if (lane >= d) w[i] += o;
+            }
+        if (lane < 16)
+#pragma unroll
+            for (int i = 0; i < N; ++i) s_tmp[lane * N + i] = w[i];  // inclusive over waves
     }
     __syncthreads();
-    int res = s_tmp[wave] + inc - v;
-    *total = s_tmp[16];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const int before = wave ? s_tmp[(wave - 1) * N + i] : 0;
+        res[i] = before + inc[i] - v[i];
+        total[i] = s_tmp[15 * N + i];
+    }
     __syncthreads();
-    return res;
+}
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+    const int vv[1] = {v};
+    int r[1], t[1];
+    block_exclusive_scan_n<1>(vv, r, t, s_tmp);
+    *total = t[0];
+    return r[0];
 }
 
 // Groups and work lists.  Thread i owns groups 2i and 2i+1 with row counts
@@ -105,12 +131,12 @@ __device__ void build_plan(const int cnt[2], const int run[2], int nb, int T, in
         t128[q] = (nn > 64 && nn <= 128) ? 1 : 0;
         t256[q] = nn > 128 ? (nn + 255) / 256 : 0;
     }
-    int ngv, n256, n128, n64, n32;
-    int gv0 = block_exclusive_scan(gv[0] + gv[1], s_tmp, &ngv);
-    int o256 = block_exclusive_scan(t256[0] + t256[1], s_tmp, &n256);
-    int o128 = block_exclusive_scan(t128[0] + t128[1], s_tmp, &n128);
-    int o64 = block_exclusive_scan(t64[0] + t64[1], s_tmp, &n64);
-    int o32 = block_exclusive_scan(t32[0] + t32[1], s_tmp, &n32);
+    const int cnts[5] = {gv[0] + gv[1], t256[0] + t256[1], t128[0] + t128[1], t64[0] + t64[1],
+                         t32[0] + t32[1]};
+    int offs[5], tots[5];
+    block_exclusive_scan_n<5>(cnts, offs, tots, s_tmp);
+    int gv0 = offs[0], o256 = offs[1], o128 = offs[2], o64 = offs[3], o32 = offs[4];
+    const int ngv = tots[0], n256 = tots[1], n128 = tots[2], n64 = tots[3], n32 = tots[4];
     int32_t* l128 = mfma_list;
     int32_t* l64 = mfma_list + 2 * (size_t)mfma_cap;
     int32_t* l32 = mfma_list + 4 * (size_t)mfma_cap;
@@ -158,7 +184,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, Group* __restrict__ groups,
     int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list, int mfma_cap,
     int32_t* __restrict__ plan_counts, int lo) {
-    __shared__ int s_tmp[17];
+    __shared__ int s_tmp[17 * 5];
     const int tid = threadIdx.x;
     int cnt[2], run[2];
 #pragma unroll
@@ -230,7 +256,7 @@ __device__ __forceinline__ void dispatch_small_body(
     int32_t* __restrict__ mfma_list, int mfma_cap, int32_t* __restrict__ plan_counts) {
     extern __shared__ unsigned long long masks[];  // [4][nb], then int offsets[nb + 1]
     int* s_off = reinterpret_cast<int*>(masks + 4 * nb);
-    __shared__ int s_tmp[17];
+    __shared__ int s_tmp[17 * 5];
     build_masks(masks, ids, T, k, lo, nb);
     const int tid = threadIdx.x;
     int cnt[2], run[2];
