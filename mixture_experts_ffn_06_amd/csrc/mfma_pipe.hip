@@ -375,13 +375,17 @@ struct W4Cfg {
     static constexpr int NT = 2;                         // 16-column subtiles per wave
     static constexpr int S = BM == 128 ? 3 : (BM == 64 ? 4 : 6);  // stages
     static constexpr int LA = BM / 32;                   // A loads per wave per stage
-    static constexpr int L = LA + 2;                     // + codes + scales or zeros
+    static constexpr int L = LA + 2;                     // + codes + one scale/zero piece
     static constexpr int ATile = BM * kBK * 2;
     static constexpr int QOff = ATile;                   // 128 rows x 32 bytes of codes
-    static constexpr int SOff = QOff + 4096;             // 128 rows x 2 bf16 scales
-    static constexpr int ZOff = SOff + 512;              // 128 rows x 2 bf16 zeros
-    static constexpr int Stage = ZOff + 512;
-    static constexpr int Lds = S * Stage;
+    static constexpr int Stage = QOff + 4096;
+    // Scales and zeros come in blocks of G steps: [scales | zeros] x 128
+    // rows x G steps x 4 bytes (the step's two groups), three blocks in LDS.
+    static constexpr int G = BM == 128 ? 4 : 8;
+    static constexpr int SZBlock = 1024 * G;
+    static constexpr int SZOff = S * Stage;
+    static constexpr int Lds = SZOff + 3 * SZBlock;
+    static_assert(G > S - 2, "a block's buffer is refilled only after its last read");
     static constexpr int PerCU = Lds <= 80 * 1024 ? 2 : 1;
     static constexpr int Threads = 64 * NW;
 };
@@ -435,17 +439,30 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         asrc[j] = arow + 8 * c;
     }
     // Wave w loads the codes of rows 32 w .. 32 w + 31 (lane: row 32 w + l / 2,
-    // half l % 2, 16 bytes), and waves 0-1 the scales, 2-3 the zeros of
-    // 64 rows each (4 bytes a lane: both groups of the step).
+    // half l % 2, 16 bytes).
     auto wrow = [&](int r) -> size_t {
         const int row = GATEUP ? (r < 64 ? nt * 64 + r : Ig + nt * 64 + (r - 64)) : nt * kBN + r;
         return (size_t)g.expert * (GATEUP ? 2 * (size_t)Ig : (size_t)H) + row;
     };
     const unsigned char* qsrc =
         (GATEUP ? a.qgu : a.qd) + wrow(32 * wave + (lane >> 1)) * (K / 2) + 16 * (lane & 1);
-    const uint16_t* szbase = wave < 2 ? (GATEUP ? a.sgu : a.sd) : (GATEUP ? a.zgu : a.zd);
-    const unsigned char* szsrc = (const unsigned char*)(szbase + wrow(64 * (wave & 1) + lane) * (K / 32));
-    const int szdst = (wave < 2 ? C::SOff : C::ZOff) + (wave & 1) * 256;
+    // Scale/zero block b (steps G b .. G b + G - 1) is 4 G pieces of 256
+    // bytes: piece i covers array i / 2G (scales, zeros), rows
+    // (i mod 2G) 64 / G .. + 64 / G - 1, lane l taking row + l / G, step
+    // G b + l % G (4 bytes: the step's two groups).  Per row the G steps are
+    // contiguous, so a piece touches 64 / G cache lines instead of 64.  Block
+    // 0 is loaded before the first stage, block b + 1 a piece per stage (one
+    // per wave) during the stages of block b, into buffer (b + 1) mod 3.
+    const uint16_t* sbase = GATEUP ? a.sgu : a.sd;
+    const uint16_t* zbase = GATEUP ? a.zgu : a.zd;
+    auto issue_sz = [&](int b, int i) {
+        const int arr = i / (2 * C::G), rg = i % (2 * C::G);
+        const int r = rg * (64 / C::G) + lane / C::G;
+        const int ks = min(C::G * b + lane % C::G, KT - 1);  // steps past the end: unused
+        const uint16_t* src = (arr ? zbase : sbase) + wrow(r) * (K / 32) + 2 * ks;
+        lds_u8* dst = smem + C::SZOff + (b % 3) * C::SZBlock + arr * (C::SZBlock / 2) + rg * 256;
+        __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+    };
 
     auto issue = [&](int kt) {
         lds_u8* st = smem + (kt % C::S) * C::Stage;
@@ -454,7 +471,7 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         for (int j = 0; j < C::LA; ++j)
             __builtin_amdgcn_global_load_lds(asrc[j] + k0, st + (wave + C::NW * j) * 1024, 16, 0, 0);
         __builtin_amdgcn_global_load_lds(qsrc + (size_t)kt * 32, st + C::QOff + wave * 1024, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(szsrc + (size_t)kt * 4, st + szdst, 4, 0, 0);
+        issue_sz(kt / C::G + 1, 4 * (kt % C::G) + wave);
     };
 
     f32x4_p acc[C::MT][C::NT];
@@ -475,10 +492,14 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
 
     __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
 #pragma unroll
+    for (int p = 0; p < C::G; ++p) issue_sz(0, 4 * p + wave);  // block 0, before stage 0
+#pragma unroll
     for (int s = 0; s < C::S - 1; ++s)
         if (s < KT) issue(s);
 
     for (int kt = 0; kt < KT; ++kt) {
+        // Stage kt landed (and, loaded before it, the scale/zero block of
+        // step kt); stages issued after it may still be in flight.
         const int after = min(C::S - 2, KT - 1 - kt);
         if (after >= 4)
             wait_vmcnt<4 * C::L>();
@@ -493,14 +514,15 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         __builtin_amdgcn_s_barrier();  // stage kt visible to all waves; stage kt-1 free
         if (kt + C::S - 1 < KT) issue(kt + C::S - 1);
         const lds_u8* st = smem + (kt % C::S) * C::Stage;
+        const lds_u8* sz = smem + C::SZOff + ((kt / C::G) % 3) * C::SZBlock + (kt % C::G) * 4;
         // Every LDS read of the step first (one wait), then the expansion,
         // then the MFMAs.
         uint32_t sw[C::NT], zw[C::NT], codes[2][C::NT];
         bf16x8_p af[2][C::MT];
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) {
-            sw[j] = *(lds_u32*)(st + C::SOff + brow[j] * 4);
-            zw[j] = *(lds_u32*)(st + C::ZOff + brow[j] * 4);
+            sw[j] = *(lds_u32*)(sz + brow[j] * (4 * C::G));
+            zw[j] = *(lds_u32*)(sz + C::SZBlock / 2 + brow[j] * (4 * C::G));
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -559,7 +581,7 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
 // expert_mfma_pipe_kernel).  BM = 128 also takes the 256-row list, each tile
 // as two 128-row halves.
 template <bool GATEUP, int BM>
-__global__ __launch_bounds__(W4Cfg<BM>::Threads) void expert_mfma_w4_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(W4Cfg<BM>::Threads, W4Cfg<BM>::PerCU) void expert_mfma_w4_kernel(ExpertArgs a) {
     using C = W4Cfg<BM>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::Lds];
     lds_u8* smem = (lds_u8*)smem_raw;
