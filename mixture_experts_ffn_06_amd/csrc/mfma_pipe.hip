@@ -629,7 +629,18 @@ void launch_mfma_w4(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st
         launch_w4_bm<false, 64>(a, num_cu, st);
         launch_w4_bm<false, 32>(a, num_cu, st);
     }
-    if (a.Is > 0) launch_mfma_pipe(a, gateup, num_cu, st);  // the bf16 shared expert
+    // the bf16 shared expert: one group of T rows, so one tile list (9 <= T
+    // since no MFMA launch runs at T <= 8)
+    if (a.Is > 0) {
+        if (a.T > 128)
+            gateup ? launch_pipe_bm<true, 256>(a, num_cu, st) : launch_pipe_bm<false, 256>(a, num_cu, st);
+        else if (a.T > 64)
+            gateup ? launch_pipe_bm<true, 128>(a, num_cu, st) : launch_pipe_bm<false, 128>(a, num_cu, st);
+        else if (a.T > 32)
+            gateup ? launch_pipe_bm<true, 64>(a, num_cu, st) : launch_pipe_bm<false, 64>(a, num_cu, st);
+        else
+            gateup ? launch_pipe_bm<true, 32>(a, num_cu, st) : launch_pipe_bm<false, 32>(a, num_cu, st);
+    }
 }
 
 }  // namespace moe
