@@ -398,13 +398,21 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// (x & m) | k in one instruction (the compiler emits an AND and an OR: a
+// VOP3 takes no literal, and only one scalar operand, so k sits in a VGPR).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t k) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(k));
+    return r;
+}
+
 // Eight codes (one word, k = 0..7 in nibbles 0..7) -> eight bf16 weights.
 __device__ __forceinline__ bf16x8_p dequant8(uint32_t c, float s, float n) {
     float v[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         // fp16 pair (1024 + q_j, 1024 + q_{j+4})
-        const f16x2_p h = __builtin_bit_cast(f16x2_p, ((c >> (4 * j)) & 0x000f000fu) | 0x64006400u);
+        const f16x2_p h = __builtin_bit_cast(f16x2_p, and_or(c >> (4 * j), 0x000f000fu, 0x64006400u));
         v[j] = fmaf((float)h.x, s, n);
         v[j + 4] = fmaf((float)h.y, s, n);
     }
