@@ -446,27 +446,31 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
             arow = a.h_r + (size_t)(g.row0 + m0 + rr) * a.I;
         asrc[j] = arow + 8 * c;
     }
-    // Wave w loads the codes of rows 32 w .. 32 w + 31 (lane: row 32 w + l / 2,
-    // half l % 2, 16 bytes).
+    // Wave w loads the codes of rows 32 w .. 32 w + 31: lane l takes row
+    // 32 w + l % 32, half l / 32 (16 bytes), so the wave's 1 KiB holds the
+    // first halves of its 32 rows, then the second halves (16 rows read at one
+    // offset then meet 8 bank groups, not 4).
     auto wrow = [&](int r) -> size_t {
         const int row = GATEUP ? (r < 64 ? nt * 64 + r : Ig + nt * 64 + (r - 64)) : nt * kBN + r;
         return (size_t)g.expert * (GATEUP ? 2 * (size_t)Ig : (size_t)H) + row;
     };
     const unsigned char* qsrc =
-        (GATEUP ? a.qgu : a.qd) + wrow(32 * wave + (lane >> 1)) * (K / 2) + 16 * (lane & 1);
+        (GATEUP ? a.qgu : a.qd) + wrow(32 * wave + (lane & 31)) * (K / 2) + 16 * (lane >> 5);
     // Scale/zero block b (steps G b .. G b + G - 1) is 4 G pieces of 256
     // bytes: piece i covers array i / 2G (scales, zeros), rows
-    // (i mod 2G) 64 / G .. + 64 / G - 1, lane l taking row + l / G, step
-    // G b + l % G (4 bytes: the step's two groups).  Per row the G steps are
-    // contiguous, so a piece touches 64 / G cache lines instead of 64.  Block
-    // 0 is loaded before the first stage, block b + 1 a piece per stage (one
-    // per wave) during the stages of block b, into buffer (b + 1) mod 3.
+    // (i mod 2G) R .. + R - 1 (R = 64 / G), lane l taking step G b + l / R of
+    // row + l % R (4 bytes: the step's two groups), stored step-major within
+    // the piece.  Per row the G steps are contiguous in memory, so a piece
+    // touches R cache lines instead of 64.  Block 0 is loaded before the first
+    // stage, block b + 1 a piece per stage (one per wave) during the stages of
+    // block b, into buffer (b + 1) mod 3.
     const uint16_t* sbase = GATEUP ? a.sgu : a.sd;
     const uint16_t* zbase = GATEUP ? a.zgu : a.zd;
+    constexpr int R = 64 / C::G;  // rows per piece
     auto issue_sz = [&](int b, int i) {
         const int arr = i / (2 * C::G), rg = i % (2 * C::G);
-        const int r = rg * (64 / C::G) + lane / C::G;
-        const int ks = min(C::G * b + lane % C::G, KT - 1);  // steps past the end: unused
+        const int r = rg * R + lane % R;
+        const int ks = min(C::G * b + lane / R, KT - 1);  // steps past the end: unused
         const uint16_t* src = (arr ? zbase : sbase) + wrow(r) * (K / 32) + 2 * ks;
         lds_u8* dst = smem + C::SZOff + (b % 3) * C::SZBlock + arr * (C::SZBlock / 2) + rg * 256;
         __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
@@ -522,21 +526,24 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         __builtin_amdgcn_s_barrier();  // stage kt visible to all waves; stage kt-1 free
         if (kt + C::S - 1 < KT) issue(kt + C::S - 1);
         const lds_u8* st = smem + (kt % C::S) * C::Stage;
-        const lds_u8* sz = smem + C::SZOff + ((kt / C::G) % 3) * C::SZBlock + (kt % C::G) * 4;
+        const lds_u8* sz = smem + C::SZOff + ((kt / C::G) % 3) * C::SZBlock + (kt % C::G) * (4 * R);
         // Every LDS read of the step first (one wait), then the expansion,
         // then the MFMAs.
         uint32_t sw[C::NT], zw[C::NT], codes[2][C::NT];
         bf16x8_p af[2][C::MT];
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) {
-            sw[j] = *(lds_u32*)(sz + brow[j] * (4 * C::G));
-            zw[j] = *(lds_u32*)(sz + C::SZBlock / 2 + brow[j] * (4 * C::G));
+            const int off = (brow[j] / R) * 256 + (brow[j] % R) * 4;  // piece, row in piece
+            sw[j] = *(lds_u32*)(sz + off);
+            zw[j] = *(lds_u32*)(sz + C::SZBlock / 2 + off);
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int q = ks * 4 + (lane >> 4);  // logical 16-byte chunk = 8 codes of k
 #pragma unroll
-            for (int j = 0; j < C::NT; ++j) codes[ks][j] = *(lds_u32*)(st + C::QOff + brow[j] * 32 + 4 * q);
+            for (int j = 0; j < C::NT; ++j)
+                codes[ks][j] = *(lds_u32*)(st + C::QOff + (brow[j] >> 5) * 1024 + (q >> 2) * 512 +
+                                           (brow[j] & 31) * 16 + 4 * (q & 3));
 #pragma unroll
             for (int i = 0; i < C::MT; ++i) af[ks][i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
         }
