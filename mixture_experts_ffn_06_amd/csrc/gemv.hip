@@ -26,6 +26,12 @@ namespace moe {
 constexpr int kGemvThreads = 512;
 constexpr int kGemvWaves = kGemvThreads / 64;
 
+// 4-bit layout of a staged row: the 32 inputs of group g (read by one lane
+// of a 4-bit lane step, lane = g mod 64) are four 16-byte chunks, chunk d
+// stored at position (d + lane / 2) mod 4 of the group, so the eight lanes
+// of a 128-byte LDS access meet eight different bank groups.
+__device__ __forceinline__ int w4_chunk(int g, int d) { return (d + ((g & 63) >> 1)) & 3; }
+
 // Stage the rows of a group in LDS.  src_h: rows come from the intermediate
 // h (down projection), else from x (gate/up).  permute: store each 8 inputs as
 // (0,4),(1,5),(2,6),(3,7) pairs and the per-32 sums (4-bit path).
@@ -41,6 +47,7 @@ __device__ void stage_rows(const ExpertArgs& a, const Group& g, bool src_h, int 
         else
             src = a.x + (size_t)(shared ? r : a.perm[g.row0 + r] / a.topk) * a.H;
         uint4 v = *reinterpret_cast<const uint4*>(src + 8 * c8);
+        int dst = c8;
         if (permute) {
             uint4 p;
             p.x = (v.x & 0xffffu) | (v.z << 16);
@@ -48,8 +55,9 @@ __device__ void stage_rows(const ExpertArgs& a, const Group& g, bool src_h, int 
             p.z = (v.y & 0xffffu) | (v.w << 16);
             p.w = (v.y >> 16) | (v.w & 0xffff0000u);
             v = p;
+            dst = (c8 & ~3) | w4_chunk(c8 >> 2, c8 & 3);
         }
-        *reinterpret_cast<uint4*>(xs + (size_t)r * K + 8 * c8) = v;
+        *reinterpret_cast<uint4*>(xs + (size_t)r * K + 8 * dst) = v;
     }
     if (permute) {
         // per-32 sums, from the staged copy (a fixed order over its 32 values)
@@ -61,7 +69,7 @@ __device__ void stage_rows(const ExpertArgs& a, const Group& g, bool src_h, int 
             float s = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint4 v = src[q];
+                const uint4 v = src[w4_chunk(gi, q)];
                 s += bf16_lo(v.x) + bf16_hi(v.x);
                 s += bf16_lo(v.y) + bf16_hi(v.y);
                 s += bf16_lo(v.z) + bf16_hi(v.z);
@@ -115,7 +123,7 @@ __device__ __forceinline__ void dot_step_w4(const uint4& q, float sc, float zz, 
         const uint32_t p3 = and_or(c >> 12, 0x000f000fu, 0x43004300u);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k + 8 * d);
+            uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k + 8 * w4_chunk(k >> 5, d));
             float s = part[r];
             s = dot2_bf16(p0, xv.x, s);
             s = dot2_bf16(p1, xv.y, s);
