@@ -173,6 +173,135 @@ int oracle_dispatch(const int32_t* ids, int T, int k, int lo, int hi,
 }
 
 /* ------------------------------------------------------------------------ */
+/* The canonical tree over expert ids.                                        */
+/*                                                                            */
+/* [P4] (maintainer reply): every sum follows one fixed tree of slices,       */
+/* however the slices fall over ranks, so all ranks hold the same bits.  The  */
+/* tree used here is the complete binary tree over expert ids 0..E'-1, E' the */
+/* least power of two >= E.  A row's leaf e holds its weighted expert output  */
+/* w_j * y_j when e is its pick j inside the band, and +0.0 otherwise (the    */
+/* leaves E..E'-1 are always +0.0); an inner node holds left + right.  A band */
+/* call returns the value of the smallest node containing its band.  Below,   */
+/* a node with no leaf set is +0.0 (the sum of +0.0 leaves), every other      */
+/* node is the sum of its two children, computed as written: the plain dense  */
+/* definition, with the shortcut for empty nodes only.                        */
+/* ------------------------------------------------------------------------ */
+
+/* Level of the smallest node containing [lo, hi): the least L such that lo  */
+/* and hi-1 agree above bit L-1.  Its first leaf is lo with the low L bits    */
+/* cleared. */
+int oracle_tree_node(int E, int lo, int hi, int* node_lo, int* level)
+{
+    if (E < 1 || lo < 0 || hi > E || lo >= hi) return OR_EINVAL;
+    int L = 0;
+    while ((lo >> L) != ((hi - 1) >> L)) L += 1;
+    *node_lo = (lo >> L) << L;
+    *level = L;
+    return OR_OK;
+}
+
+/* Value of node [node_lo, node_lo + 2^level) for one column: ids[i] are the  */
+/* leaf positions of the set leaves, vals[i] their fp32 values (ids distinct, */
+/* any order). */
+static float tree_value_f(int node_lo, int level, const int32_t* ids, const float* vals, int m)
+{
+    int size = 1 << level;
+    int found = -1, cnt = 0;
+    for (int i = 0; i < m; ++i)
+        if (ids[i] >= node_lo && ids[i] < node_lo + size) {
+            found = i;
+            cnt += 1;
+        }
+    if (cnt == 0) return 0.0f;
+    if (level == 0) return vals[found];
+    float left = tree_value_f(node_lo, level - 1, ids, vals, m);
+    float right = tree_value_f(node_lo + size / 2, level - 1, ids, vals, m);
+    return left + right;
+}
+
+/* The same tree in fp64, for the layer below. */
+static double tree_value_d(int node_lo, int level, const int32_t* ids, const double* vals, int m)
+{
+    int size = 1 << level;
+    int found = -1, cnt = 0;
+    for (int i = 0; i < m; ++i)
+        if (ids[i] >= node_lo && ids[i] < node_lo + size) {
+            found = i;
+            cnt += 1;
+        }
+    if (cnt == 0) return 0.0;
+    if (level == 0) return vals[found];
+    double left = tree_value_d(node_lo, level - 1, ids, vals, m);
+    double right = tree_value_d(node_lo + size / 2, level - 1, ids, vals, m);
+    return left + right;
+}
+
+/* Node values for n columns: vals is [m, n] (row i = leaf ids[i]), out [n]. */
+int oracle_tree_value(const int32_t* ids, const float* vals, int m, int node_lo, int level,
+                      size_t n, float* out)
+{
+    if (m < 0 || level < 0 || level > 20) return OR_EINVAL;
+    float* col = (float*)malloc(sizeof(float) * (size_t)(m > 0 ? m : 1));
+    for (size_t c = 0; c < n; ++c) {
+        for (int i = 0; i < m; ++i) col[i] = vals[(size_t)i * n + c];
+        out[c] = tree_value_f(node_lo, level, ids, col, m);
+    }
+    free(col);
+    return OR_OK;
+}
+
+/* Value of node [nlo, nlo + 2^lev) from parts whose nodes tile it: part p    */
+/* covers node (plo[p], plev[p]); a node past E with no part is +0.0. */
+static float merge_value(int nlo, int lev, int E, int nparts, const int* plo, const int* plev,
+                         const float* const* parts, size_t c)
+{
+    for (int p = 0; p < nparts; ++p)
+        if (plo[p] == nlo && plev[p] == lev) return parts[p][c];
+    if (nlo >= E) return 0.0f;
+    if (lev == 0) return 0.0f; /* unreachable for a valid tiling */
+    float left = merge_value(nlo, lev - 1, E, nparts, plo, plev, parts, c);
+    float right = merge_value(nlo + (1 << (lev - 1)), lev - 1, E, nparts, plo, plev, parts, c);
+    return left + right;
+}
+
+/* Sum of band partials along the canonical tree.  Part p is the output of a */
+/* band call for [lo[p], hi[p]); the bands must tile a range [U_lo, U_hi) in  */
+/* order, each band must be its node clipped to [0, E), and so must the       */
+/* range.  out = value of the range's node (+ shared, when not NULL, last);   */
+/* parts, shared and out are [n] each.  Returns OR_EINVAL for other bands.   */
+int oracle_tree_merge(int E, int nparts, const int32_t* lo, const int32_t* hi,
+                      const float* const* parts, const float* shared, size_t n, float* out)
+{
+    if (nparts < 1) return OR_EINVAL;
+    int* plo = (int*)malloc(sizeof(int) * (size_t)nparts);
+    int* plev = (int*)malloc(sizeof(int) * (size_t)nparts);
+    int ok = 1;
+    for (int p = 0; p < nparts && ok; ++p) {
+        if (oracle_tree_node(E, lo[p], hi[p], &plo[p], &plev[p]) != OR_OK) ok = 0;
+        else if (plo[p] != lo[p]) ok = 0;
+        else {
+            int end = plo[p] + (1 << plev[p]);
+            if ((end < E ? end : E) != hi[p]) ok = 0;
+        }
+        if (ok && p > 0 && lo[p] != hi[p - 1]) ok = 0;
+    }
+    int ulo = 0, ulev = 0;
+    if (ok && oracle_tree_node(E, lo[0], hi[nparts - 1], &ulo, &ulev) != OR_OK) ok = 0;
+    if (ok) {
+        int end = ulo + (1 << ulev);
+        if (ulo != lo[0] || (end < E ? end : E) != hi[nparts - 1]) ok = 0;
+    }
+    if (ok)
+        for (size_t c = 0; c < n; ++c) {
+            float v = merge_value(ulo, ulev, E, nparts, plo, plev, parts, c);
+            out[c] = shared ? v + shared[c] : v;
+        }
+    free(plo);
+    free(plev);
+    return ok ? OR_OK : OR_EINVAL;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Expert weights.                                                            */
 /*                                                                            */
 /* bf16: w_gate_up [E, 2I, H] (rows 0..I-1 gate, I..2I-1 up: [P5]'s fused     */
@@ -297,17 +426,25 @@ static void shared_ffn(const double* x, const uint16_t* wgu, const uint16_t* wd,
 /*   acc += w_j * FFN_{id_j}(x_t), acc starting at +0.0; then, if a shared     */
 /*   expert is given, acc += FFN_shared(x_t) last.  The result is the row's    */
 /*   partial residual for the band ([P1]: per-rank [H] residual partials;     */
-/*   [P2]: partials summed in rank order).                                    */
+/*   [P2]: partials summed in rank order).  combine = 1 sums the weighted     */
+/*   outputs along the canonical tree instead (the value of the smallest node */
+/*   containing the band, see above), then adds the shared expert.             */
 /*                                                                            */
 /* rows == NULL means rows 0..T-1 (nrows must equal T).  out is [nrows, H];   */
 /* ids_out [nrows, k] and w_out [nrows, k] may be NULL.                        */
 /* ------------------------------------------------------------------------ */
 static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                       const oracle_experts* ex, const uint16_t* sh_wgu, const uint16_t* sh_wd,
-                      int Is, int use_band, int lo, int hi, int k, const int32_t* rows, int nrows,
-                      double* out, int32_t* ids_out, double* w_out)
+                      int Is, int use_band, int lo, int hi, int k, int combine,
+                      const int32_t* rows, int nrows, double* out, int32_t* ids_out,
+                      double* w_out)
 {
     if (T < 1 || H % 256 != 0 || E < 1 || k < 1 || k > E) return OR_EINVAL;
+    if (combine != 0 && combine != 1) return OR_EINVAL;
+    int node_lo = 0, node_lev = 0;
+    if (combine == 1 && oracle_tree_node(E, use_band ? lo : 0, use_band ? hi : E, &node_lo,
+                                         &node_lev) != OR_OK)
+        return OR_EINVAL;
     if (ex->E != E || ex->H != H) return OR_EINVAL;
     if (use_band && (lo < 0 || hi > E || lo >= hi)) return OR_EINVAL;
     if (!rows && nrows != T) return OR_EINVAL;
@@ -320,6 +457,9 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
         int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
         double* w = (double*)malloc(sizeof(double) * (size_t)k);
         double* y = (double*)malloc(sizeof(double) * (size_t)H);
+        double* leaf = (double*)malloc(sizeof(double) * (size_t)k * H);
+        int32_t* leaf_id = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+        double* col = (double*)malloc(sizeof(double) * (size_t)k);
 #pragma omp for schedule(dynamic, 1)
         for (int r = 0; r < nrows; ++r) {
             int t = rows ? rows[r] : r;
@@ -341,11 +481,22 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
             topk_row(l, E, k, ids, w);
             double* acc = out + (size_t)r * H;
             for (int c = 0; c < H; ++c) acc[c] = 0.0;
+            int m = 0;
             for (int j = 0; j < k; ++j) {
                 if (use_band && (ids[j] < lo || ids[j] >= hi)) continue;
                 oracle_expert_ffn(xd, ex, ids[j], y);
-                for (int c = 0; c < H; ++c) acc[c] += w[j] * y[c];
+                if (combine == 0) {
+                    for (int c = 0; c < H; ++c) acc[c] += w[j] * y[c];
+                } else {
+                    for (int c = 0; c < H; ++c) leaf[(size_t)m * H + c] = w[j] * y[c];
+                    leaf_id[m++] = ids[j];
+                }
             }
+            if (combine == 1)
+                for (int c = 0; c < H; ++c) {
+                    for (int i = 0; i < m; ++i) col[i] = leaf[(size_t)i * H + c];
+                    acc[c] = tree_value_d(node_lo, node_lev, leaf_id, col, m);
+                }
             if (sh_wgu && sh_wd) {
                 shared_ffn(xd, sh_wgu, sh_wd, H, Is, y);
                 for (int c = 0; c < H; ++c) acc[c] += y[c];
@@ -361,6 +512,9 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
         free(ids);
         free(w);
         free(y);
+        free(leaf);
+        free(leaf_id);
+        free(col);
     }
     return status;
 }
@@ -368,11 +522,11 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
 /* The layer restricted to the expert band [lo, hi). */
 int oracle_moe_ffn(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                    const oracle_experts* ex, const uint16_t* sh_wgu, const uint16_t* sh_wd, int Is,
-                   int lo, int hi, int k, const int32_t* rows, int nrows, double* out,
-                   int32_t* ids_out, double* w_out)
+                   int lo, int hi, int k, int combine, const int32_t* rows, int nrows,
+                   double* out, int32_t* ids_out, double* w_out)
 {
-    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 1, lo, hi, k, rows, nrows, out,
-                      ids_out, w_out);
+    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 1, lo, hi, k, combine, rows,
+                      nrows, out, ids_out, w_out);
 }
 
 /* The routed monolith: the same layer with no band logic at all (every pick
@@ -382,8 +536,8 @@ int oracle_moe_ffn_monolith(const uint16_t* x, int T, int H, const float* wr, co
                             const uint16_t* sh_wd, int Is, int k, const int32_t* rows, int nrows,
                             double* out)
 {
-    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 0, 0, E, k, rows, nrows, out,
-                      NULL, NULL);
+    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 0, 0, E, k, 0, rows, nrows,
+                      out, NULL, NULL);
 }
 
 /* Dequantised weight matrix of one expert, for pins that compare the 4-bit

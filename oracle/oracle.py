@@ -76,7 +76,13 @@ def _load():
         lib.oracle_expert_matrix.argtypes = [ctypes.POINTER(_Experts), I32, I32, P]
         layer = [P, I32, I32, P, P, I32, ctypes.POINTER(_Experts), P, P, I32]
         lib.oracle_moe_ffn.restype = I32
-        lib.oracle_moe_ffn.argtypes = layer + [I32, I32, I32, P, I32, P, P, P]
+        lib.oracle_moe_ffn.argtypes = layer + [I32, I32, I32, I32, P, I32, P, P, P]
+        lib.oracle_tree_node.restype = I32
+        lib.oracle_tree_node.argtypes = [I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        lib.oracle_tree_value.restype = I32
+        lib.oracle_tree_value.argtypes = [P, P, I32, I32, I32, ctypes.c_size_t, P]
+        lib.oracle_tree_merge.restype = I32
+        lib.oracle_tree_merge.argtypes = [I32, I32, P, P, P, P, ctypes.c_size_t, P]
         lib.oracle_moe_ffn_monolith.restype = I32
         lib.oracle_moe_ffn_monolith.argtypes = layer + [I32, P, I32, P]
         _lib = lib
@@ -177,10 +183,48 @@ def expert_matrix(experts: Experts, e: int, which: int) -> torch.Tensor:
     return out
 
 
+def tree_node(E: int, lo: int, hi: int):
+    """(first leaf, level) of the smallest canonical-tree node containing [lo, hi)."""
+    nlo, lev = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(_load().oracle_tree_node(E, lo, hi, ctypes.byref(nlo), ctypes.byref(lev)), "tree_node")
+    return nlo.value, lev.value
+
+
+def tree_value(ids, vals: torch.Tensor, node_lo: int, level: int) -> torch.Tensor:
+    """fp32 value of a canonical-tree node: leaf ids[i] holds the fp32 row
+    vals[i] (vals [m, n]), every other leaf +0.0.  Returns [n]."""
+    idt = torch.as_tensor(ids, dtype=torch.int32).contiguous()
+    v = _cpu(vals).float().contiguous()
+    m = idt.numel()
+    n = v.shape[1] if m else (v.numel() if v.dim() == 1 else v.shape[-1])
+    out = torch.empty(n, dtype=torch.float32)
+    _check(_load().oracle_tree_value(_ptr(idt), _ptr(v), m, node_lo, level, n, _ptr(out)),
+           "tree_value")
+    return out
+
+
+def tree_merge(parts, bands, E: int, shared: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sum of fp32 band partials along the canonical tree (+ shared last)."""
+    ps = [_cpu(p).float().contiguous() for p in parts]
+    n = ps[0].numel()
+    lo = torch.tensor([b[0] for b in bands], dtype=torch.int32)
+    hi = torch.tensor([b[1] for b in bands], dtype=torch.int32)
+    arr = (ctypes.c_void_p * len(ps))(*[p.data_ptr() for p in ps])
+    sh = None if shared is None else _cpu(shared).float().contiguous()
+    out = torch.empty(n, dtype=torch.float32)
+    _check(_load().oracle_tree_merge(E, len(ps), _ptr(lo), _ptr(hi), ctypes.cast(arr, ctypes.c_void_p),
+                                     _ptr(sh), n, _ptr(out)), "tree_merge")
+    return out.reshape(ps[0].shape)
+
+
 def moe_ffn(inputs: dict, E: int, I: int, Is: int, lo: int, hi: int, k: int,
-            rows: Optional[torch.Tensor] = None, experts: Optional[Experts] = None):
+            rows: Optional[torch.Tensor] = None, experts: Optional[Experts] = None,
+            combine: str = "pick"):
     """The layer for the band [lo, hi) on the listed rows (all rows if None).
+    combine: "pick" (pick order) or "tree" (canonical tree over expert ids).
     Returns (out fp64 [nrows, H], ids int32 [nrows, k], w fp64 [nrows, k])."""
+    if combine not in ("pick", "tree"):
+        raise ValueError(f"oracle: combine {combine!r}")
     x, wr, b = _cpu(inputs["x"]), _cpu(inputs["router_w"]).float(), _cpu(inputs["bias"])
     T, H = x.shape
     ex = experts if experts is not None else Experts(inputs["experts"], E, H, I)
@@ -198,7 +242,8 @@ def moe_ffn(inputs: dict, E: int, I: int, Is: int, lo: int, hi: int, k: int,
     if b is not None and b.numel() != Er:
         raise ValueError("oracle: bias length != router experts")
     _check(_load().oracle_moe_ffn(_ptr(x), T, H, _ptr(wr), _ptr(b), Er, ctypes.byref(ex.desc),
-                                  _ptr(sgu), _ptr(sd), Is if sh else 0, lo, hi, k, _ptr(r), nrows,
+                                  _ptr(sgu), _ptr(sd), Is if sh else 0, lo, hi, k,
+                                  0 if combine == "pick" else 1, _ptr(r), nrows,
                                   _ptr(out), _ptr(ids), _ptr(w)), "moe_ffn")
     return out, ids, w
 
