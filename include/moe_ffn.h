@@ -34,10 +34,25 @@
  *      (SwiGLU; silu(g) = g / (1 + exp(-g)));
  *   5. out[t,:] = sum over picks j in pick order with the expert in the band
  *      of w_j * y_j, accumulated in fp32 from +0.0, then + the shared
- *      expert's output (weight 1) when `shared` is not NULL.
+ *      expert's output (weight 1) when `shared` is not NULL.  With
+ *      moe_out.combine = MOE_COMBINE_TREE the routed sum follows the
+ *      canonical tree over expert ids instead (below).
  * The full band [0, E) gives the whole layer (the routed monolith plus the
  * shared expert).  Summing the outputs of consecutive bands in band order
- * gives the whole layer up to fp32 reassociation.
+ * gives the whole layer up to fp32 reassociation; in tree mode, summing the
+ * outputs of bands that are tree nodes along the tree (moe_ffn_reduce) gives
+ * it bit for bit.
+ *
+ * The canonical tree ([P4] maintainer reply: every sum follows one fixed tree
+ * of slices however the slices fall over ranks, so every rank holds the same
+ * bits): the complete binary tree over expert ids 0..E'-1, E' the least
+ * power of two >= E.  For row t, leaf e holds w_j * y_j (one fp32 product)
+ * when e is the row's pick j and lies in the band, else +0.0; an inner node
+ * holds left + right (fp32).  A node is the range [a 2^L, (a+1) 2^L) of
+ * leaves; a call returns the value of the smallest node containing
+ * [band_lo, band_hi).  Bands that are nodes (clipped to [0, E)) are the
+ * pieces moe_ffn_reduce can add back together exactly; every contiguous band
+ * is a run of such nodes.
  *
  * Memory: every pointer is device memory owned by the caller, contiguous
  * row-major, 16-byte aligned.  The library never allocates device memory and
@@ -73,8 +88,10 @@ extern "C" {
 #define MOE_E_ALIGN (-8)     /* a pointer is not 16-byte aligned */
 #define MOE_E_HIP (-9)       /* the HIP runtime reported an error while enqueuing */
 #define MOE_E_DEVICE (-10)   /* the current device is not a gfx950 GPU */
+#define MOE_E_COMBINE (-11)  /* unknown combine mode or reduce order */
 
 #define MOE_MAX_TOPK 16
+#define MOE_MAX_PARTS 64 /* partials one moe_ffn_reduce call adds */
 #define MOE_MAX_E 1024
 #define MOE_MAX_T (1 << 20)
 
@@ -143,6 +160,10 @@ typedef struct moe_shared {
 #define MOE_EV_END 8
 #define MOE_NUM_EVENTS 9
 
+/* Order of the routed sum (moe_out.combine). */
+#define MOE_COMBINE_PICK 0 /* pick order (descending logit), fp32 fused multiply-adds */
+#define MOE_COMBINE_TREE 1 /* the canonical tree over expert ids */
+
 /* Outputs.  y is required and fully overwritten (rows with no in-band pick
  * and no shared expert become +0.0).  The other outputs are optional exports
  * of the routing and dispatch (NULL = not exported):
@@ -155,7 +176,13 @@ typedef struct moe_shared {
  *        pick is outside the band.
  * workspace: device scratch of at least moe_ffn_workspace_bytes() bytes.
  * stage_events: NULL, or MOE_NUM_EVENTS hipEvent_t handles (created by the
- *        caller) recorded at the stage boundaries, for timing. */
+ *        caller) recorded at the stage boundaries, for timing.
+ * y_shared: NULL, or fp32 [T, H]: the shared expert's output is written
+ *        there and not added to y (for moe_ffn_reduce, which adds it after
+ *        the partials); ignored without a shared expert.
+ * y_picks: NULL, or fp32 [T*topk, H]: row i receives the expert output of
+ *        pick perm[i] before weighting (rows past N_in unspecified).
+ * combine: MOE_COMBINE_PICK (0) or MOE_COMBINE_TREE. */
 typedef struct moe_out {
     float* y; /* fp32 [T, H] */
     int32_t* topk_ids;
@@ -167,6 +194,9 @@ typedef struct moe_out {
     void* workspace;
     size_t workspace_bytes;
     void* const* stage_events;
+    float* y_shared;
+    float* y_picks;
+    int32_t combine;
 } moe_out;
 
 /* Run the layer for the band [band_lo, band_hi) on `stream` (a hipStream_t;
@@ -180,6 +210,31 @@ int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe_experts* e
  * Returns 0 for sizes moe_ffn would reject. */
 size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t I, int32_t Is,
                                int32_t topk, int32_t fmt);
+
+/* Orders of moe_ffn_reduce. */
+#define MOE_REDUCE_RANK 0 /* ((p_0 + p_1) + p_2) + ...: rank (band) order */
+#define MOE_REDUCE_TREE 1 /* along the canonical tree over expert ids */
+
+/* The exchange step of an expert-parallel layer, on one GPU: add the fp32
+ * partials of several band calls ([P2] "Per MoE layer" and [P4]: the ranks'
+ * fp32 partials summed in rank order; [P4] maintainer reply: one fixed tree
+ * of slices), then the shared expert's output, then a residual.
+ *   parts: host array of nparts device pointers, fp32 [T, H] each
+ *          (1 <= nparts <= MOE_MAX_PARTS);
+ *   band_lo, band_hi: host arrays [nparts], the band of each part.  They are
+ *          read only by MOE_REDUCE_TREE (may be NULL for MOE_REDUCE_RANK),
+ *          where the bands must follow each other ([lo_0, hi_0), [hi_0, hi_1),
+ *          ...), each must be a tree node clipped to [0, E) (its band call
+ *          returned that node's value), and so must their union; y is then
+ *          the value of the union's node;
+ *   y_shared: NULL or fp32 [T, H], added after the partials;
+ *   residual: NULL or bf16 [T, H], added last;
+ *   y: fp32 [T, H] output (may be parts[0] for MOE_REDUCE_RANK).
+ * Errors as for moe_ffn (MOE_E_BAND for bands that break the rule above,
+ * MOE_E_COMBINE for an unknown order); nothing is enqueued on error. */
+int32_t moe_ffn_reduce(const float* const* parts, int32_t nparts, const int32_t* band_lo,
+                       const int32_t* band_hi, int32_t E, int32_t order, const float* y_shared,
+                       const void* residual, int32_t T, int32_t H, float* y, void* stream);
 
 /* A static, human-readable message for a return code. */
 const char* moe_ffn_strerror(int32_t code);

@@ -28,8 +28,15 @@ EVENT_SLOTS = ("router", "topk", "dispatch", "gu_gemv", "gu_mfma", "dn_gemv", "d
 ERRORS = {
     0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_DIM", -4: "MOE_E_BAND",
     -5: "MOE_E_TOPK", -6: "MOE_E_FORMAT", -7: "MOE_E_WORKSPACE", -8: "MOE_E_ALIGN",
-    -9: "MOE_E_HIP", -10: "MOE_E_DEVICE",
+    -9: "MOE_E_HIP", -10: "MOE_E_DEVICE", -11: "MOE_E_COMBINE",
 }
+MOE_COMBINE_PICK = 0
+MOE_COMBINE_TREE = 1
+MOE_REDUCE_RANK = 0
+MOE_REDUCE_TREE = 1
+MOE_MAX_PARTS = 64
+_COMBINE = {"pick": MOE_COMBINE_PICK, "tree": MOE_COMBINE_TREE}
+_REDUCE = {"rank": MOE_REDUCE_RANK, "tree": MOE_REDUCE_TREE}
 
 
 class MoeError(RuntimeError):
@@ -67,7 +74,8 @@ class MoeOut(ctypes.Structure):
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
                 ("perm", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("stage_events", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("y_shared", ctypes.c_void_p),
+                ("y_picks", ctypes.c_void_p), ("combine", ctypes.c_int32)]
 
 
 _lib = None
@@ -89,6 +97,8 @@ def load_library() -> ctypes.CDLL:
         lib.moe_ffn_workspace_bytes.argtypes = [I32] * 7
         lib.moe_ffn_strerror.restype = ctypes.c_char_p
         lib.moe_ffn_strerror.argtypes = [I32]
+        lib.moe_ffn_reduce.restype = I32
+        lib.moe_ffn_reduce.argtypes = [P, I32, P, P, I32, I32, P, P, I32, I32, P, P]
         _lib = lib
     return _lib
 
@@ -134,7 +144,9 @@ def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None):
 def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor], experts: dict,
             shared: Optional[dict], band_lo: int, band_hi: int, topk: int,
             out: Optional[torch.Tensor] = None, exports: Optional[dict] = None,
-            workspace: Optional[torch.Tensor] = None, stream=None, events=None) -> torch.Tensor:
+            workspace: Optional[torch.Tensor] = None, stream=None, events=None,
+            combine: str = "pick", y_shared: Optional[torch.Tensor] = None,
+            y_picks: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Run the layer for the expert band [band_lo, band_hi).
 
     x bf16 [T,H]; router_w fp32 [E,H]; bias fp32 [E] or None; experts / shared
@@ -142,7 +154,13 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
     [T,H] partial residual (`out` if given).  `exports`, if a dict, receives
     topk_ids, topk_w, counts, offsets, perm, pos.  `events` is a list of
     MOE_NUM_EVENTS raw hipEvent_t handles recorded at the stage boundaries.
+    combine: "pick" (pick order) or "tree" (canonical tree over expert ids).
+    y_shared: fp32 [T,H] receiving the shared expert's output instead of
+    adding it; y_picks: fp32 [T*topk,H] receiving the per-pick expert outputs
+    in perm order.
     """
+    if combine not in _COMBINE:
+        raise MoeError(-11, f"combine must be one of {sorted(_COMBINE)}")
     lib = load_library()
     T, H = x.shape
     dx, dr, de, ds = make_descriptors(x, router_w, bias, experts, shared)
@@ -169,7 +187,8 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
     dout = MoeOut(_p(out), _p(ex.get("topk_ids")), _p(ex.get("topk_w")), _p(ex.get("counts")),
                   _p(ex.get("offsets")), _p(ex.get("perm")), _p(ex.get("pos")),
                   _p(workspace), workspace.numel(),
-                  ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+                  ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
+                  _p(y_shared), _p(y_picks), _COMBINE[combine])
     if stream is None:
         st = torch.cuda.current_stream(dev).cuda_stream if dev.type == "cuda" else 0
     else:
@@ -184,6 +203,65 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
     return out
 
 
-__all__ = ["moe_ffn", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
+def _stream_handle(dev, stream):
+    if stream is None:
+        return torch.cuda.current_stream(dev).cuda_stream if dev.type == "cuda" else 0
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def reduce(parts, order: str = "rank", bands=None, E: int = 0,
+           y_shared: Optional[torch.Tensor] = None, residual: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Sum fp32 [T,H] band partials in rank order or along the canonical tree
+    (bands: their [lo, hi) ranges, tree nodes), then + y_shared, + residual
+    (bf16 [T,H])."""
+    if order not in _REDUCE:
+        raise MoeError(-11, f"order must be one of {sorted(_REDUCE)}")
+    lib = load_library()
+    T, H = parts[0].shape
+    dev = parts[0].device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    n = len(parts)
+    arr = (ctypes.c_void_p * max(n, 1))(*[p.data_ptr() for p in parts])
+    lo = hi = None
+    if bands is not None:
+        lo = (ctypes.c_int32 * n)(*[int(b[0]) for b in bands])
+        hi = (ctypes.c_int32 * n)(*[int(b[1]) for b in bands])
+    rc = lib.moe_ffn_reduce(ctypes.cast(arr, ctypes.c_void_p), n,
+                            ctypes.cast(lo, ctypes.c_void_p) if lo is not None else None,
+                            ctypes.cast(hi, ctypes.c_void_p) if hi is not None else None,
+                            E, _REDUCE[order], _p(y_shared), _p(residual), T, H, _p(out),
+                            ctypes.c_void_p(_stream_handle(dev, stream)))
+    if rc != 0:
+        raise MoeError(rc, strerror(rc))
+    return out
+
+
+def tree_pieces(lo: int, hi: int, E: int):
+    """Cut the band [lo, hi) into canonical-tree nodes (clipped to [0, E)),
+    largest first from the left: the bands whose tree-mode outputs
+    moe_ffn_reduce adds back exactly.  Host logic only."""
+    if not (0 <= lo < hi <= E):
+        raise ValueError(f"band [{lo}, {hi}) outside [0, {E})")
+    Ep = 1
+    while Ep < E:
+        Ep *= 2
+    out = []
+    a = lo
+    while a < hi:
+        size = 1
+        # grow while the node stays aligned, inside the padded range, and its
+        # in-range part stays inside the band
+        while a % (2 * size) == 0 and a + 2 * size <= Ep and min(a + 2 * size, E) <= hi:
+            size *= 2
+        b = min(a + size, E)
+        out.append((a, b))
+        a = b
+    return out
+
+
+__all__ = ["moe_ffn", "reduce", "tree_pieces", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
            "MOE_BF16", "MOE_W4A16", "MOE_NUM_EVENTS", "EVENT_SLOTS", "make_descriptors",
-           "MoeX", "MoeRouter", "MoeExperts", "MoeShared", "MoeOut"]
+           "MoeX", "MoeRouter", "MoeExperts", "MoeShared", "MoeOut", "MOE_COMBINE_PICK",
+           "MOE_COMBINE_TREE", "MOE_REDUCE_RANK", "MOE_REDUCE_TREE", "MOE_MAX_PARTS"]

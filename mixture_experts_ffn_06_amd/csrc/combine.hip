@@ -1,5 +1,6 @@
-// combine.hip -- the weighted sum of each row's in-band expert outputs in pick
-// order, then the shared expert, in fp32 with no atomics.
+// combine.hip -- the weighted sum of each row's in-band expert outputs (in pick
+// order, or along the canonical tree over expert ids), then the shared expert,
+// in fp32 with no atomics; and the sum of band partials (moe_ffn_reduce).
 //
 // [P1] "GLM-5.2 multi-GPU: expert-parallel sharding + the resident-fit
 // benchmark", "What landed": per-rank [H] residual partials, each rank adding
@@ -45,6 +46,206 @@ void launch_combine(const float* y_r, const float* y_s, const int32_t* pos, cons
                     int H, int k, float* out, hipStream_t st) {
     const int ctiles = (H / 4 + 255) / 256;
     combine_kernel<<<T * ctiles, 256, 0, st>>>(y_r, y_s, pos, w, H, k, ctiles, out);
+}
+
+// ---- the canonical tree ------------------------------------------------------
+//
+// [P4] "GLM-5.3-Flash on CUDA over three ranks (--tp 3) ... #310", maintainer
+// reply: every sum follows one fixed tree of slices however the slices fall
+// over ranks.  The tree is the complete binary tree over expert ids; a row's
+// leaf e is w_j * y_j for its in-band pick j of expert e, +0.0 elsewhere, and
+// an inner node is left + right.  Only the picked leaves are visited: sorted
+// by id, two neighbours meet at the node of level c = bit length of (e_a xor
+// e_b), and an entry waiting for its right neighbour at level c is kept in
+// pend[c] (waiting levels are distinct and grow towards the bottom of the
+// stack, so indexing by level is a stack).  A node whose leaves all sit in
+// one child equals that child + (+0.0): it turns -0.0 into +0.0 and changes
+// nothing else, and applying it twice is applying it once, so an operand is
+// "normalised" when at least one such node lies between it and the node
+// where it is added.
+
+constexpr int kTreeLevels = 11;  // levels 0..10: E <= 1024
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 norm4(float4 a) { return add4(a, make_float4(0.f, 0.f, 0.f, 0.f)); }
+
+// One block per (row, 1024 columns).  Thread 0 builds the row's program:
+// the in-band picks sorted by expert id and, before leaf i is taken, the
+// levels whose waiting entries merge with the running value (ascending), the
+// operands to normalise there, and the level where the running value then
+// waits; entry m holds the final merges.
+__global__ __launch_bounds__(256) void combine_tree_kernel(const float* __restrict__ y_r,
+                                                          const float* __restrict__ y_s,
+                                                          const int32_t* __restrict__ ids,
+                                                          const int32_t* __restrict__ pos,
+                                                          const float* __restrict__ w, int H, int k,
+                                                          int ctiles, int node_level,
+                                                          float* __restrict__ out) {
+    __shared__ int s_p[16];
+    __shared__ float s_w[16];
+    __shared__ uint32_t s_mask[17], s_nl[17], s_nr[17];
+    __shared__ int s_push[17];
+    __shared__ int s_m, s_rootnorm;
+    const int t = blockIdx.x / ctiles;
+    if (threadIdx.x == 0) {
+        int e_[16], p_[16];
+        float w_[16];
+        int m = 0;
+        for (int j = 0; j < k; ++j) {
+            const int p = pos[(size_t)t * k + j];
+            if (p < 0) continue;
+            const int e = ids[(size_t)t * k + j];
+            const float wj = w[(size_t)t * k + j];
+            int q = m++;
+            while (q > 0 && e_[q - 1] > e) {
+                e_[q] = e_[q - 1];
+                p_[q] = p_[q - 1];
+                w_[q] = w_[q - 1];
+                --q;
+            }
+            e_[q] = e;
+            p_[q] = p;
+            w_[q] = wj;
+        }
+        uint32_t occ = 0;  // levels holding a waiting entry
+        int tl[kTreeLevels];  // level of the top node of each waiting entry
+        int tlc = 0;          // level of the top node of the running value
+        for (int i = 0; i <= m; ++i) {
+            if (i < m) {
+                s_p[i] = p_[i];
+                s_w[i] = w_[i];
+            }
+            if (i == 0) continue;
+            const int c = i < m ? 32 - __clz(e_[i - 1] ^ e_[i]) : kTreeLevels;
+            const uint32_t mask = occ & ((1u << c) - 1u);
+            uint32_t nl = 0, nr = 0;
+            for (int lev = 1; lev < kTreeLevels; ++lev) {
+                if (!(mask >> lev & 1u)) continue;
+                if (tl[lev] < lev - 1) nl |= 1u << lev;
+                if (tlc < lev - 1) nr |= 1u << lev;
+                tlc = lev;
+            }
+            occ &= ~mask;
+            s_mask[i] = mask;
+            s_nl[i] = nl;
+            s_nr[i] = nr;
+            s_push[i] = c;
+            if (i < m) {
+                occ |= 1u << c;
+                tl[c] = tlc;
+                tlc = 0;
+            }
+        }
+        s_m = m;
+        s_rootnorm = (m > 0 && tlc < node_level) ? 1 : 0;
+    }
+    __syncthreads();
+    const int c = ((blockIdx.x - t * ctiles) * 256 + threadIdx.x) * 4;
+    if (c >= H) return;
+    const int m = __builtin_amdgcn_readfirstlane(s_m);
+    float4 cur = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 pend[kTreeLevels];
+#pragma unroll
+    for (int lev = 0; lev < kTreeLevels; ++lev) pend[lev] = cur;
+    for (int i = 0; i <= m; ++i) {
+        if (i > 0) {
+            const uint32_t mask = __builtin_amdgcn_readfirstlane(s_mask[i]);
+            const uint32_t nl = __builtin_amdgcn_readfirstlane(s_nl[i]);
+            const uint32_t nr = __builtin_amdgcn_readfirstlane(s_nr[i]);
+            const int push = __builtin_amdgcn_readfirstlane(s_push[i]);
+#pragma unroll
+            for (int lev = 1; lev < kTreeLevels; ++lev) {
+                if (mask >> lev & 1u) {
+                    float4 l = pend[lev], r = cur;
+                    if (nl >> lev & 1u) l = norm4(l);
+                    if (nr >> lev & 1u) r = norm4(r);
+                    cur = add4(l, r);
+                }
+            }
+            if (i < m) {
+#pragma unroll
+                for (int lev = 1; lev < kTreeLevels; ++lev)
+                    if (lev == push) pend[lev] = cur;
+            }
+        }
+        if (i < m) {
+            const int p = __builtin_amdgcn_readfirstlane(s_p[i]);
+            const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_w[i])));
+            const float4 v = *reinterpret_cast<const float4*>(y_r + (size_t)p * H + c);
+            cur = make_float4(wi * v.x, wi * v.y, wi * v.z, wi * v.w);
+        }
+    }
+    if (__builtin_amdgcn_readfirstlane(s_rootnorm)) cur = norm4(cur);
+    if (y_s) cur = add4(cur, *reinterpret_cast<const float4*>(y_s + (size_t)t * H + c));
+    *reinterpret_cast<float4*>(out + (size_t)t * H + c) = cur;
+}
+
+void launch_combine_tree(const float* y_r, const float* y_s, const int32_t* ids, const int32_t* pos,
+                         const float* w, int T, int H, int k, int node_level, float* out,
+                         hipStream_t st) {
+    const int ctiles = (H / 4 + 255) / 256;
+    combine_tree_kernel<<<T * ctiles, 256, 0, st>>>(y_r, y_s, ids, pos, w, H, k, ctiles, node_level,
+                                                    out);
+}
+
+// ---- sum of band partials ------------------------------------------------------
+//
+// Rank order: ((p_0 + p_1) + p_2) + ...  ([P2] "Per MoE layer": the partials
+// are summed in rank order).  Tree order: the host turns the parts (tree nodes
+// tiling a node) into pushes of a node value at level l0, which then merges
+// with the waiting entries at levels l0 .. l1-1 (left + right) and waits at
+// level l1; nodes past E with no part are pushed as +0.0.  Then the shared
+// expert's output and the residual are added, in that order.
+
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceProgram pg, const float* __restrict__ y_s,
+                                                    const uint16_t* __restrict__ res, size_t n4,
+                                                    float* __restrict__ y) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        float4 acc;
+        if (pg.order == 0) {
+            acc = reinterpret_cast<const float4*>(pg.part[0])[i];
+            for (int p = 1; p < pg.nparts; ++p)
+                acc = add4(acc, reinterpret_cast<const float4*>(pg.part[p])[i]);
+        } else {
+            float4 pend[kTreeLevels];
+            const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int lev = 0; lev < kTreeLevels; ++lev) pend[lev] = zero;
+            for (int o = 0; o < pg.nops; ++o) {
+                const int pi = pg.op_part[o], l0 = pg.op_l0[o], l1 = pg.op_l1[o];
+                float4 v = pi >= 0 ? reinterpret_cast<const float4*>(pg.part[pi])[i] : zero;
+#pragma unroll
+                for (int lev = 0; lev < kTreeLevels; ++lev)
+                    if (lev >= l0 && lev < l1) v = add4(pend[lev], v);
+#pragma unroll
+                for (int lev = 0; lev < kTreeLevels; ++lev)
+                    if (lev == l1) pend[lev] = v;
+            }
+            acc = zero;
+#pragma unroll
+            for (int lev = 0; lev < kTreeLevels; ++lev)
+                if (lev == pg.root_level) acc = pend[lev];
+        }
+        if (y_s) acc = add4(acc, reinterpret_cast<const float4*>(y_s)[i]);
+        if (res) {
+            const uint2 b = reinterpret_cast<const uint2*>(res)[i];
+            acc = add4(acc, make_float4(bf16_bits_to_f32(b.x & 0xffffu), bf16_bits_to_f32(b.x >> 16),
+                                        bf16_bits_to_f32(b.y & 0xffffu), bf16_bits_to_f32(b.y >> 16)));
+        }
+        reinterpret_cast<float4*>(y)[i] = acc;
+    }
+}
+
+void launch_reduce(const ReduceProgram& pg, const float* y_s, const uint16_t* res, size_t n,
+                   float* y, int num_cu, hipStream_t st) {
+    const size_t n4 = n / 4;
+    size_t grid = (n4 + 255) / 256;
+    const size_t cap = (size_t)num_cu * 8;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    reduce_kernel<<<(int)grid, 256, 0, st>>>(pg, y_s, res, n4, y);
 }
 
 }  // namespace moe

@@ -142,5 +142,24 @@ void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t 
 void launch_mfma_w4(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st);
 void launch_combine(const float* y_r, const float* y_s, const int32_t* pos, const float* w,
                     int T, int H, int k, float* out, hipStream_t st);
+void launch_combine_tree(const float* y_r, const float* y_s, const int32_t* ids, const int32_t* pos,
+                         const float* w, int T, int H, int k, int node_level, float* out,
+                         hipStream_t st);
+
+// The sum of band partials: order 0 = rank order over part[0..nparts-1];
+// order 1 = the canonical tree, as nops pushes of part op_part[o] (-1: a
+// +0.0 node) at level op_l0[o], merged up to level op_l1[o]; the result is
+// the entry at root_level.
+constexpr int kMaxParts = 64;
+constexpr int kMaxReduceOps = 96;
+struct ReduceProgram {
+    const float* part[kMaxParts];
+    int8_t op_part[kMaxReduceOps];
+    uint8_t op_l0[kMaxReduceOps];
+    uint8_t op_l1[kMaxReduceOps];
+    int nparts, nops, order, root_level;
+};
+void launch_reduce(const ReduceProgram& pg, const float* y_s, const uint16_t* res, size_t n,
+                   float* y, int num_cu, hipStream_t st);
 
 }  // namespace moe

@@ -95,6 +95,13 @@ int32_t device_info(int* num_cu) {
     return MOE_OK;
 }
 
+// Level of the smallest canonical-tree node containing [lo, hi).
+int tree_level(int lo, int hi) {
+    int L = 0;
+    while ((lo >> L) != ((hi - 1) >> L)) ++L;
+    return L;
+}
+
 }  // namespace
 
 extern "C" size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t I, int32_t Is,
@@ -116,6 +123,7 @@ extern "C" const char* moe_ffn_strerror(int32_t code) {
         case MOE_E_ALIGN: return "a pointer is not 16-byte aligned";
         case MOE_E_HIP: return "HIP runtime error while enqueuing";
         case MOE_E_DEVICE: return "the current device is not a gfx950 GPU";
+        case MOE_E_COMBINE: return "unknown combine mode or reduce order";
         default: return "unknown error code";
     }
 }
@@ -149,6 +157,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     }
     if (fmt == MOE_W4A16 && experts->group != 32) return MOE_E_FORMAT;
     if (band_lo < 0 || band_hi > E || band_lo >= band_hi) return MOE_E_BAND;
+    if (out->combine != MOE_COMBINE_PICK && out->combine != MOE_COMBINE_TREE) return MOE_E_COMBINE;
 
     const bool bf = fmt == MOE_BF16;
     const void* ptrs[] = {x->ptr, router_w->w, router_w->bias,
@@ -158,7 +167,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
                           bf ? nullptr : experts->s_down, bf ? nullptr : experts->z_down,
                           shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
                           out->y, out->topk_ids, out->topk_w, out->counts, out->offsets,
-                          out->perm, out->pos, out->workspace};
+                          out->perm, out->pos, out->workspace, out->y_shared, out->y_picks};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MOE_E_ALIGN;
 
@@ -241,8 +250,10 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     a.perm = perm;
     a.h_r = reinterpret_cast<uint16_t*>(ws + L.h_r);
     a.h_s = reinterpret_cast<uint16_t*>(ws + L.h_s);
-    a.y_r = reinterpret_cast<float*>(ws + L.y_r);
-    a.y_s = reinterpret_cast<float*>(ws + L.y_s);
+    // the expert outputs land in the caller's export buffers when given
+    a.y_r = out->y_picks ? out->y_picks : reinterpret_cast<float*>(ws + L.y_r);
+    const bool shared_apart = has_shared && out->y_shared;
+    a.y_s = shared_apart ? out->y_shared : reinterpret_cast<float*>(ws + L.y_s);
 
     // Groups on each path: a group has at most T rows (a row picks an expert
     // at most once), so with T <= 8 nothing reaches the MFMA path.
@@ -269,9 +280,90 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
             moe::launch_mfma_w4(a, false, num_cu, st);
     }
     mark(MOE_EV_COMBINE);
-    moe::launch_combine(a.y_r, has_shared ? a.y_s : nullptr, pos, wts, T, H, topk, out->y, st);
+    const float* add_s = has_shared && !shared_apart ? a.y_s : nullptr;
+    if (out->combine == MOE_COMBINE_TREE)
+        moe::launch_combine_tree(a.y_r, add_s, ids, pos, wts, T, H, topk,
+                                 tree_level(band_lo, band_hi), out->y, st);
+    else
+        moe::launch_combine(a.y_r, add_s, pos, wts, T, H, topk, out->y, st);
     mark(MOE_EV_END);
 
+    if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
+    return MOE_OK;
+}
+
+extern "C" int32_t moe_ffn_reduce(const float* const* parts, int32_t nparts, const int32_t* band_lo,
+                                  const int32_t* band_hi, int32_t E, int32_t order,
+                                  const float* y_shared, const void* residual, int32_t T, int32_t H,
+                                  float* y, void* stream) {
+    if (!parts || !y) return MOE_E_NULL;
+    if (order != MOE_REDUCE_RANK && order != MOE_REDUCE_TREE) return MOE_E_COMBINE;
+    if (nparts < 1 || nparts > MOE_MAX_PARTS || T < 1 || T > MOE_MAX_T || H < 256 || H % 256 != 0)
+        return MOE_E_SHAPE;
+    for (int p = 0; p < nparts; ++p) {
+        if (!parts[p]) return MOE_E_NULL;
+        if (!aligned16(parts[p])) return MOE_E_ALIGN;
+    }
+    if (!aligned16(y) || (y_shared && !aligned16(y_shared)) || (residual && !aligned16(residual)))
+        return MOE_E_ALIGN;
+
+    moe::ReduceProgram pg;
+    memset(&pg, 0, sizeof pg);
+    pg.nparts = nparts;
+    pg.order = order;
+    for (int p = 0; p < nparts; ++p) pg.part[p] = parts[p];
+    if (order == MOE_REDUCE_TREE) {
+        if (!band_lo || !band_hi) return MOE_E_NULL;
+        if (E < 1 || E > MOE_MAX_E) return MOE_E_SHAPE;
+        // every band a node clipped to [0, E), in order, and so their union
+        auto is_node = [&](int lo, int hi, int* lev) {
+            if (lo < 0 || hi > E || lo >= hi) return false;
+            const int L = tree_level(lo, hi);
+            const int end = lo + (1 << L);
+            *lev = L;
+            return ((lo >> L) << L) == lo && (end < E ? end : E) == hi;
+        };
+        int ulev = 0;
+        if (!is_node(band_lo[0], band_hi[nparts - 1], &ulev)) return MOE_E_BAND;
+        int cursor = band_lo[0];
+        uint32_t occ = 0;
+        auto push = [&](int part, int lev) {
+            if (pg.nops >= moe::kMaxReduceOps) return false;
+            int l1 = lev;
+            while (occ >> l1 & 1u) occ &= ~(1u << l1++);
+            occ |= 1u << l1;
+            pg.op_part[pg.nops] = (int8_t)part;
+            pg.op_l0[pg.nops] = (uint8_t)lev;
+            pg.op_l1[pg.nops] = (uint8_t)l1;
+            pg.nops += 1;
+            return true;
+        };
+        for (int p = 0; p < nparts; ++p) {
+            int lev = 0;
+            if (band_lo[p] != cursor || !is_node(band_lo[p], band_hi[p], &lev)) return MOE_E_BAND;
+            if (!push(p, lev)) return MOE_E_SHAPE;
+            cursor = band_lo[p] + (1 << lev);  // the node's end (past E for the last one)
+        }
+        // the union's node past the last part: +0.0 nodes, largest first
+        const int uend = band_lo[0] + (1 << ulev);
+        while (cursor < uend) {
+            int lev = 0;
+            while (((cursor >> (lev + 1)) << (lev + 1)) == cursor && cursor + (2 << lev) <= uend) ++lev;
+            if (!push(-1, lev)) return MOE_E_SHAPE;
+            cursor += 1 << lev;
+        }
+        pg.root_level = ulev;
+        if (occ != (1u << ulev)) return MOE_E_BAND;  // not one node: unreachable for a valid tiling
+    }
+
+    int num_cu = 0;
+    {
+        int32_t rc = device_info(&num_cu);
+        if (rc != MOE_OK) return rc;
+    }
+    (void)hipGetLastError();
+    moe::launch_reduce(pg, y_shared, static_cast<const uint16_t*>(residual), (size_t)T * H, y,
+                       num_cu, reinterpret_cast<hipStream_t>(stream));
     if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
     return MOE_OK;
 }

@@ -71,14 +71,15 @@ class OracleSide:
                     self._experts[name][e].copy_(t[e])
             self._have.add(e)
 
-    def layer(self, rows, lo, hi, shared=True):
+    def layer(self, rows, lo, hi, shared=True, combine="pick"):
         rows = torch.as_tensor(rows, dtype=torch.int32)
         need = {int(e) for e in self.ids[rows.long()].flatten().tolist() if lo <= e < hi}
         self._fetch(need)
         inputs = {"x": self.x, "router_w": self.wr, "bias": self.bias, "experts": self._experts,
                   "shared": self.shared if shared else None}
         w = self.w
-        out, ids, wts = orc.moe_ffn(inputs, w.E, w.I, w.Is, lo, hi, self.k, rows=rows)
+        out, ids, wts = orc.moe_ffn(inputs, w.E, w.I, w.Is, lo, hi, self.k, rows=rows,
+                                    combine=combine)
         return out
 
 

@@ -23,7 +23,7 @@ HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
 def test_library_exports_every_declared_symbol():
     text = open(HEADER).read()
     declared = set(re.findall(r"^\S.*?\b(moe_ffn\w*)\s*\(", text, flags=re.M))
-    assert declared == {"moe_ffn", "moe_ffn_workspace_bytes", "moe_ffn_strerror"}
+    assert declared == {"moe_ffn", "moe_ffn_workspace_bytes", "moe_ffn_strerror", "moe_ffn_reduce"}
     out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
