@@ -208,6 +208,11 @@ def main():
                     help="how L2 and MALL are evicted before each step (1 GiB scratch read or write)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--combine", choices=["pick", "tree"], default="pick",
+                    help="order of the routed sum: pick order or the canonical tree over expert ids")
+    ap.add_argument("--reduce-parts", type=int, default=0, metavar="N",
+                    help="also time moe_ffn_reduce adding N band partials of the output along "
+                         "the tree (N a power of two dividing E)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB five times (a known byte "
                          "count for calibrating HBM byte counters), then exit")
@@ -260,7 +265,8 @@ def main():
     def step(events=None, exports=None):
         evict()
         moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
-                    w.band_hi, w.topk, out=out, workspace=ws, events=events, exports=exports)
+                    w.band_hi, w.topk, out=out, workspace=ws, events=events, exports=exports,
+                    combine=args.combine)
 
     step(exports=ex)  # also exports the routing, for the roofline bookkeeping
     for _ in range(args.warmup):
@@ -276,7 +282,7 @@ def main():
         evict()
         starts[i].record(stream)
         moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
-                    w.band_hi, w.topk, out=out, workspace=ws)
+                    w.band_hi, w.topk, out=out, workspace=ws, combine=args.combine)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -296,6 +302,30 @@ def main():
     counts = ex["counts"].cpu()
     roof = roofline_for(w, counts, stage)
 
+    reduce_info = None
+    if args.reduce_parts:
+        # the exchange step: N band partials (copies of this output) added
+        # along the canonical tree, then the shared output and the residual
+        n = args.reduce_parts
+        span = w.E // n
+        parts = [out.clone() for _ in range(n)]
+        bands = [(i * span, (i + 1) * span) for i in range(n)]
+        red = torch.empty_like(out)
+        r_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        for i in range(args.steps + 2):
+            evict()
+            if i >= 2:
+                r_ev[i - 2][0].record(stream)
+            moe.reduce(parts, "tree", bands=bands, E=w.E, y_shared=out, residual=d["x"], out=red)
+            if i >= 2:
+                r_ev[i - 2][1].record(stream)
+        torch.cuda.synchronize()
+        r_ms = sum(a.elapsed_time(b) for a, b in r_ev) / len(r_ev)
+        nbytes = (n + 2) * w.T * w.H * 4 + w.T * w.H * 2
+        reduce_info = {"parts": n, "us": round(r_ms * 1e3, 2), "bytes": nbytes,
+                       "GB_per_s": round(nbytes / (r_ms * 1e-3) / 1e9, 1)}
+
     line = {
         "metric": METRIC,
         "value": round(w.T / (ms * 1e-3), 2),
@@ -314,11 +344,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "topk": w.topk, "I": w.I,
                    "Is": w.Is, "fmt": w.fmt, "band": [w.band_lo, w.band_hi],
+                   "combine": args.combine,
                    "l2_mall_eviction": {"read": "1 GiB read", "write": "1 GiB write",
                                         "none": None}[args.flush]},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "roofline": roof,
     }
+    if reduce_info is not None:
+        line["reduce"] = reduce_info
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, d, ex, args.cpu_rows)
     print(json.dumps(line), flush=True)

@@ -302,6 +302,24 @@ int oracle_tree_merge(int E, int nparts, const int32_t* lo, const int32_t* hi,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Tensor-parallel shares.                                                    */
+/*                                                                            */
+/* [P4] (proposal and comments): a dimension splits in whole units, as evenly */
+/* as it goes, with the remainder on the lowest ranks.  units = dim / unit;   */
+/* rank r gets floor(units / ranks) units, plus one when r < units mod ranks. */
+/* Rejects a dim that is not a positive multiple of unit and more ranks than  */
+/* units (a rank would hold nothing).                                         */
+/* ------------------------------------------------------------------------ */
+int oracle_tp_shares(int dim, int unit, int ranks, int32_t* shares)
+{
+    if (unit < 1 || dim < unit || dim % unit != 0 || ranks < 1) return OR_EINVAL;
+    int units = dim / unit;
+    if (ranks > units) return OR_EINVAL;
+    for (int r = 0; r < ranks; ++r) shares[r] = (units / ranks + (r < units % ranks ? 1 : 0)) * unit;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Expert weights.                                                            */
 /*                                                                            */
 /* bf16: w_gate_up [E, 2I, H] (rows 0..I-1 gate, I..2I-1 up: [P5]'s fused     */

@@ -81,6 +81,8 @@ def _load():
         lib.oracle_tree_node.argtypes = [I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         lib.oracle_tree_value.restype = I32
         lib.oracle_tree_value.argtypes = [P, P, I32, I32, I32, ctypes.c_size_t, P]
+        lib.oracle_tp_shares.restype = I32
+        lib.oracle_tp_shares.argtypes = [I32, I32, I32, P]
         lib.oracle_tree_merge.restype = I32
         lib.oracle_tree_merge.argtypes = [I32, I32, P, P, P, P, ctypes.c_size_t, P]
         lib.oracle_moe_ffn_monolith.restype = I32
@@ -181,6 +183,38 @@ def expert_matrix(experts: Experts, e: int, which: int) -> torch.Tensor:
     out = torch.empty(shape, dtype=torch.float64)
     _check(_load().oracle_expert_matrix(ctypes.byref(d), e, which, _ptr(out)), "expert_matrix")
     return out
+
+
+def tp_shares(dim: int, unit: int, ranks: int):
+    """Tensor-parallel shares of dim: whole units, remainder on the lowest ranks."""
+    out = torch.empty(max(ranks, 1), dtype=torch.int32)
+    _check(_load().oracle_tp_shares(dim, unit, ranks, _ptr(out)), "tp_shares")
+    return out[:ranks].tolist()
+
+
+def tp_slice(experts: dict, i_lo: int, i_hi: int) -> dict:
+    """The intermediate columns [i_lo, i_hi) of every expert (gate rows, up
+    rows, down-projection inputs), as a smaller expert set.  Plain indexing of
+    the stored arrays: bf16 [E,2I,H] / [E,H,I], or 4-bit codes with one
+    (scale, zero) per 32 inputs."""
+    fmt = experts["fmt"]
+    if fmt == "bf16":
+        gu = experts["w_gate_up"]
+        I = gu.shape[-2] // 2
+        rows = list(range(i_lo, i_hi)) + list(range(I + i_lo, I + i_hi))
+        out = {"fmt": fmt, "w_gate_up": gu[..., rows, :].contiguous(),
+               "w_down": experts["w_down"][..., i_lo:i_hi].contiguous()}
+        return out
+    q = experts["q_gate_up"]
+    I = q.shape[-2] // 2
+    rows = list(range(i_lo, i_hi)) + list(range(I + i_lo, I + i_hi))
+    return {"fmt": fmt,
+            "q_gate_up": q[..., rows, :].contiguous(),
+            "s_gate_up": experts["s_gate_up"][..., rows, :].contiguous(),
+            "z_gate_up": experts["z_gate_up"][..., rows, :].contiguous(),
+            "q_down": experts["q_down"][..., i_lo // 2:i_hi // 2].contiguous(),
+            "s_down": experts["s_down"][..., i_lo // 32:i_hi // 32].contiguous(),
+            "z_down": experts["z_down"][..., i_lo // 32:i_hi // 32].contiguous()}
 
 
 def tree_node(E: int, lo: int, hi: int):
