@@ -236,6 +236,35 @@ int32_t moe_ffn_reduce(const float* const* parts, int32_t nparts, const int32_t*
                        const int32_t* band_hi, int32_t E, int32_t order, const float* y_shared,
                        const void* residual, int32_t T, int32_t H, float* y, void* stream);
 
+/* Tensor-parallel expert slices ([P4] "GLM-5.3-Flash on CUDA over three
+ * ranks (--tp 3) ... #310": every rank holds a whole-unit slice of each
+ * expert's intermediate columns and returns a full-width fp32 partial; the
+ * partials are added in rank order, i.e. moe_ffn_reduce with
+ * MOE_REDUCE_RANK).  A rank's slice is an expert set of its own (I = its
+ * share), so moe_ffn runs it unchanged; the functions below give the shares
+ * and lay a rank's slice out from full weights.
+ *
+ * Shares of dim over ranks: whole units of `unit`, as even as it goes, the
+ * remainder on the lowest ranks (the page's examples: 2048 columns in 128-wide
+ * units over three ranks -> 768/640/640, in 64-wide units -> 704/704/640).
+ * shares: host int32 [ranks].  MOE_E_SHAPE when dim is not a positive
+ * multiple of unit, ranks < 1 or ranks > dim / unit.  Host only. */
+int32_t moe_tp_shares(int32_t dim, int32_t unit, int32_t ranks, int32_t* shares);
+
+/* Copy intermediate columns [i_lo, i_hi) of every routed expert -- gate rows
+ * i_lo..i_hi-1, up rows I+i_lo..I+i_hi-1 and the same inputs of the down
+ * projection (codes, scales and zeros alike for MOE_W4A16) -- into dst, an
+ * expert set of the same E, H and format with I = i_hi - i_lo whose arrays
+ * the caller allocated.  i_lo and i_hi are multiples of 64 with
+ * 0 <= i_lo < i_hi <= I.  Device-to-device copies enqueued on stream; errors
+ * as for moe_ffn (MOE_E_SHAPE for a slice outside the rule). */
+int32_t moe_tp_slice_experts(const moe_experts* src, int32_t i_lo, int32_t i_hi,
+                             const moe_experts* dst, void* stream);
+
+/* The same for the shared expert: columns [i_lo, i_hi) of Is. */
+int32_t moe_tp_slice_shared(const moe_shared* src, int32_t i_lo, int32_t i_hi,
+                            const moe_shared* dst, void* stream);
+
 /* A static, human-readable message for a return code. */
 const char* moe_ffn_strerror(int32_t code);
 

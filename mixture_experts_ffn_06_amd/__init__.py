@@ -97,6 +97,14 @@ def load_library() -> ctypes.CDLL:
         lib.moe_ffn_workspace_bytes.argtypes = [I32] * 7
         lib.moe_ffn_strerror.restype = ctypes.c_char_p
         lib.moe_ffn_strerror.argtypes = [I32]
+        lib.moe_tp_shares.restype = I32
+        lib.moe_tp_shares.argtypes = [I32, I32, I32, P]
+        lib.moe_tp_slice_experts.restype = I32
+        lib.moe_tp_slice_experts.argtypes = [ctypes.POINTER(MoeExperts), I32, I32,
+                                             ctypes.POINTER(MoeExperts), P]
+        lib.moe_tp_slice_shared.restype = I32
+        lib.moe_tp_slice_shared.argtypes = [ctypes.POINTER(MoeShared), I32, I32,
+                                            ctypes.POINTER(MoeShared), P]
         lib.moe_ffn_reduce.restype = I32
         lib.moe_ffn_reduce.argtypes = [P, I32, P, P, I32, I32, P, P, I32, I32, P, P]
         _lib = lib
@@ -238,6 +246,63 @@ def reduce(parts, order: str = "rank", bands=None, E: int = 0,
     return out
 
 
+def tp_shares(dim: int, unit: int, ranks: int):
+    """Tensor-parallel shares of dim: whole units, remainder on the lowest ranks."""
+    arr = (ctypes.c_int32 * max(ranks, 1))()
+    rc = load_library().moe_tp_shares(dim, unit, ranks, ctypes.cast(arr, ctypes.c_void_p))
+    if rc != 0:
+        raise MoeError(rc, strerror(rc))
+    return list(arr)[:ranks]
+
+
+_SLICE_GU = ("w_gate_up", "q_gate_up", "s_gate_up", "z_gate_up")
+
+
+def tp_slice_experts(experts: dict, i_lo: int, i_hi: int, stream=None) -> dict:
+    """A rank's slice of every routed expert (intermediate columns
+    [i_lo, i_hi)), laid out by the library into new device tensors."""
+    lib = load_library()
+    fmt = _fmt_code(experts)
+    ref = experts["w_gate_up"] if fmt == MOE_BF16 else experts["q_gate_up"]
+    E, I2 = ref.shape[0], ref.shape[1]
+    I = I2 // 2
+    n = i_hi - i_lo
+    out = {"fmt": experts["fmt"]}
+    for name, t in experts.items():
+        if not isinstance(t, torch.Tensor):
+            continue
+        shape = list(t.shape)
+        if name in _SLICE_GU:
+            shape[1] = 2 * n
+        else:  # down projection: inputs along the last dimension
+            shape[2] = shape[2] * n // I
+        out[name] = torch.empty(shape, dtype=t.dtype, device=t.device)
+    H = (out.get("w_down") if fmt == MOE_BF16 else out["q_down"]).shape[1]
+    src = make_descriptors(torch.empty((1, H)), torch.empty((E, H)), None, experts, None, E=E, I=I)[2]
+    dst = make_descriptors(torch.empty((1, H)), torch.empty((E, H)), None, out, None, E=E, I=n)[2]
+    rc = lib.moe_tp_slice_experts(ctypes.byref(src), i_lo, i_hi, ctypes.byref(dst),
+                                  ctypes.c_void_p(_stream_handle(ref.device, stream)))
+    if rc != 0:
+        raise MoeError(rc, strerror(rc))
+    return out
+
+
+def tp_slice_shared(shared: dict, i_lo: int, i_hi: int, stream=None) -> dict:
+    """A rank's slice of the shared expert (columns [i_lo, i_hi) of Is)."""
+    lib = load_library()
+    gu, dn = shared["w_gate_up"], shared["w_down"]
+    H, Is, n = gu.shape[1], dn.shape[1], i_hi - i_lo
+    out = {"w_gate_up": torch.empty((2 * n, H), dtype=gu.dtype, device=gu.device),
+           "w_down": torch.empty((H, n), dtype=dn.dtype, device=dn.device)}
+    src = MoeShared(Is, H, _p(gu), _p(dn))
+    dst = MoeShared(n, H, _p(out["w_gate_up"]), _p(out["w_down"]))
+    rc = lib.moe_tp_slice_shared(ctypes.byref(src), i_lo, i_hi, ctypes.byref(dst),
+                                 ctypes.c_void_p(_stream_handle(gu.device, stream)))
+    if rc != 0:
+        raise MoeError(rc, strerror(rc))
+    return out
+
+
 def tree_pieces(lo: int, hi: int, E: int):
     """Cut the band [lo, hi) into canonical-tree nodes (clipped to [0, E)),
     largest first from the left: the bands whose tree-mode outputs
@@ -261,7 +326,7 @@ def tree_pieces(lo: int, hi: int, E: int):
     return out
 
 
-__all__ = ["moe_ffn", "reduce", "tree_pieces", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
+__all__ = ["moe_ffn", "reduce", "tree_pieces", "tp_shares", "tp_slice_experts", "tp_slice_shared", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
            "MOE_BF16", "MOE_W4A16", "MOE_NUM_EVENTS", "EVENT_SLOTS", "make_descriptors",
            "MoeX", "MoeRouter", "MoeExperts", "MoeShared", "MoeOut", "MOE_COMBINE_PICK",
            "MOE_COMBINE_TREE", "MOE_REDUCE_RANK", "MOE_REDUCE_TREE", "MOE_MAX_PARTS"]

@@ -367,3 +367,130 @@ extern "C" int32_t moe_ffn_reduce(const float* const* parts, int32_t nparts, con
     if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
     return MOE_OK;
 }
+
+// ---- tensor-parallel slices ----------------------------------------------------
+
+extern "C" int32_t moe_tp_shares(int32_t dim, int32_t unit, int32_t ranks, int32_t* shares) {
+    if (!shares) return MOE_E_NULL;
+    if (unit < 1 || dim < unit || dim % unit != 0 || ranks < 1 || ranks > dim / unit)
+        return MOE_E_SHAPE;
+    const int units = dim / unit;
+    for (int r = 0; r < ranks; ++r) shares[r] = (units / ranks + (r < units % ranks ? 1 : 0)) * unit;
+    return MOE_OK;
+}
+
+namespace {
+
+// rows [r0, r0 + n) of each of `blocks` blocks of `rows_per_block` rows of
+// `row_bytes` bytes -> consecutive blocks of n rows
+hipError_t copy_rows(void* dst, const void* src, size_t blocks, size_t rows_per_block, size_t r0,
+                     size_t n, size_t row_bytes, hipStream_t st) {
+    return hipMemcpy2DAsync(dst, n * row_bytes,
+                            static_cast<const unsigned char*>(src) + r0 * row_bytes,
+                            rows_per_block * row_bytes, n * row_bytes, blocks,
+                            hipMemcpyDeviceToDevice, st);
+}
+
+// bytes [b0, b0 + nb) of every row of `rows` rows of `row_bytes` bytes
+hipError_t copy_cols(void* dst, const void* src, size_t rows, size_t row_bytes, size_t b0, size_t nb,
+                     hipStream_t st) {
+    return hipMemcpy2DAsync(dst, nb, static_cast<const unsigned char*>(src) + b0, row_bytes, nb, rows,
+                            hipMemcpyDeviceToDevice, st);
+}
+
+// gate rows [lo, hi) and up rows [I + lo, I + hi) of E blocks of 2I rows
+hipError_t copy_gate_up(void* dst, const void* src, size_t E, size_t I, size_t lo, size_t hi,
+                        size_t row_bytes, hipStream_t st) {
+    const size_t n = hi - lo;
+    // each destination block holds n gate rows then n up rows: two strided
+    // copies with a destination pitch of 2n rows
+    hipError_t e = hipMemcpy2DAsync(dst, 2 * n * row_bytes,
+                                    static_cast<const unsigned char*>(src) + lo * row_bytes,
+                                    2 * I * row_bytes, n * row_bytes, E, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return e;
+    return hipMemcpy2DAsync(static_cast<unsigned char*>(dst) + n * row_bytes, 2 * n * row_bytes,
+                            static_cast<const unsigned char*>(src) + (I + lo) * row_bytes,
+                            2 * I * row_bytes, n * row_bytes, E, hipMemcpyDeviceToDevice, st);
+}
+
+}  // namespace
+
+extern "C" int32_t moe_tp_slice_experts(const moe_experts* src, int32_t i_lo, int32_t i_hi,
+                                        const moe_experts* dst, void* stream) {
+    if (!src || !dst) return MOE_E_NULL;
+    const int fmt = src->fmt;
+    if (fmt != MOE_BF16 && fmt != MOE_W4A16) return MOE_E_FORMAT;
+    if (dst->fmt != fmt || (fmt == MOE_W4A16 && (src->group != 32 || dst->group != 32)))
+        return MOE_E_FORMAT;
+    const int E = src->E, H = src->H, I = src->I;
+    if (E < 1 || E > MOE_MAX_E || H < 256 || H % 256 != 0 || I < 64 || I % 64 != 0)
+        return MOE_E_SHAPE;
+    if (i_lo < 0 || i_hi > I || i_lo >= i_hi || i_lo % 64 != 0 || i_hi % 64 != 0) return MOE_E_SHAPE;
+    if (dst->E != E || dst->H != H || dst->I != i_hi - i_lo) return MOE_E_SHAPE;
+    const void* need_src[6] = {src->w_gate_up, src->w_down, nullptr, nullptr, nullptr, nullptr};
+    const void* need_dst[6] = {dst->w_gate_up, dst->w_down, nullptr, nullptr, nullptr, nullptr};
+    int nneed = 2;
+    if (fmt == MOE_W4A16) {
+        const void* s6[6] = {src->q_gate_up, src->s_gate_up, src->z_gate_up, src->q_down,
+                             src->s_down, src->z_down};
+        const void* d6[6] = {dst->q_gate_up, dst->s_gate_up, dst->z_gate_up, dst->q_down,
+                             dst->s_down, dst->z_down};
+        for (int i = 0; i < 6; ++i) {
+            need_src[i] = s6[i];
+            need_dst[i] = d6[i];
+        }
+        nneed = 6;
+    }
+    for (int i = 0; i < nneed; ++i) {
+        if (!need_src[i] || !need_dst[i]) return MOE_E_NULL;
+        if (!aligned16(need_src[i]) || !aligned16(need_dst[i])) return MOE_E_ALIGN;
+    }
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const size_t n = (size_t)(i_hi - i_lo);
+    hipError_t e = hipSuccess;
+    if (fmt == MOE_BF16) {
+        e = copy_gate_up(const_cast<void*>(dst->w_gate_up), src->w_gate_up, E, I, i_lo, i_hi, (size_t)H * 2, st);
+        if (e == hipSuccess)
+            e = copy_cols(const_cast<void*>(dst->w_down), src->w_down, (size_t)E * H, (size_t)I * 2, (size_t)i_lo * 2,
+                          n * 2, st);
+    } else {
+        e = copy_gate_up(const_cast<void*>((const void*)dst->q_gate_up), src->q_gate_up, E, I, i_lo, i_hi, (size_t)H / 2, st);
+        if (e == hipSuccess)
+            e = copy_gate_up(const_cast<void*>((const void*)dst->s_gate_up), src->s_gate_up, E, I, i_lo, i_hi, (size_t)H / 16, st);
+        if (e == hipSuccess)
+            e = copy_gate_up(const_cast<void*>((const void*)dst->z_gate_up), src->z_gate_up, E, I, i_lo, i_hi, (size_t)H / 16, st);
+        if (e == hipSuccess)
+            e = copy_cols(const_cast<void*>((const void*)dst->q_down), src->q_down, (size_t)E * H, (size_t)I / 2,
+                          (size_t)i_lo / 2, n / 2, st);
+        if (e == hipSuccess)
+            e = copy_cols(const_cast<void*>((const void*)dst->s_down), src->s_down, (size_t)E * H, (size_t)I / 16,
+                          (size_t)i_lo / 16, n / 16, st);
+        if (e == hipSuccess)
+            e = copy_cols(const_cast<void*>((const void*)dst->z_down), src->z_down, (size_t)E * H, (size_t)I / 16,
+                          (size_t)i_lo / 16, n / 16, st);
+    }
+    if (e != hipSuccess) return MOE_E_HIP;
+    return MOE_OK;
+}
+
+extern "C" int32_t moe_tp_slice_shared(const moe_shared* src, int32_t i_lo, int32_t i_hi,
+                                       const moe_shared* dst, void* stream) {
+    if (!src || !dst || !src->w_gate_up || !src->w_down || !dst->w_gate_up || !dst->w_down)
+        return MOE_E_NULL;
+    const int H = src->H, Is = src->Is;
+    if (H < 256 || H % 256 != 0 || Is < 64 || Is % 64 != 0) return MOE_E_SHAPE;
+    if (i_lo < 0 || i_hi > Is || i_lo >= i_hi || i_lo % 64 != 0 || i_hi % 64 != 0) return MOE_E_SHAPE;
+    if (dst->H != H || dst->Is != i_hi - i_lo) return MOE_E_SHAPE;
+    if (!aligned16(src->w_gate_up) || !aligned16(src->w_down) || !aligned16(dst->w_gate_up) ||
+        !aligned16(dst->w_down))
+        return MOE_E_ALIGN;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const size_t n = (size_t)(i_hi - i_lo);
+    hipError_t e = copy_gate_up(const_cast<void*>(dst->w_gate_up), src->w_gate_up, 1, Is, i_lo, i_hi, (size_t)H * 2, st);
+    if (e == hipSuccess)
+        e = copy_cols(const_cast<void*>(dst->w_down), src->w_down, (size_t)H, (size_t)Is * 2, (size_t)i_lo * 2, n * 2, st);
+    if (e != hipSuccess) return MOE_E_HIP;
+    return MOE_OK;
+}

@@ -22,8 +22,9 @@ HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
 
 def test_library_exports_every_declared_symbol():
     text = open(HEADER).read()
-    declared = set(re.findall(r"^\S.*?\b(moe_ffn\w*)\s*\(", text, flags=re.M))
-    assert declared == {"moe_ffn", "moe_ffn_workspace_bytes", "moe_ffn_strerror", "moe_ffn_reduce"}
+    declared = set(re.findall(r"^\S.*?\b(moe_\w+)\s*\(", text, flags=re.M))
+    assert declared == {"moe_ffn", "moe_ffn_workspace_bytes", "moe_ffn_strerror", "moe_ffn_reduce",
+                        "moe_tp_shares", "moe_tp_slice_experts", "moe_tp_slice_shared"}
     out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -176,3 +177,15 @@ def test_python_binding_raises(monkeypatch):
                      "w_down": torch.zeros(8, 250, 128, dtype=torch.bfloat16)},
                     None, 0, 8, 2, workspace=torch.zeros(16, dtype=torch.uint8))
     assert e.value.code == -2
+
+
+def test_tp_shares_match_the_page_examples():
+    # host-only entry point: the shares the page prints (tests/golden/tp_shares.json)
+    import json
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "tp_shares.json")))["cases"]
+    for c in cases:
+        assert moe.tp_shares(c["dim"], c["unit"], c["ranks"]) == c["shares"], c["what"]
+    for args in ((2000, 64, 3), (64, 64, 2), (0, 64, 1), (128, 64, 0)):
+        with pytest.raises(moe.MoeError) as e:
+            moe.tp_shares(*args)
+        assert e.value.code == -2
