@@ -213,6 +213,11 @@ def main():
     ap.add_argument("--reduce-parts", type=int, default=0, metavar="N",
                     help="also time moe_ffn_reduce adding N band partials of the output along "
                          "the tree (N a power of two dividing E)")
+    ap.add_argument("--tp", type=int, default=1, metavar="N",
+                    help="time one tensor-parallel rank's share: the experts' intermediate "
+                         "columns split over N ranks (whole units, remainder on the lowest ranks)")
+    ap.add_argument("--tp-rank", type=int, default=0)
+    ap.add_argument("--tp-unit", type=int, default=64)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB five times (a known byte "
                          "count for calibrating HBM byte counters), then exit")
@@ -244,6 +249,20 @@ def main():
     torch.cuda.set_device(dev)
     t_gen = time.perf_counter()
     d = synth.make_inputs(w, dev)
+    tp_info = None
+    if args.tp > 1:
+        # this rank's slice of every expert (and of the shared expert), laid
+        # out by the library; the layer then runs at the rank's real shape
+        shares = moe.tp_shares(w.I, args.tp_unit, args.tp)
+        sshares = moe.tp_shares(w.Is, args.tp_unit, args.tp)
+        r = args.tp_rank
+        lo, slo = sum(shares[:r]), sum(sshares[:r])
+        d["experts"] = moe.tp_slice_experts(d["experts"], lo, lo + shares[r])
+        d["shared"] = moe.tp_slice_shared(d["shared"], slo, slo + sshares[r])
+        tp_info = {"ranks": args.tp, "rank": r, "unit": args.tp_unit, "I": shares[r],
+                   "Is": sshares[r]}
+        w = w.with_(I=shares[r], Is=sshares[r])
+        torch.cuda.empty_cache()
     torch.cuda.synchronize()
     print(f"inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
@@ -344,7 +363,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "topk": w.topk, "I": w.I,
                    "Is": w.Is, "fmt": w.fmt, "band": [w.band_lo, w.band_hi],
-                   "combine": args.combine,
+                   "combine": args.combine, "tp": tp_info,
                    "l2_mall_eviction": {"read": "1 GiB read", "write": "1 GiB write",
                                         "none": None}[args.flush]},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},

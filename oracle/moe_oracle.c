@@ -135,6 +135,92 @@ int oracle_topk(const float* logits, int T, int E, int k, int32_t* ids, double* 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Sigmoid router with a selection bias.                                      */
+/*                                                                            */
+/* [P5] "What exists now": GLM's own router (glm_route) is sigmoid + bias     */
+/* top-k with raw-score weights.  Reading: score s_e = sigmoid(l_e) of the    */
+/* unbiased logit; experts are ordered by (s_e + bias_e descending, id        */
+/* ascending), -0.0 counting as +0.0; the weight of pick j is its raw score   */
+/* s_{id_j}, not renormalised.  The selection turns on fp32 values, so the    */
+/* sigmoid is a fixed fp32 computation that both sides write out in full:     */
+/*   exp_c(x): n = rint(x * log2(e)) (fp32 product, ties to even);           */
+/*             r = fma(-n, LN2_HI, x); r = fma(-n, LN2_LO, r) with LN2_HI =   */
+/*             0.693145751953125 (exact in 16 bits) and LN2_LO = the fp32    */
+/*             value nearest ln 2 - LN2_HI;                                   */
+/*             p = Horner over the Taylor terms 1/i!, i = 6 down to 0, with  */
+/*             fp32 coefficients (nearest to 1/i!): p = fma(p, r, c_i);       */
+/*             exp_c = p * 2^n (exact scaling; overflow to +inf);            */
+/*             x > 88.8 gives +inf and x < -104 gives +0 directly.            */
+/*   sigmoid_c(l) = 1 / (1 + exp_c(-l)), each operation one IEEE fp32         */
+/*             rounding (correctly rounded division).                          */
+/* ------------------------------------------------------------------------ */
+static const float EXPC_LOG2E = 1.44269504088896341f;
+static const float EXPC_LN2_HI = 0.693145751953125f;
+static const float EXPC_LN2_LO = 1.42860682030941723212e-6f;
+
+float oracle_exp_c(float x)
+{
+    if (x > 88.8f) return INFINITY;
+    if (x < -104.0f) return 0.0f;
+    float t = x * EXPC_LOG2E;
+    float n = rintf(t);
+    float r = fmaf(-n, EXPC_LN2_HI, x);
+    r = fmaf(-n, EXPC_LN2_LO, r);
+    /* 1/i! for i = 6..0, each rounded to the nearest fp32 */
+    const float c[7] = {(float)(1.0 / 720.0), (float)(1.0 / 120.0), (float)(1.0 / 24.0),
+                        (float)(1.0 / 6.0), 0.5f, 1.0f, 1.0f};
+    float p = c[0];
+    for (int i = 1; i < 7; ++i) p = fmaf(p, r, c[i]);
+    return ldexpf(p, (int)n);
+}
+
+float oracle_sigmoid_c(float l)
+{
+    float e = oracle_exp_c(-l);
+    float d = 1.0f + e;
+    return 1.0f / d;
+}
+
+/* Row of unbiased logits -> k picks by (score + bias desc, id asc) and their */
+/* raw scores. */
+static void topk_sigmoid_row(const float* l, const float* bias, int E, int k, int32_t* ids,
+                             double* w)
+{
+    float* key = (float*)malloc(sizeof(float) * (size_t)E);
+    float* sc = (float*)malloc(sizeof(float) * (size_t)E);
+    unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+    for (int e = 0; e < E; ++e) {
+        sc[e] = oracle_sigmoid_c(l[e]);
+        float v = bias ? sc[e] + bias[e] : sc[e];
+        if (v == 0.0f) v = 0.0f;
+        key[e] = v;
+    }
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken[e]) continue;
+            if (best < 0 || key[e] > key[best]) best = e; /* strict: ties keep lower id */
+        }
+        taken[best] = 1;
+        ids[j] = best;
+        w[j] = (double)sc[best];
+    }
+    free(key);
+    free(sc);
+    free(taken);
+}
+
+int oracle_topk_sigmoid(const float* logits, const float* bias, int T, int E, int k, int32_t* ids,
+                        double* w)
+{
+    if (T < 0 || E <= 0 || k < 1 || k > E) return OR_EINVAL;
+    for (int t = 0; t < T; ++t)
+        topk_sigmoid_row(logits + (size_t)t * E, bias, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+    return OR_OK;
+}
+
+
+/* ------------------------------------------------------------------------ */
 /* Dispatch for the band [lo, hi).                                            */
 /*                                                                            */
 /* [P1] "What landed": each rank contributes only the picks it owns.  The     */
@@ -453,12 +539,13 @@ static void shared_ffn(const double* x, const uint16_t* wgu, const uint16_t* wd,
 /* ------------------------------------------------------------------------ */
 static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                       const oracle_experts* ex, const uint16_t* sh_wgu, const uint16_t* sh_wd,
-                      int Is, int use_band, int lo, int hi, int k, int combine,
+                      int Is, int use_band, int lo, int hi, int k, int combine, int router,
                       const int32_t* rows, int nrows, double* out, int32_t* ids_out,
                       double* w_out)
 {
     if (T < 1 || H % 256 != 0 || E < 1 || k < 1 || k > E) return OR_EINVAL;
     if (combine != 0 && combine != 1) return OR_EINVAL;
+    if (router != 0 && router != 1) return OR_EINVAL;
     int node_lo = 0, node_lev = 0;
     if (combine == 1 && oracle_tree_node(E, use_band ? lo : 0, use_band ? hi : E, &node_lo,
                                          &node_lev) != OR_OK)
@@ -492,11 +579,14 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
             }
             for (int e = 0; e < E; ++e) {
                 float v = oracle_dot_r(xf, wr + (size_t)e * H, H);
-                if (bias) v = v + bias[e];
+                if (bias && router == 0) v = v + bias[e];
                 if (v == 0.0f) v = 0.0f;
                 l[e] = v;
             }
-            topk_row(l, E, k, ids, w);
+            if (router == 0)
+                topk_row(l, E, k, ids, w);
+            else
+                topk_sigmoid_row(l, bias, E, k, ids, w);
             double* acc = out + (size_t)r * H;
             for (int c = 0; c < H; ++c) acc[c] = 0.0;
             int m = 0;
@@ -540,11 +630,11 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
 /* The layer restricted to the expert band [lo, hi). */
 int oracle_moe_ffn(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                    const oracle_experts* ex, const uint16_t* sh_wgu, const uint16_t* sh_wd, int Is,
-                   int lo, int hi, int k, int combine, const int32_t* rows, int nrows,
-                   double* out, int32_t* ids_out, double* w_out)
+                   int lo, int hi, int k, int combine, int router, const int32_t* rows,
+                   int nrows, double* out, int32_t* ids_out, double* w_out)
 {
-    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 1, lo, hi, k, combine, rows,
-                      nrows, out, ids_out, w_out);
+    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 1, lo, hi, k, combine, router,
+                      rows, nrows, out, ids_out, w_out);
 }
 
 /* The routed monolith: the same layer with no band logic at all (every pick
@@ -554,7 +644,7 @@ int oracle_moe_ffn_monolith(const uint16_t* x, int T, int H, const float* wr, co
                             const uint16_t* sh_wd, int Is, int k, const int32_t* rows, int nrows,
                             double* out)
 {
-    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 0, 0, E, k, 0, rows, nrows,
+    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 0, 0, E, k, 0, 0, rows, nrows,
                       out, NULL, NULL);
 }
 

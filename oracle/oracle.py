@@ -76,7 +76,13 @@ def _load():
         lib.oracle_expert_matrix.argtypes = [ctypes.POINTER(_Experts), I32, I32, P]
         layer = [P, I32, I32, P, P, I32, ctypes.POINTER(_Experts), P, P, I32]
         lib.oracle_moe_ffn.restype = I32
-        lib.oracle_moe_ffn.argtypes = layer + [I32, I32, I32, I32, P, I32, P, P, P]
+        lib.oracle_moe_ffn.argtypes = layer + [I32, I32, I32, I32, I32, P, I32, P, P, P]
+        lib.oracle_exp_c.restype = ctypes.c_float
+        lib.oracle_exp_c.argtypes = [ctypes.c_float]
+        lib.oracle_sigmoid_c.restype = ctypes.c_float
+        lib.oracle_sigmoid_c.argtypes = [ctypes.c_float]
+        lib.oracle_topk_sigmoid.restype = I32
+        lib.oracle_topk_sigmoid.argtypes = [P, P, I32, I32, I32, P, P]
         lib.oracle_tree_node.restype = I32
         lib.oracle_tree_node.argtypes = [I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         lib.oracle_tree_value.restype = I32
@@ -151,6 +157,30 @@ def topk(logits: torch.Tensor, k: int):
     ids = torch.empty((T, k), dtype=torch.int32)
     w = torch.empty((T, k), dtype=torch.float64)
     _check(_load().oracle_topk(_ptr(lg), T, E, k, _ptr(ids), _ptr(w)), "topk")
+    return ids, w
+
+
+def exp_c(x: float) -> float:
+    """The fixed fp32 exp of the sigmoid router (range reduction by ln 2,
+    degree-6 Taylor polynomial, exact scaling)."""
+    return float(_load().oracle_exp_c(float(x)))
+
+
+def sigmoid_c(x: float) -> float:
+    """The fixed fp32 sigmoid 1 / (1 + exp_c(-x))."""
+    return float(_load().oracle_sigmoid_c(float(x)))
+
+
+def topk_sigmoid(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int):
+    """Sigmoid router: picks by (sigmoid(l) + bias desc, id asc), weights the
+    raw scores.  logits are unbiased."""
+    lg = _cpu(logits).float()
+    b = None if bias is None else _cpu(bias).float()
+    T, E = lg.shape
+    ids = torch.empty((T, k), dtype=torch.int32)
+    w = torch.empty((T, k), dtype=torch.float64)
+    _check(_load().oracle_topk_sigmoid(_ptr(lg), _ptr(b), T, E, k, _ptr(ids), _ptr(w)),
+           "topk_sigmoid")
     return ids, w
 
 
@@ -253,12 +283,16 @@ def tree_merge(parts, bands, E: int, shared: Optional[torch.Tensor] = None) -> t
 
 def moe_ffn(inputs: dict, E: int, I: int, Is: int, lo: int, hi: int, k: int,
             rows: Optional[torch.Tensor] = None, experts: Optional[Experts] = None,
-            combine: str = "pick"):
+            combine: str = "pick", router: str = "softmax"):
     """The layer for the band [lo, hi) on the listed rows (all rows if None).
     combine: "pick" (pick order) or "tree" (canonical tree over expert ids).
+    router: "softmax" (bias on the logits) or "sigmoid" (bias steers the
+    selection only, weights are the raw scores).
     Returns (out fp64 [nrows, H], ids int32 [nrows, k], w fp64 [nrows, k])."""
     if combine not in ("pick", "tree"):
         raise ValueError(f"oracle: combine {combine!r}")
+    if router not in ("softmax", "sigmoid"):
+        raise ValueError(f"oracle: router {router!r}")
     x, wr, b = _cpu(inputs["x"]), _cpu(inputs["router_w"]).float(), _cpu(inputs["bias"])
     T, H = x.shape
     ex = experts if experts is not None else Experts(inputs["experts"], E, H, I)
@@ -277,7 +311,8 @@ def moe_ffn(inputs: dict, E: int, I: int, Is: int, lo: int, hi: int, k: int,
         raise ValueError("oracle: bias length != router experts")
     _check(_load().oracle_moe_ffn(_ptr(x), T, H, _ptr(wr), _ptr(b), Er, ctypes.byref(ex.desc),
                                   _ptr(sgu), _ptr(sd), Is if sh else 0, lo, hi, k,
-                                  0 if combine == "pick" else 1, _ptr(r), nrows,
+                                  0 if combine == "pick" else 1, 0 if router == "softmax" else 1,
+                                  _ptr(r), nrows,
                                   _ptr(out), _ptr(ids), _ptr(w)), "moe_ffn")
     return out, ids, w
 
