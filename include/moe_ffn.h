@@ -89,6 +89,7 @@ extern "C" {
 #define MOE_E_HIP (-9)       /* the HIP runtime reported an error while enqueuing */
 #define MOE_E_DEVICE (-10)   /* the current device is not a gfx950 GPU */
 #define MOE_E_COMBINE (-11)  /* unknown combine mode or reduce order */
+#define MOE_E_ROUTER (-12)   /* unknown router mode */
 
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_PARTS 64 /* partials one moe_ffn_reduce call adds */
@@ -105,12 +106,28 @@ typedef struct moe_x {
     int32_t T, H;
 } moe_x;
 
-/* Router: fp32 gate weight [E, H] and an optional fp32 per-expert bias [E]
- * added to the logits before selection and weighting. */
+/* Router modes. */
+#define MOE_ROUTER_SOFTMAX 0 /* steps 1-2 above: the bias shifts the logits */
+#define MOE_ROUTER_SIGMOID 1 /* sigmoid + bias top-k, raw-score weights */
+
+/* Router: fp32 gate weight [E, H] and an optional fp32 per-expert bias [E].
+ * MOE_ROUTER_SOFTMAX: the bias is added to the logits before selection and
+ * weighting.  MOE_ROUTER_SIGMOID ([P5] "What exists now": GLM's glm_route is
+ * sigmoid + bias top-k with raw-score weights): score s_e = sigmoid(l_e) of
+ * the unbiased logit; experts are ordered by (s_e + bias_e descending, id
+ * ascending, -0.0 as +0.0); the weight of a pick is its raw score s_e, not
+ * renormalised.  The selection turns on fp32 values, so the sigmoid is fixed
+ * step by step: exp_c(x) = p(r) * 2^n with n = rint(x * log2(e)) (fp32
+ * product, ties to even), r = fma(-n, ln2_lo, fma(-n, ln2_hi, x)) where
+ * ln2_hi = 0.693145751953125 and ln2_lo is the fp32 value nearest
+ * ln 2 - ln2_hi, p(r) the Taylor terms 1/i! (i = 6..0, nearest fp32) in
+ * Horner form with fused multiply-adds; exp_c(x) = +inf for x > 88.8 and +0
+ * for x < -104; sigmoid(l) = 1 / (1 + exp_c(-l)), IEEE fp32 operations. */
 typedef struct moe_router {
     const float* w;    /* fp32 [E, H] */
     const float* bias; /* fp32 [E] or NULL */
     int32_t E, H;
+    int32_t mode; /* MOE_ROUTER_SOFTMAX or MOE_ROUTER_SIGMOID */
 } moe_router;
 
 /* Routed experts, all E of them (the band selects which ones run).

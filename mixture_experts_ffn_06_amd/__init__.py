@@ -28,8 +28,11 @@ EVENT_SLOTS = ("router", "topk", "dispatch", "gu_gemv", "gu_mfma", "dn_gemv", "d
 ERRORS = {
     0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_DIM", -4: "MOE_E_BAND",
     -5: "MOE_E_TOPK", -6: "MOE_E_FORMAT", -7: "MOE_E_WORKSPACE", -8: "MOE_E_ALIGN",
-    -9: "MOE_E_HIP", -10: "MOE_E_DEVICE", -11: "MOE_E_COMBINE",
+    -9: "MOE_E_HIP", -10: "MOE_E_DEVICE", -11: "MOE_E_COMBINE", -12: "MOE_E_ROUTER",
 }
+MOE_ROUTER_SOFTMAX = 0
+MOE_ROUTER_SIGMOID = 1
+_ROUTER = {"softmax": MOE_ROUTER_SOFTMAX, "sigmoid": MOE_ROUTER_SIGMOID}
 MOE_COMBINE_PICK = 0
 MOE_COMBINE_TREE = 1
 MOE_REDUCE_RANK = 0
@@ -52,7 +55,7 @@ class MoeX(ctypes.Structure):
 
 class MoeRouter(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("E", ctypes.c_int32),
-                ("H", ctypes.c_int32)]
+                ("H", ctypes.c_int32), ("mode", ctypes.c_int32)]
 
 
 class MoeExperts(ctypes.Structure):
@@ -127,7 +130,7 @@ def _fmt_code(experts: dict) -> int:
     return MOE_BF16 if experts["fmt"] == "bf16" else MOE_W4A16
 
 
-def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None):
+def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None, router="softmax"):
     """ctypes descriptors for the tensors (no copies, no checks: the library checks)."""
     T, H = x.shape
     fmt = _fmt_code(experts)
@@ -136,7 +139,8 @@ def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None):
     if I is None:
         I = (experts["w_gate_up"] if fmt == MOE_BF16 else experts["q_gate_up"]).shape[1] // 2
     dx = MoeX(_p(x), T, H)
-    dr = MoeRouter(_p(router_w), _p(bias), router_w.shape[0], router_w.shape[1])
+    dr = MoeRouter(_p(router_w), _p(bias), router_w.shape[0], router_w.shape[1],
+                   _ROUTER[router] if router in _ROUTER else int(router))
     de = MoeExperts(E, H, I, fmt, 32 if fmt == MOE_W4A16 else 0,
                     _p(experts.get("w_gate_up")), _p(experts.get("w_down")),
                     _p(experts.get("q_gate_up")), _p(experts.get("s_gate_up")),
@@ -154,7 +158,7 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
             out: Optional[torch.Tensor] = None, exports: Optional[dict] = None,
             workspace: Optional[torch.Tensor] = None, stream=None, events=None,
             combine: str = "pick", y_shared: Optional[torch.Tensor] = None,
-            y_picks: Optional[torch.Tensor] = None) -> torch.Tensor:
+            y_picks: Optional[torch.Tensor] = None, router: str = "softmax") -> torch.Tensor:
     """Run the layer for the expert band [band_lo, band_hi).
 
     x bf16 [T,H]; router_w fp32 [E,H]; bias fp32 [E] or None; experts / shared
@@ -165,13 +169,14 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
     combine: "pick" (pick order) or "tree" (canonical tree over expert ids).
     y_shared: fp32 [T,H] receiving the shared expert's output instead of
     adding it; y_picks: fp32 [T*topk,H] receiving the per-pick expert outputs
-    in perm order.
+    in perm order.  router: "softmax" (bias on the logits) or "sigmoid" (bias
+    steers the selection only, raw-score weights).
     """
     if combine not in _COMBINE:
         raise MoeError(-11, f"combine must be one of {sorted(_COMBINE)}")
     lib = load_library()
     T, H = x.shape
-    dx, dr, de, ds = make_descriptors(x, router_w, bias, experts, shared)
+    dx, dr, de, ds = make_descriptors(x, router_w, bias, experts, shared, router=router)
     dev = x.device
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -329,4 +334,5 @@ def tree_pieces(lo: int, hi: int, E: int):
 __all__ = ["moe_ffn", "reduce", "tree_pieces", "tp_shares", "tp_slice_experts", "tp_slice_shared", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
            "MOE_BF16", "MOE_W4A16", "MOE_NUM_EVENTS", "EVENT_SLOTS", "make_descriptors",
            "MoeX", "MoeRouter", "MoeExperts", "MoeShared", "MoeOut", "MOE_COMBINE_PICK",
-           "MOE_COMBINE_TREE", "MOE_REDUCE_RANK", "MOE_REDUCE_TREE", "MOE_MAX_PARTS"]
+           "MOE_COMBINE_TREE", "MOE_REDUCE_RANK", "MOE_REDUCE_TREE", "MOE_MAX_PARTS",
+           "MOE_ROUTER_SOFTMAX", "MOE_ROUTER_SIGMOID"]

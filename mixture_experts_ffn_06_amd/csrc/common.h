@@ -120,10 +120,13 @@ inline void allow_lds(F* kernel, size_t bytes) {
 // Host-side launchers (one per kernel family).
 void launch_router_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H,
                           int E, float* logits, hipStream_t st);
-void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                        hipStream_t st);
+// sigmoid = 0: softmax over the picks of biased logits; 1: picks by
+// sigmoid + bias of unbiased logits, raw-score weights (topk.h)
+void launch_router_topk(const float* logits, const float* bias, int sigmoid, int T, int E, int k,
+                        int32_t* ids, float* w, hipStream_t st);
 // Batches of at most 16 rows: top-k and the dispatch in one block.
-void launch_topk_dispatch_small(const float* logits, int E, float* wts, int32_t* ids, int T, int k,
+void launch_topk_dispatch_small(const float* logits, const float* bias, int sigmoid, int E, float* wts,
+                                int32_t* ids, int T, int k,
                                 int lo, int hi, bool has_shared, int32_t* counts, int32_t* offsets,
                                 int32_t* perm, int32_t* pos, Group* groups, int32_t* gemv_list,
                                 int32_t* mfma_list, int mfma_cap, int32_t* plan_counts, hipStream_t st);

@@ -316,20 +316,22 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
 // them.
 template <int PER>
 __global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(
-    const float* __restrict__ logits, int E, float* __restrict__ wts, int32_t* __restrict__ ids,
+    const float* __restrict__ logits, const float* __restrict__ bias, int sigmoid, int E,
+    float* __restrict__ wts, int32_t* __restrict__ ids,
     int T, int k, int lo, int nb, bool has_shared, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
     Group* __restrict__ groups, int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list,
     int mfma_cap, int32_t* __restrict__ plan_counts) {
     __shared__ int32_t s_ids[16 * 16];  // rows x picks (at most 16 each)
     const int wave = threadIdx.x >> 6;
-    if (wave < T) topk_row<PER>(logits, wave, E, k, ids, wts, s_ids);
+    if (wave < T) topk_row<PER>(logits, bias, sigmoid, wave, E, k, ids, wts, s_ids);
     __syncthreads();
     dispatch_small_body(s_ids, T, k, lo, nb, has_shared, counts, offsets, perm, pos, groups, gemv_list,
                         mfma_list, mfma_cap, plan_counts);
 }
 
-void launch_topk_dispatch_small(const float* logits, int E, float* wts, int32_t* ids, int T, int k,
+void launch_topk_dispatch_small(const float* logits, const float* bias, int sigmoid, int E, float* wts,
+                                int32_t* ids, int T, int k,
                                 int lo, int hi, bool has_shared, int32_t* counts, int32_t* offsets,
                                 int32_t* perm, int32_t* pos, Group* groups, int32_t* gemv_list,
                                 int32_t* mfma_list, int mfma_cap, int32_t* plan_counts, hipStream_t st) {
@@ -337,7 +339,7 @@ void launch_topk_dispatch_small(const float* logits, int E, float* wts, int32_t*
     const size_t lds = sizeof(unsigned long long) * 4 * (size_t)nb + sizeof(int) * ((size_t)nb + 1);
     const int per = (E + 63) / 64;
 #define MOE_TOPK_DISPATCH(P)                                                                          \
-    topk_dispatch_small_kernel<P><<<1, 1024, lds, st>>>(logits, E, wts, ids, T, k, lo, nb, has_shared, \
+    topk_dispatch_small_kernel<P><<<1, 1024, lds, st>>>(logits, bias, sigmoid, E, wts, ids, T, k, lo, nb, has_shared, \
                                                          counts, offsets, perm, pos, groups, gemv_list, \
                                                          mfma_list, mfma_cap, plan_counts)
     if (per <= 1)

@@ -124,6 +124,7 @@ extern "C" const char* moe_ffn_strerror(int32_t code) {
         case MOE_E_HIP: return "HIP runtime error while enqueuing";
         case MOE_E_DEVICE: return "the current device is not a gfx950 GPU";
         case MOE_E_COMBINE: return "unknown combine mode or reduce order";
+        case MOE_E_ROUTER: return "unknown router mode";
         default: return "unknown error code";
     }
 }
@@ -151,6 +152,8 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     if (router_w->H != H || experts->H != H || (shared && shared->H != H)) return MOE_E_SHAPE;
     if (shared && Is <= 0) return MOE_E_SHAPE;
     if (router_w->E != E) return MOE_E_DIM;
+    if (router_w->mode != MOE_ROUTER_SOFTMAX && router_w->mode != MOE_ROUTER_SIGMOID)
+        return MOE_E_ROUTER;
     {
         const int32_t rc = check_sizes(T, H, E, I, Is, topk, fmt);
         if (rc != MOE_OK) return rc;
@@ -206,18 +209,22 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     const int nb = band_hi - band_lo;
     const bool has_shared = shared != nullptr;
     mark(MOE_EV_ROUTER);
-    moe::launch_router_logits(static_cast<const uint16_t*>(x->ptr), router_w->w, router_w->bias, T,
-                              H, E, logits, st);
+    // softmax: the bias shifts the logits; sigmoid: it steers the selection
+    // only and joins at the top-k
+    const int sigmoid = router_w->mode == MOE_ROUTER_SIGMOID ? 1 : 0;
+    moe::launch_router_logits(static_cast<const uint16_t*>(x->ptr), router_w->w,
+                              sigmoid ? nullptr : router_w->bias, T, H, E, logits, st);
+    const float* sel_bias = sigmoid ? router_w->bias : nullptr;
     mark(MOE_EV_TOPK);
     const int mfma_cap = max_mfma_tiles(T, E, topk);
     if (T <= 16) {
         // one block: top-k (a wave per row) and the dispatch
         mark(MOE_EV_DISPATCH);
-        moe::launch_topk_dispatch_small(logits, E, wts, ids, T, topk, band_lo, band_hi, has_shared, counts,
+        moe::launch_topk_dispatch_small(logits, sel_bias, sigmoid, E, wts, ids, T, topk, band_lo, band_hi, has_shared, counts,
                                         offsets, perm, pos, groups, gemv_list, mfma_list, mfma_cap,
                                         plan_counts, st);
     } else {
-        moe::launch_router_topk(logits, T, E, topk, ids, wts, st);
+        moe::launch_router_topk(logits, sel_bias, sigmoid, T, E, topk, ids, wts, st);
         mark(MOE_EV_DISPATCH);
         moe::launch_dispatch(ids, T, topk, band_lo, band_hi, has_shared, blkcnt, counts, offsets, perm,
                              pos, groups, gemv_list, mfma_list, mfma_cap, plan_counts, st);

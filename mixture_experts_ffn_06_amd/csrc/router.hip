@@ -135,27 +135,28 @@ void launch_router_logits(const uint16_t* x, const float* wr, const float* bias,
 
 // Top-k of one row per wave (topk.h).
 template <int PER>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int T,
-                                                          int E, int k, int32_t* __restrict__ ids,
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          const float* __restrict__ bias, int sigmoid,
+                                                          int T, int E, int k, int32_t* __restrict__ ids,
                                                           float* __restrict__ w) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    topk_row<PER>(logits, t, E, k, ids, w, nullptr);
+    topk_row<PER>(logits, bias, sigmoid, t, E, k, ids, w, nullptr);
 }
-void launch_router_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                        hipStream_t st) {
+void launch_router_topk(const float* logits, const float* bias, int sigmoid, int T, int E, int k,
+                        int32_t* ids, float* w, hipStream_t st) {
     int blocks = (T + 3) / 4;
     int per = (E + 63) / 64;
     if (per <= 1)
-        router_topk_kernel<1><<<blocks, 256, 0, st>>>(logits, T, E, k, ids, w);
+        router_topk_kernel<1><<<blocks, 256, 0, st>>>(logits, bias, sigmoid, T, E, k, ids, w);
     else if (per <= 2)
-        router_topk_kernel<2><<<blocks, 256, 0, st>>>(logits, T, E, k, ids, w);
+        router_topk_kernel<2><<<blocks, 256, 0, st>>>(logits, bias, sigmoid, T, E, k, ids, w);
     else if (per <= 4)
-        router_topk_kernel<4><<<blocks, 256, 0, st>>>(logits, T, E, k, ids, w);
+        router_topk_kernel<4><<<blocks, 256, 0, st>>>(logits, bias, sigmoid, T, E, k, ids, w);
     else if (per <= 8)
-        router_topk_kernel<8><<<blocks, 256, 0, st>>>(logits, T, E, k, ids, w);
+        router_topk_kernel<8><<<blocks, 256, 0, st>>>(logits, bias, sigmoid, T, E, k, ids, w);
     else
-        router_topk_kernel<16><<<blocks, 256, 0, st>>>(logits, T, E, k, ids, w);
+        router_topk_kernel<16><<<blocks, 256, 0, st>>>(logits, bias, sigmoid, T, E, k, ids, w);
 }
 
 }  // namespace moe

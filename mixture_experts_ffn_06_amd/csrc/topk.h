@@ -50,20 +50,60 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
     i = bi;
 }
 
+// The sigmoid router's fixed fp32 sigmoid ([P5] "What exists now": GLM's
+// router is sigmoid + bias top-k; the selection turns on these fp32 values,
+// so every step is pinned): exp_c(x) reduces x by n = rint(x log2 e) times
+// ln 2 split in two parts (0.693145751953125, exact in 16 bits, and the fp32
+// value nearest the rest), evaluates the Taylor terms 1/i!, i = 6..0, as fp32
+// coefficients in Horner form with fused multiply-adds, and scales by 2^n;
+// sigmoid_c(l) = 1 / (1 + exp_c(-l)) with IEEE fp32 operations.
+__device__ __forceinline__ float exp_c(float x) {
+#pragma clang fp contract(off)
+    if (x > 88.8f) return INFINITY;
+    if (x < -104.0f) return 0.0f;
+    const float n = __builtin_rintf(x * 1.44269504088896341f);
+    float r = __builtin_fmaf(-n, 0.693145751953125f, x);
+    r = __builtin_fmaf(-n, 1.42860682030941723212e-6f, r);
+    float p = (float)(1.0 / 720.0);
+    p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float sigmoid_c(float l) {
+#pragma clang fp contract(off)
+    const float d = 1.0f + exp_c(-l);
+    return 1.0f / d;
+}
+
 // Row t of logits [T, E] (PER = ceil(E / 64) values per lane): writes the k
 // picks and weights to ids[t k ..], w[t k ..] and, when sids is not null, the
 // ids to sids[t k ..] as well.  Called by all 64 lanes of a wave.
+// sigmoid = 0: the logits carry the bias; picks by logit, weights the softmax
+// over the picks.  sigmoid = 1: the logits are unbiased; picks by
+// sigmoid_c(l) + bias (-0.0 as +0.0), weights the picks' raw scores.
 template <int PER>
-__device__ __forceinline__ void topk_row(const float* __restrict__ logits, int t, int E, int k,
+__device__ __forceinline__ void topk_row(const float* __restrict__ logits, const float* __restrict__ bias,
+                                         int sigmoid, int t, int E, int k,
                                          int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sids) {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
-    float v[PER];
+    float v[PER], sc[PER];
     uint32_t taken = 0;
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
         int e = lane + 64 * m;
         v[m] = (e < E) ? logits[(size_t)t * E + e] : -INFINITY;
+        sc[m] = 0.0f;
+        if (sigmoid && e < E) {
+            sc[m] = sigmoid_c(v[m]);
+            float key = bias ? sc[m] + bias[e] : sc[m];
+            v[m] = key == 0.0f ? 0.0f : key;
+        }
         if (e >= E) taken |= 1u << m;
     }
     float sel_v[16];
@@ -91,6 +131,26 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ logits, int t
         if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
         sel_v[j] = bv;
         sel_id[j] = bid;
+        if (sigmoid) {
+            // the pick's raw score, from the lane that holds it
+            float mine = 0.0f;
+#pragma unroll
+            for (int m = 0; m < PER; ++m)
+                if (m == (bid >> 6)) mine = sc[m];
+            sel_v[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), bid & 63));
+        }
+    }
+    if (sigmoid) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (j >= k) break;
+            if (lane == j) {
+                ids[(size_t)t * k + j] = sel_id[j];
+                w[(size_t)t * k + j] = sel_v[j];
+                if (sids) sids[t * k + j] = sel_id[j];
+            }
+        }
+        return;
     }
     const float m0 = sel_v[0];
     float a[16];
