@@ -95,6 +95,55 @@ int oracle_router_logits(const uint16_t* x, int T, int H, const float* wr,
 }
 
 /* ------------------------------------------------------------------------ */
+/* RMSNorm of the rows before routing.                                        */
+/*                                                                            */
+/* [P2] "Per MoE layer": the expert side receives the normed rows; [P5]       */
+/* "What exists now" lists rmsnorm among the fixed-order fp32 glue kernels,    */
+/* and its first byte-gate run found the cross-lane total reaching only some  */
+/* lanes, which then ran inv_rms(0) ~ 316x -- 1/sqrt(eps) with eps = 1e-5.    */
+/* Every step here is one IEEE fp32 rounding:                                 */
+/*   ss  = sum of x[c]^2 in the R-order above (fused multiply-adds);          */
+/*   ms  = ss / H;  inv = 1 / sqrt(ms + eps);                                 */
+/*   xn[c] = bf16_rne((x[c] * inv) * g[c]).                                   */
+/* ------------------------------------------------------------------------ */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u); /* NaN */
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+static float rms_inv(const float* xf, int H, float eps)
+{
+    float ss = oracle_dot_r(xf, xf, H);
+    float ms = ss / (float)H;
+    float r = sqrtf(ms + eps);
+    return 1.0f / r;
+}
+
+/* x bf16 [T, H], gamma bf16 [H] -> xn bf16 [T, H]; inv [T] (may be NULL). */
+int oracle_rmsnorm(const uint16_t* x, int T, int H, const uint16_t* gamma, float eps,
+                   uint16_t* xn, float* inv)
+{
+    if (T < 0 || H % 256 != 0 || H <= 0) return OR_EINVAL;
+    float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+    for (int t = 0; t < T; ++t) {
+        for (int c = 0; c < H; ++c) xf[c] = bf16_to_f32(x[(size_t)t * H + c]);
+        float r = rms_inv(xf, H, eps);
+        if (inv) inv[t] = r;
+        for (int c = 0; c < H; ++c) {
+            float v = xf[c] * r;
+            v = v * bf16_to_f32(gamma[c]);
+            xn[(size_t)t * H + c] = f32_to_bf16_rne(v);
+        }
+    }
+    free(xf);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Top-k selection and renormalised weights, one row.                         */
 /*                                                                            */
 /* [P2] "Per MoE layer": the expert side receives the rows with their top-k   */
@@ -540,6 +589,7 @@ static void shared_ffn(const double* x, const uint16_t* wgu, const uint16_t* wd,
 static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                       const oracle_experts* ex, const uint16_t* sh_wgu, const uint16_t* sh_wd,
                       int Is, int use_band, int lo, int hi, int k, int combine, int router,
+                      const uint16_t* gamma, float eps, int residual,
                       const int32_t* rows, int nrows, double* out, int32_t* ids_out,
                       double* w_out)
 {
@@ -558,6 +608,7 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
     {
         float* xf = (float*)malloc(sizeof(float) * (size_t)H);
         double* xd = (double*)malloc(sizeof(double) * (size_t)H);
+        double* xres = (double*)malloc(sizeof(double) * (size_t)H);
         float* l = (float*)malloc(sizeof(float) * (size_t)E);
         int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
         double* w = (double*)malloc(sizeof(double) * (size_t)k);
@@ -573,10 +624,20 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
                 status = OR_EINVAL;
                 continue;
             }
-            for (int c = 0; c < H; ++c) {
-                xf[c] = bf16_to_f32(x[(size_t)t * H + c]);
-                xd[c] = (double)xf[c];
+            for (int c = 0; c < H; ++c) xf[c] = bf16_to_f32(x[(size_t)t * H + c]);
+            if (gamma) {
+                /* the layer sees the normed rows; the residual is the raw row */
+                float r = rms_inv(xf, H, eps);
+                for (int c = 0; c < H; ++c) {
+                    xres[c] = (double)xf[c];
+                    float v = xf[c] * r;
+                    v = v * bf16_to_f32(gamma[c]);
+                    xf[c] = bf16_to_f32(f32_to_bf16_rne(v));
+                }
+            } else {
+                for (int c = 0; c < H; ++c) xres[c] = (double)xf[c];
             }
+            for (int c = 0; c < H; ++c) xd[c] = (double)xf[c];
             for (int e = 0; e < E; ++e) {
                 float v = oracle_dot_r(xf, wr + (size_t)e * H, H);
                 if (bias && router == 0) v = v + bias[e];
@@ -609,6 +670,8 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
                 shared_ffn(xd, sh_wgu, sh_wd, H, Is, y);
                 for (int c = 0; c < H; ++c) acc[c] += y[c];
             }
+            if (residual)
+                for (int c = 0; c < H; ++c) acc[c] += xres[c];
             if (ids_out)
                 for (int j = 0; j < k; ++j) ids_out[(size_t)r * k + j] = ids[j];
             if (w_out)
@@ -616,6 +679,7 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
         }
         free(xf);
         free(xd);
+        free(xres);
         free(l);
         free(ids);
         free(w);
@@ -630,11 +694,12 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
 /* The layer restricted to the expert band [lo, hi). */
 int oracle_moe_ffn(const uint16_t* x, int T, int H, const float* wr, const float* bias, int E,
                    const oracle_experts* ex, const uint16_t* sh_wgu, const uint16_t* sh_wd, int Is,
-                   int lo, int hi, int k, int combine, int router, const int32_t* rows,
-                   int nrows, double* out, int32_t* ids_out, double* w_out)
+                   int lo, int hi, int k, int combine, int router, const uint16_t* gamma,
+                   float eps, int residual, const int32_t* rows, int nrows, double* out,
+                   int32_t* ids_out, double* w_out)
 {
     return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 1, lo, hi, k, combine, router,
-                      rows, nrows, out, ids_out, w_out);
+                      gamma, eps, residual, rows, nrows, out, ids_out, w_out);
 }
 
 /* The routed monolith: the same layer with no band logic at all (every pick
@@ -644,8 +709,8 @@ int oracle_moe_ffn_monolith(const uint16_t* x, int T, int H, const float* wr, co
                             const uint16_t* sh_wd, int Is, int k, const int32_t* rows, int nrows,
                             double* out)
 {
-    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 0, 0, E, k, 0, 0, rows, nrows,
-                      out, NULL, NULL);
+    return layer_rows(x, T, H, wr, bias, E, ex, sh_wgu, sh_wd, Is, 0, 0, E, k, 0, 0, NULL, 0.0f, 0,
+                      rows, nrows, out, NULL, NULL);
 }
 
 /* Dequantised weight matrix of one expert, for pins that compare the 4-bit

@@ -76,7 +76,10 @@ def _load():
         lib.oracle_expert_matrix.argtypes = [ctypes.POINTER(_Experts), I32, I32, P]
         layer = [P, I32, I32, P, P, I32, ctypes.POINTER(_Experts), P, P, I32]
         lib.oracle_moe_ffn.restype = I32
-        lib.oracle_moe_ffn.argtypes = layer + [I32, I32, I32, I32, I32, P, I32, P, P, P]
+        lib.oracle_moe_ffn.argtypes = layer + [I32, I32, I32, I32, I32, P, ctypes.c_float, I32,
+                                               P, I32, P, P, P]
+        lib.oracle_rmsnorm.restype = I32
+        lib.oracle_rmsnorm.argtypes = [P, I32, I32, P, ctypes.c_float, P, P]
         lib.oracle_exp_c.restype = ctypes.c_float
         lib.oracle_exp_c.argtypes = [ctypes.c_float]
         lib.oracle_sigmoid_c.restype = ctypes.c_float
@@ -184,6 +187,18 @@ def topk_sigmoid(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int):
     return ids, w
 
 
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-5):
+    """Normed bf16 rows (every step one fp32 rounding, the sum of squares in
+    R-order) and the per-row inverse RMS."""
+    xb = _cpu(x).to(torch.bfloat16).contiguous()
+    g = _cpu(gamma).to(torch.bfloat16).contiguous()
+    T, H = xb.shape
+    out = torch.empty((T, H), dtype=torch.bfloat16)
+    inv = torch.empty(T, dtype=torch.float32)
+    _check(_load().oracle_rmsnorm(_ptr(xb), T, H, _ptr(g), eps, _ptr(out), _ptr(inv)), "rmsnorm")
+    return out, inv
+
+
 def dispatch(ids: torch.Tensor, lo: int, hi: int):
     """Returns (counts [nb], offsets [nb+1], perm [N_in], pos [T*k])."""
     ids = _cpu(ids).to(torch.int32)
@@ -283,11 +298,14 @@ def tree_merge(parts, bands, E: int, shared: Optional[torch.Tensor] = None) -> t
 
 def moe_ffn(inputs: dict, E: int, I: int, Is: int, lo: int, hi: int, k: int,
             rows: Optional[torch.Tensor] = None, experts: Optional[Experts] = None,
-            combine: str = "pick", router: str = "softmax"):
+            combine: str = "pick", router: str = "softmax",
+            norm: Optional[torch.Tensor] = None, eps: float = 1e-5, residual: bool = False):
     """The layer for the band [lo, hi) on the listed rows (all rows if None).
     combine: "pick" (pick order) or "tree" (canonical tree over expert ids).
     router: "softmax" (bias on the logits) or "sigmoid" (bias steers the
-    selection only, weights are the raw scores).
+    selection only, weights are the raw scores).  norm: bf16 [H] RMSNorm
+    weight (the layer then runs on the normed rows); residual: add the raw
+    rows last.
     Returns (out fp64 [nrows, H], ids int32 [nrows, k], w fp64 [nrows, k])."""
     if combine not in ("pick", "tree"):
         raise ValueError(f"oracle: combine {combine!r}")
@@ -300,6 +318,7 @@ def moe_ffn(inputs: dict, E: int, I: int, Is: int, lo: int, hi: int, k: int,
     sgu = _cpu(sh["w_gate_up"]) if sh else None
     sd = _cpu(sh["w_down"]) if sh else None
     r = None if rows is None else _cpu(rows).to(torch.int32)
+    gm = None if norm is None else _cpu(norm).to(torch.bfloat16).contiguous()
     nrows = T if r is None else r.numel()
     out = torch.empty((nrows, H), dtype=torch.float64)
     ids = torch.empty((nrows, k), dtype=torch.int32)
@@ -312,7 +331,7 @@ def moe_ffn(inputs: dict, E: int, I: int, Is: int, lo: int, hi: int, k: int,
     _check(_load().oracle_moe_ffn(_ptr(x), T, H, _ptr(wr), _ptr(b), Er, ctypes.byref(ex.desc),
                                   _ptr(sgu), _ptr(sd), Is if sh else 0, lo, hi, k,
                                   0 if combine == "pick" else 1, 0 if router == "softmax" else 1,
-                                  _ptr(r), nrows,
+                                  _ptr(gm), eps, 1 if residual else 0, _ptr(r), nrows,
                                   _ptr(out), _ptr(ids), _ptr(w)), "moe_ffn")
     return out, ids, w
 
