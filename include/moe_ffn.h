@@ -100,10 +100,19 @@ extern "C" {
 #define MOE_BF16 0  /* bf16 weights */
 #define MOE_W4A16 1 /* 4-bit unsigned codes, bf16 scale and zero per 32 inputs */
 
-/* Rows: x is bf16 [T, H]. */
+/* Rows: x is bf16 [T, H].  With norm_w (bf16 [H]) the layer runs on the
+ * RMSNorm of the rows ([P2] "Per MoE layer": the expert side receives the
+ * normed rows; [P5] "What exists now": rmsnorm is a fixed-order fp32 glue
+ * kernel whose inv_rms(0) is about 316, i.e. eps = 1e-5): per row, the sum of
+ * squares in the router's fixed order (step 1 below), ms = ss / H,
+ * inv = 1 / sqrt(ms + eps) (correctly rounded), xn = bf16((x * inv) * norm_w)
+ * (round to nearest even); router and experts read xn.  eps must be finite
+ * and >= 0 (else MOE_E_SHAPE). */
 typedef struct moe_x {
     const void* ptr; /* bf16 [T, H] */
     int32_t T, H;
+    const void* norm_w; /* bf16 [H] or NULL: no norm */
+    float eps;
 } moe_x;
 
 /* Router modes. */
@@ -199,7 +208,10 @@ typedef struct moe_shared {
  *        the partials); ignored without a shared expert.
  * y_picks: NULL, or fp32 [T*topk, H]: row i receives the expert output of
  *        pick perm[i] before weighting (rows past N_in unspecified).
- * combine: MOE_COMBINE_PICK (0) or MOE_COMBINE_TREE. */
+ * combine: MOE_COMBINE_PICK (0) or MOE_COMBINE_TREE.
+ * residual: nonzero adds the raw rows x (not the normed ones) to y last, after
+ *        the shared expert ([P2]: the partials are the rows' residual updates).
+ * xn: NULL, or bf16 [T, H] receiving the normed rows (only with norm_w). */
 typedef struct moe_out {
     float* y; /* fp32 [T, H] */
     int32_t* topk_ids;
@@ -214,6 +226,8 @@ typedef struct moe_out {
     float* y_shared;
     float* y_picks;
     int32_t combine;
+    int32_t residual;
+    void* xn;
 } moe_out;
 
 /* Run the layer for the band [band_lo, band_hi) on `stream` (a hipStream_t;

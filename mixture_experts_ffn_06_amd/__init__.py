@@ -50,7 +50,8 @@ class MoeError(RuntimeError):
 
 
 class MoeX(ctypes.Structure):
-    _fields_ = [("ptr", ctypes.c_void_p), ("T", ctypes.c_int32), ("H", ctypes.c_int32)]
+    _fields_ = [("ptr", ctypes.c_void_p), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("norm_w", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
 class MoeRouter(ctypes.Structure):
@@ -78,7 +79,8 @@ class MoeOut(ctypes.Structure):
                 ("perm", ctypes.c_void_p), ("pos", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("stage_events", ctypes.c_void_p), ("y_shared", ctypes.c_void_p),
-                ("y_picks", ctypes.c_void_p), ("combine", ctypes.c_int32)]
+                ("y_picks", ctypes.c_void_p), ("combine", ctypes.c_int32),
+                ("residual", ctypes.c_int32), ("xn", ctypes.c_void_p)]
 
 
 _lib = None
@@ -130,7 +132,8 @@ def _fmt_code(experts: dict) -> int:
     return MOE_BF16 if experts["fmt"] == "bf16" else MOE_W4A16
 
 
-def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None, router="softmax"):
+def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None, router="softmax",
+                     norm=None, eps=1e-5):
     """ctypes descriptors for the tensors (no copies, no checks: the library checks)."""
     T, H = x.shape
     fmt = _fmt_code(experts)
@@ -138,7 +141,7 @@ def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None, router=
         E = (experts["w_gate_up"] if fmt == MOE_BF16 else experts["q_gate_up"]).shape[0]
     if I is None:
         I = (experts["w_gate_up"] if fmt == MOE_BF16 else experts["q_gate_up"]).shape[1] // 2
-    dx = MoeX(_p(x), T, H)
+    dx = MoeX(_p(x), T, H, _p(norm), eps)
     dr = MoeRouter(_p(router_w), _p(bias), router_w.shape[0], router_w.shape[1],
                    _ROUTER[router] if router in _ROUTER else int(router))
     de = MoeExperts(E, H, I, fmt, 32 if fmt == MOE_W4A16 else 0,
@@ -158,7 +161,9 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
             out: Optional[torch.Tensor] = None, exports: Optional[dict] = None,
             workspace: Optional[torch.Tensor] = None, stream=None, events=None,
             combine: str = "pick", y_shared: Optional[torch.Tensor] = None,
-            y_picks: Optional[torch.Tensor] = None, router: str = "softmax") -> torch.Tensor:
+            y_picks: Optional[torch.Tensor] = None, router: str = "softmax",
+            norm: Optional[torch.Tensor] = None, eps: float = 1e-5, residual: bool = False,
+            xn: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Run the layer for the expert band [band_lo, band_hi).
 
     x bf16 [T,H]; router_w fp32 [E,H]; bias fp32 [E] or None; experts / shared
@@ -170,13 +175,16 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
     y_shared: fp32 [T,H] receiving the shared expert's output instead of
     adding it; y_picks: fp32 [T*topk,H] receiving the per-pick expert outputs
     in perm order.  router: "softmax" (bias on the logits) or "sigmoid" (bias
-    steers the selection only, raw-score weights).
+    steers the selection only, raw-score weights).  norm: bf16 [H] RMSNorm
+    weight (the layer runs on the normed rows, eps as given); residual: add
+    the raw rows last; xn: bf16 [T,H] receiving the normed rows.
     """
     if combine not in _COMBINE:
         raise MoeError(-11, f"combine must be one of {sorted(_COMBINE)}")
     lib = load_library()
     T, H = x.shape
-    dx, dr, de, ds = make_descriptors(x, router_w, bias, experts, shared, router=router)
+    dx, dr, de, ds = make_descriptors(x, router_w, bias, experts, shared, router=router, norm=norm,
+                                      eps=eps)
     dev = x.device
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -201,7 +209,7 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
                   _p(ex.get("offsets")), _p(ex.get("perm")), _p(ex.get("pos")),
                   _p(workspace), workspace.numel(),
                   ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
-                  _p(y_shared), _p(y_picks), _COMBINE[combine])
+                  _p(y_shared), _p(y_picks), _COMBINE[combine], 1 if residual else 0, _p(xn))
     if stream is None:
         st = torch.cuda.current_stream(dev).cuda_stream if dev.type == "cuda" else 0
     else:

@@ -11,10 +11,22 @@
 // #310": fp32 partial rows.
 #include "common.h"
 
+// every product and sum below is rounded where it is written (the tree's
+// leaves are rounded products): no contraction into fused multiply-adds
+#pragma clang fp contract(off)
+
 namespace moe {
+
+// acc + four bf16 residual values (fp32 adds; the bf16 -> fp32 widening is exact)
+__device__ __forceinline__ float4 add_res(float4 acc, const uint16_t* r) {
+    const uint2 b = *reinterpret_cast<const uint2*>(r);
+    return make_float4(acc.x + bf16_lo(b.x), acc.y + bf16_hi(b.x), acc.z + bf16_lo(b.y),
+                       acc.w + bf16_hi(b.y));
+}
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_r,
                                                      const float* __restrict__ y_s,
+                                                     const uint16_t* __restrict__ res,
                                                      const int32_t* __restrict__ pos,
                                                      const float* __restrict__ w, int H, int k,
                                                      int ctiles, float* __restrict__ out) {
@@ -39,13 +51,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         acc.z = acc.z + v.z;
         acc.w = acc.w + v.w;
     }
+    if (res) acc = add_res(acc, res + (size_t)t * H + c);
     *reinterpret_cast<float4*>(out + (size_t)t * H + c) = acc;
 }
 
-void launch_combine(const float* y_r, const float* y_s, const int32_t* pos, const float* w, int T,
-                    int H, int k, float* out, hipStream_t st) {
+void launch_combine(const float* y_r, const float* y_s, const uint16_t* res, const int32_t* pos,
+                    const float* w, int T, int H, int k, float* out, hipStream_t st) {
     const int ctiles = (H / 4 + 255) / 256;
-    combine_kernel<<<T * ctiles, 256, 0, st>>>(y_r, y_s, pos, w, H, k, ctiles, out);
+    combine_kernel<<<T * ctiles, 256, 0, st>>>(y_r, y_s, res, pos, w, H, k, ctiles, out);
 }
 
 // ---- the canonical tree ------------------------------------------------------
@@ -78,6 +91,7 @@ __device__ __forceinline__ float4 norm4(float4 a) { return add4(a, make_float4(0
 // waits; entry m holds the final merges.
 __global__ __launch_bounds__(256) void combine_tree_kernel(const float* __restrict__ y_r,
                                                           const float* __restrict__ y_s,
+                                                          const uint16_t* __restrict__ res,
                                                           const int32_t* __restrict__ ids,
                                                           const int32_t* __restrict__ pos,
                                                           const float* __restrict__ w, int H, int k,
@@ -179,15 +193,16 @@ __global__ __launch_bounds__(256) void combine_tree_kernel(const float* __restri
     }
     if (__builtin_amdgcn_readfirstlane(s_rootnorm)) cur = norm4(cur);
     if (y_s) cur = add4(cur, *reinterpret_cast<const float4*>(y_s + (size_t)t * H + c));
+    if (res) cur = add_res(cur, res + (size_t)t * H + c);
     *reinterpret_cast<float4*>(out + (size_t)t * H + c) = cur;
 }
 
-void launch_combine_tree(const float* y_r, const float* y_s, const int32_t* ids, const int32_t* pos,
-                         const float* w, int T, int H, int k, int node_level, float* out,
-                         hipStream_t st) {
+void launch_combine_tree(const float* y_r, const float* y_s, const uint16_t* res, const int32_t* ids,
+                         const int32_t* pos, const float* w, int T, int H, int k, int node_level,
+                         float* out, hipStream_t st) {
     const int ctiles = (H / 4 + 255) / 256;
-    combine_tree_kernel<<<T * ctiles, 256, 0, st>>>(y_r, y_s, ids, pos, w, H, k, ctiles, node_level,
-                                                    out);
+    combine_tree_kernel<<<T * ctiles, 256, 0, st>>>(y_r, y_s, res, ids, pos, w, H, k, ctiles,
+                                                    node_level, out);
 }
 
 // ---- sum of band partials ------------------------------------------------------
@@ -229,11 +244,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceProgram pg, const flo
                 if (lev == pg.root_level) acc = pend[lev];
         }
         if (y_s) acc = add4(acc, reinterpret_cast<const float4*>(y_s)[i]);
-        if (res) {
-            const uint2 b = reinterpret_cast<const uint2*>(res)[i];
-            acc = add4(acc, make_float4(bf16_bits_to_f32(b.x & 0xffffu), bf16_bits_to_f32(b.x >> 16),
-                                        bf16_bits_to_f32(b.y & 0xffffu), bf16_bits_to_f32(b.y >> 16)));
-        }
+        if (res) acc = add_res(acc, res + 4 * i);
         reinterpret_cast<float4*>(y)[i] = acc;
     }
 }

@@ -118,6 +118,8 @@ inline void allow_lds(F* kernel, size_t bytes) {
 }
 
 // Host-side launchers (one per kernel family).
+void launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int T, int H, uint16_t* xn,
+                    hipStream_t st);
 void launch_router_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H,
                           int E, float* logits, hipStream_t st);
 // sigmoid = 0: softmax over the picks of biased logits; 1: picks by
@@ -143,9 +145,9 @@ void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t 
 // 4-bit experts: the same pipeline with the codes dequantized in LDS, tiles
 // of 128 (and 256 as two halves), 64 and 32 rows; then the shared expert.
 void launch_mfma_w4(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st);
-void launch_combine(const float* y_r, const float* y_s, const int32_t* pos, const float* w,
+void launch_combine(const float* y_r, const float* y_s, const uint16_t* res, const int32_t* pos, const float* w,
                     int T, int H, int k, float* out, hipStream_t st);
-void launch_combine_tree(const float* y_r, const float* y_s, const int32_t* ids, const int32_t* pos,
+void launch_combine_tree(const float* y_r, const float* y_s, const uint16_t* res, const int32_t* ids, const int32_t* pos,
                          const float* w, int T, int H, int k, int node_level, float* out,
                          hipStream_t st);
 

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <mutex>
 #include <string.h>
 
@@ -20,7 +21,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 // Byte offsets of the scratch buffers inside the workspace.
 struct Layout {
     size_t logits, ids, w, counts, offsets, perm, pos, blkcnt, groups, gemv_list, mfma_list,
-        plan_counts, h_r, h_s, y_r, y_s, total;
+        plan_counts, h_r, h_s, y_r, y_s, xn, total;
 };
 
 int max_mfma_tiles(int T, int E, int k) {
@@ -49,6 +50,7 @@ Layout make_layout(int T, int H, int E, int I, int Is, int k) {
     L.h_s = o; o += align_up((size_t)T * (Is > 0 ? Is : 0) * 2);
     L.y_r = o; o += align_up(Tk * H * 4);
     L.y_s = o; o += align_up((size_t)T * H * 4);
+    L.xn = o; o += align_up((size_t)T * H * 2);
     L.total = o;
     return L;
 }
@@ -161,6 +163,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     if (fmt == MOE_W4A16 && experts->group != 32) return MOE_E_FORMAT;
     if (band_lo < 0 || band_hi > E || band_lo >= band_hi) return MOE_E_BAND;
     if (out->combine != MOE_COMBINE_PICK && out->combine != MOE_COMBINE_TREE) return MOE_E_COMBINE;
+    if (x->norm_w && !(x->eps >= 0.0f && x->eps < INFINITY)) return MOE_E_SHAPE;
 
     const bool bf = fmt == MOE_BF16;
     const void* ptrs[] = {x->ptr, router_w->w, router_w->bias,
@@ -170,7 +173,8 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
                           bf ? nullptr : experts->s_down, bf ? nullptr : experts->z_down,
                           shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
                           out->y, out->topk_ids, out->topk_w, out->counts, out->offsets,
-                          out->perm, out->pos, out->workspace, out->y_shared, out->y_picks};
+                          out->perm, out->pos, out->workspace, out->y_shared, out->y_picks,
+                          x->norm_w, out->xn};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MOE_E_ALIGN;
 
@@ -209,10 +213,18 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     const int nb = band_hi - band_lo;
     const bool has_shared = shared != nullptr;
     mark(MOE_EV_ROUTER);
+    // the layer runs on the normed rows when a norm weight is given; the
+    // residual is always the raw rows
+    const uint16_t* xin = static_cast<const uint16_t*>(x->ptr);
+    if (x->norm_w) {
+        uint16_t* xn = out->xn ? static_cast<uint16_t*>(out->xn) : reinterpret_cast<uint16_t*>(ws + L.xn);
+        moe::launch_rmsnorm(xin, static_cast<const uint16_t*>(x->norm_w), x->eps, T, H, xn, st);
+        xin = xn;
+    }
     // softmax: the bias shifts the logits; sigmoid: it steers the selection
     // only and joins at the top-k
     const int sigmoid = router_w->mode == MOE_ROUTER_SIGMOID ? 1 : 0;
-    moe::launch_router_logits(static_cast<const uint16_t*>(x->ptr), router_w->w,
+    moe::launch_router_logits(xin, router_w->w,
                               sigmoid ? nullptr : router_w->bias, T, H, E, logits, st);
     const float* sel_bias = sigmoid ? router_w->bias : nullptr;
     mark(MOE_EV_TOPK);
@@ -232,7 +244,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
 
     moe::ExpertArgs a;
     memset(&a, 0, sizeof a);
-    a.x = static_cast<const uint16_t*>(x->ptr);
+    a.x = xin;
     a.T = T;
     a.H = H;
     a.topk = topk;
@@ -288,11 +300,12 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     }
     mark(MOE_EV_COMBINE);
     const float* add_s = has_shared && !shared_apart ? a.y_s : nullptr;
+    const uint16_t* res = out->residual ? static_cast<const uint16_t*>(x->ptr) : nullptr;
     if (out->combine == MOE_COMBINE_TREE)
-        moe::launch_combine_tree(a.y_r, add_s, ids, pos, wts, T, H, topk,
+        moe::launch_combine_tree(a.y_r, add_s, res, ids, pos, wts, T, H, topk,
                                  tree_level(band_lo, band_hi), out->y, st);
     else
-        moe::launch_combine(a.y_r, add_s, pos, wts, T, H, topk, out->y, st);
+        moe::launch_combine(a.y_r, add_s, res, pos, wts, T, H, topk, out->y, st);
     mark(MOE_EV_END);
 
     if (hipGetLastError() != hipSuccess) return MOE_E_HIP;

@@ -115,6 +115,57 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
         }
 }
 
+// RMSNorm of the rows before routing ([P2] "GLM-5.3-Flash on CUDA: attention
+// on one GPU, routed experts on the Sparks (proposal) #214", "Per MoE layer":
+// the expert side receives the normed rows; [P5] "What exists now": rmsnorm
+// is a fixed-order fp32 glue kernel, and its first byte-gate run found the
+// cross-lane total reaching only some lanes).  One wave per row: the sum of
+// squares in the router's fixed order (lane l: fused multiply-adds over
+// k = 256 i + 4 l + c, then the xor rounds, after which every lane holds the
+// total), ms = ss / H, inv = 1 / sqrt(ms + eps) (correctly rounded division
+// and square root), xn = bf16((x * inv) * gamma).
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ gamma, float eps,
+                                                     int T, int H, uint16_t* __restrict__ xn) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const uint16_t* xr = x + (size_t)t * H;
+    const int nI = H / 256;
+    float p = 0.0f;
+    for (int i = 0; i < nI; ++i) {
+        const uint2 u = *reinterpret_cast<const uint2*>(xr + 256 * i + 4 * lane);
+        const float v0 = bf16_lo(u.x), v1 = bf16_hi(u.x), v2 = bf16_lo(u.y), v3 = bf16_hi(u.y);
+        p = __builtin_fmaf(v0, v0, p);
+        p = __builtin_fmaf(v1, v1, p);
+        p = __builtin_fmaf(v2, v2, p);
+        p = __builtin_fmaf(v3, v3, p);
+    }
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) p = p + __shfl_xor(p, s, 64);
+    const float ms = p / (float)H;
+    const float inv = 1.0f / __builtin_sqrtf(ms + eps);
+    uint16_t* out = xn + (size_t)t * H;
+    for (int i = 0; i < nI; ++i) {
+        const int c = 256 * i + 4 * lane;
+        const uint2 u = *reinterpret_cast<const uint2*>(xr + c);
+        const uint2 g = *reinterpret_cast<const uint2*>(gamma + c);
+        const float v0 = (bf16_lo(u.x) * inv) * bf16_lo(g.x);
+        const float v1 = (bf16_hi(u.x) * inv) * bf16_hi(g.x);
+        const float v2 = (bf16_lo(u.y) * inv) * bf16_lo(g.y);
+        const float v3 = (bf16_hi(u.y) * inv) * bf16_hi(g.y);
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+        o.y = (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
+        *reinterpret_cast<uint2*>(out + c) = o;
+    }
+}
+
+void launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int T, int H, uint16_t* xn,
+                    hipStream_t st) {
+    rmsnorm_kernel<<<(T + 3) / 4, 256, 0, st>>>(x, gamma, eps, T, H, xn);
+}
+
 void launch_router_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H,
                           int E, float* logits, hipStream_t st) {
     // Up to 64 rows: one wave per block, so the E (or a few times E) waves
