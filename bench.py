@@ -164,7 +164,7 @@ def roofline_for(w, counts, stage_ms):
     return out
 
 
-def cpu_baseline(w, d, ex, rows_budget, min_seconds=10.0):
+def cpu_baseline(w, d, ex, rows_budget, min_seconds=10.0, modes=None):
     """The oracle, as it stands, on a bounded sample of rows of the workload."""
     import torch
 
@@ -187,7 +187,8 @@ def cpu_baseline(w, d, ex, rows_budget, min_seconds=10.0):
     # the sample is run again until about min_seconds of host time are spent
     reps, t0 = 0, time.perf_counter()
     while True:
-        orc.moe_ffn(inputs, w.E, w.I, w.Is, w.band_lo, w.band_hi, w.topk, rows=rows_t, experts=ex_o)
+        orc.moe_ffn(inputs, w.E, w.I, w.Is, w.band_lo, w.band_hi, w.topk, rows=rows_t, experts=ex_o,
+                    **(modes or {}))
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -213,6 +214,11 @@ def main():
     ap.add_argument("--reduce-parts", type=int, default=0, metavar="N",
                     help="also time moe_ffn_reduce adding N band partials of the output along "
                          "the tree (N a power of two dividing E)")
+    ap.add_argument("--router", choices=["softmax", "sigmoid"], default="softmax",
+                    help="softmax router (bias on the logits) or sigmoid + selection bias")
+    ap.add_argument("--norm", action="store_true",
+                    help="RMSNorm the rows before routing (weight ~ 1 + N(0, 0.05), eps 1e-5) "
+                         "and add the raw rows after the combine")
     ap.add_argument("--tp", type=int, default=1, metavar="N",
                     help="time one tensor-parallel rank's share: the experts' intermediate "
                          "columns split over N ranks (whole units, remainder on the lowest ranks)")
@@ -266,6 +272,12 @@ def main():
     torch.cuda.synchronize()
     print(f"inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
+    gamma = None
+    if args.norm:
+        gg = torch.Generator().manual_seed(1000 * 0 + 7)
+        gamma = (1.0 + 0.05 * torch.randn(w.H, generator=gg)).to(torch.bfloat16).to(dev)
+    opts = dict(combine=args.combine, router=args.router, norm=gamma, residual=args.norm)
+
     hip = Hip()
     stream = torch.cuda.current_stream(dev)
     out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
@@ -285,7 +297,7 @@ def main():
         evict()
         moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
                     w.band_hi, w.topk, out=out, workspace=ws, events=events, exports=exports,
-                    combine=args.combine)
+                    **opts)
 
     step(exports=ex)  # also exports the routing, for the roofline bookkeeping
     for _ in range(args.warmup):
@@ -301,7 +313,7 @@ def main():
         evict()
         starts[i].record(stream)
         moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
-                    w.band_hi, w.topk, out=out, workspace=ws, combine=args.combine)
+                    w.band_hi, w.topk, out=out, workspace=ws, **opts)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -363,7 +375,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "topk": w.topk, "I": w.I,
                    "Is": w.Is, "fmt": w.fmt, "band": [w.band_lo, w.band_hi],
-                   "combine": args.combine, "tp": tp_info,
+                   "combine": args.combine, "tp": tp_info, "router": args.router,
+                   "norm": "rmsnorm eps 1e-5 + residual" if args.norm else None,
                    "l2_mall_eviction": {"read": "1 GiB read", "write": "1 GiB write",
                                         "none": None}[args.flush]},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
@@ -372,7 +385,10 @@ def main():
     if reduce_info is not None:
         line["reduce"] = reduce_info
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, d, ex, args.cpu_rows)
+        line["cpu_baseline"] = cpu_baseline(
+            w, d, ex, args.cpu_rows,
+            modes=dict(combine=args.combine, router=args.router,
+                       norm=None if gamma is None else gamma.cpu(), residual=args.norm))
     print(json.dumps(line), flush=True)
 
 

@@ -84,55 +84,62 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 }
 __device__ __forceinline__ float4 norm4(float4 a) { return add4(a, make_float4(0.f, 0.f, 0.f, 0.f)); }
 
-// One block per (row, 1024 columns).  Thread 0 builds the row's program:
-// the in-band picks sorted by expert id and, before leaf i is taken, the
-// levels whose waiting entries merge with the running value (ascending), the
-// operands to normalise there, and the level where the running value then
-// waits; entry m holds the final merges.
+// One block per (row, column slice).  The first wave loads the row's picks (a lane each),
+// ranks the in-band ones by expert id with shuffles (ids in a row are
+// distinct) and stores them sorted; thread 0 then builds the row's program:
+// before leaf i is taken, the levels whose waiting entries merge with the
+// running value (ascending), the operands to normalise there, and the level
+// where the running value then waits; entry m holds the final merges.  Every
+// thread then runs the program on its columns, four at a time.
 __global__ __launch_bounds__(256) void combine_tree_kernel(const float* __restrict__ y_r,
                                                           const float* __restrict__ y_s,
                                                           const uint16_t* __restrict__ res,
                                                           const int32_t* __restrict__ ids,
                                                           const int32_t* __restrict__ pos,
                                                           const float* __restrict__ w, int H, int k,
-                                                          int ctiles, int node_level,
+                                                          int nsplit, int node_level,
                                                           float* __restrict__ out) {
-    __shared__ int s_p[16];
+    __shared__ int s_e[16], s_p[16];
     __shared__ float s_w[16];
     __shared__ uint32_t s_mask[17], s_nl[17], s_nr[17];
     __shared__ int s_push[17];
     __shared__ int s_m, s_rootnorm;
-    const int t = blockIdx.x / ctiles;
-    if (threadIdx.x == 0) {
-        int e_[16], p_[16];
-        float w_[16];
-        int m = 0;
-        for (int j = 0; j < k; ++j) {
-            const int p = pos[(size_t)t * k + j];
-            if (p < 0) continue;
-            const int e = ids[(size_t)t * k + j];
-            const float wj = w[(size_t)t * k + j];
-            int q = m++;
-            while (q > 0 && e_[q - 1] > e) {
-                e_[q] = e_[q - 1];
-                p_[q] = p_[q - 1];
-                w_[q] = w_[q - 1];
-                --q;
+    const int t = blockIdx.x / nsplit;
+    const int slice = blockIdx.x - t * nsplit;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int e = 0x7fffffff, p = -1;
+        float wj = 0.0f;
+        if (lane < k) {
+            p = pos[(size_t)t * k + lane];
+            if (p >= 0) {
+                e = ids[(size_t)t * k + lane];
+                wj = w[(size_t)t * k + lane];
             }
-            e_[q] = e;
-            p_[q] = p;
-            w_[q] = wj;
         }
-        uint32_t occ = 0;  // levels holding a waiting entry
+        int rank = 0, m = 0;
+        for (int i = 0; i < k; ++i) {
+            const int ei = __shfl(e, i, 64);
+            if (ei != 0x7fffffff) {
+                ++m;
+                if (ei < e) ++rank;
+            }
+        }
+        if (lane < k && p >= 0) {
+            s_e[rank] = e;
+            s_p[rank] = p;
+            s_w[rank] = wj;
+        }
+        if (lane == 0) s_m = m;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int m = s_m;
+        uint32_t occ = 0;     // levels holding a waiting entry
         int tl[kTreeLevels];  // level of the top node of each waiting entry
         int tlc = 0;          // level of the top node of the running value
-        for (int i = 0; i <= m; ++i) {
-            if (i < m) {
-                s_p[i] = p_[i];
-                s_w[i] = w_[i];
-            }
-            if (i == 0) continue;
-            const int c = i < m ? 32 - __clz(e_[i - 1] ^ e_[i]) : kTreeLevels;
+        for (int i = 1; i <= m; ++i) {
+            const int c = i < m ? 32 - __clz(s_e[i - 1] ^ s_e[i]) : kTreeLevels;
             const uint32_t mask = occ & ((1u << c) - 1u);
             uint32_t nl = 0, nr = 0;
             for (int lev = 1; lev < kTreeLevels; ++lev) {
@@ -152,56 +159,62 @@ __global__ __launch_bounds__(256) void combine_tree_kernel(const float* __restri
                 tlc = 0;
             }
         }
-        s_m = m;
         s_rootnorm = (m > 0 && tlc < node_level) ? 1 : 0;
     }
     __syncthreads();
-    const int c = ((blockIdx.x - t * ctiles) * 256 + threadIdx.x) * 4;
-    if (c >= H) return;
     const int m = __builtin_amdgcn_readfirstlane(s_m);
-    float4 cur = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 pend[kTreeLevels];
+    const int rootnorm = __builtin_amdgcn_readfirstlane(s_rootnorm);
+    // the slice's columns: 1024-column steps slice, slice + nsplit, ...
+    for (int c = 1024 * slice + 4 * threadIdx.x; c < H; c += 1024 * nsplit) {
+        float4 cur = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 pend[kTreeLevels];
 #pragma unroll
-    for (int lev = 0; lev < kTreeLevels; ++lev) pend[lev] = cur;
-    for (int i = 0; i <= m; ++i) {
-        if (i > 0) {
-            const uint32_t mask = __builtin_amdgcn_readfirstlane(s_mask[i]);
-            const uint32_t nl = __builtin_amdgcn_readfirstlane(s_nl[i]);
-            const uint32_t nr = __builtin_amdgcn_readfirstlane(s_nr[i]);
-            const int push = __builtin_amdgcn_readfirstlane(s_push[i]);
+        for (int lev = 0; lev < kTreeLevels; ++lev) pend[lev] = cur;
+        for (int i = 0; i <= m; ++i) {
+            if (i > 0) {
+                const uint32_t mask = __builtin_amdgcn_readfirstlane(s_mask[i]);
+                const uint32_t nl = __builtin_amdgcn_readfirstlane(s_nl[i]);
+                const uint32_t nr = __builtin_amdgcn_readfirstlane(s_nr[i]);
+                const int push = __builtin_amdgcn_readfirstlane(s_push[i]);
 #pragma unroll
-            for (int lev = 1; lev < kTreeLevels; ++lev) {
-                if (mask >> lev & 1u) {
-                    float4 l = pend[lev], r = cur;
-                    if (nl >> lev & 1u) l = norm4(l);
-                    if (nr >> lev & 1u) r = norm4(r);
-                    cur = add4(l, r);
+                for (int lev = 1; lev < kTreeLevels; ++lev) {
+                    if (mask >> lev & 1u) {
+                        float4 l = pend[lev], r = cur;
+                        if (nl >> lev & 1u) l = norm4(l);
+                        if (nr >> lev & 1u) r = norm4(r);
+                        cur = add4(l, r);
+                    }
+                }
+                if (i < m) {
+#pragma unroll
+                    for (int lev = 1; lev < kTreeLevels; ++lev)
+                        if (lev == push) pend[lev] = cur;
                 }
             }
             if (i < m) {
-#pragma unroll
-                for (int lev = 1; lev < kTreeLevels; ++lev)
-                    if (lev == push) pend[lev] = cur;
+                const int p = __builtin_amdgcn_readfirstlane(s_p[i]);
+                const float wi = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_w[i])));
+                const float4 v = *reinterpret_cast<const float4*>(y_r + (size_t)p * H + c);
+                cur = make_float4(wi * v.x, wi * v.y, wi * v.z, wi * v.w);
             }
         }
-        if (i < m) {
-            const int p = __builtin_amdgcn_readfirstlane(s_p[i]);
-            const float wi = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_w[i])));
-            const float4 v = *reinterpret_cast<const float4*>(y_r + (size_t)p * H + c);
-            cur = make_float4(wi * v.x, wi * v.y, wi * v.z, wi * v.w);
-        }
+        if (rootnorm) cur = norm4(cur);
+        if (y_s) cur = add4(cur, *reinterpret_cast<const float4*>(y_s + (size_t)t * H + c));
+        if (res) cur = add_res(cur, res + (size_t)t * H + c);
+        *reinterpret_cast<float4*>(out + (size_t)t * H + c) = cur;
     }
-    if (__builtin_amdgcn_readfirstlane(s_rootnorm)) cur = norm4(cur);
-    if (y_s) cur = add4(cur, *reinterpret_cast<const float4*>(y_s + (size_t)t * H + c));
-    if (res) cur = add_res(cur, res + (size_t)t * H + c);
-    *reinterpret_cast<float4*>(out + (size_t)t * H + c) = cur;
 }
 
 void launch_combine_tree(const float* y_r, const float* y_s, const uint16_t* res, const int32_t* ids,
                          const int32_t* pos, const float* w, int T, int H, int k, int node_level,
                          float* out, hipStream_t st) {
-    const int ctiles = (H / 4 + 255) / 256;
-    combine_tree_kernel<<<T * ctiles, 256, 0, st>>>(y_r, y_s, res, ids, pos, w, H, k, ctiles,
+    // small batches split each row over several blocks so the grid fills the chip
+    const int steps = (H + 1023) / 1024;
+    int nsplit = (2048 + T - 1) / T;
+    if (nsplit > steps) nsplit = steps;
+    if (nsplit < 1) nsplit = 1;
+    combine_tree_kernel<<<T * nsplit, 256, 0, st>>>(y_r, y_s, res, ids, pos, w, H, k, nsplit,
                                                     node_level, out);
 }
 

@@ -124,6 +124,26 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 // k = 256 i + 4 l + c, then the xor rounds, after which every lane holds the
 // total), ms = ss / H, inv = 1 / sqrt(ms + eps) (correctly rounded division
 // and square root), xn = bf16((x * inv) * gamma).
+__device__ __forceinline__ uint2 rms_scale4(uint2 u, uint2 g, float inv) {
+    const float v0 = (bf16_lo(u.x) * inv) * bf16_lo(g.x);
+    const float v1 = (bf16_hi(u.x) * inv) * bf16_hi(g.x);
+    const float v2 = (bf16_lo(u.y) * inv) * bf16_lo(g.y);
+    const float v3 = (bf16_hi(u.y) * inv) * bf16_hi(g.y);
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+    o.y = (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
+    return o;
+}
+
+__device__ __forceinline__ float rms_inv(float ss, int H, float eps) {
+    const float ms = ss / (float)H;
+    return 1.0f / __builtin_sqrtf(ms + eps);
+}
+
+// Rows of up to kRmsRegSteps * 256 values stay in registers: every load of
+// the row and of the weight is issued at once (one memory round trip).
+constexpr int kRmsRegSteps = 32;
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ gamma, float eps,
                                                      int T, int H, uint16_t* __restrict__ xn) {
@@ -131,33 +151,66 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const uint16_t* xr = x + (size_t)t * H;
+    uint16_t* out = xn + (size_t)t * H;
     const int nI = H / 256;
     float p = 0.0f;
-    for (int i = 0; i < nI; ++i) {
-        const uint2 u = *reinterpret_cast<const uint2*>(xr + 256 * i + 4 * lane);
-        const float v0 = bf16_lo(u.x), v1 = bf16_hi(u.x), v2 = bf16_lo(u.y), v3 = bf16_hi(u.y);
-        p = __builtin_fmaf(v0, v0, p);
-        p = __builtin_fmaf(v1, v1, p);
-        p = __builtin_fmaf(v2, v2, p);
-        p = __builtin_fmaf(v3, v3, p);
+    if (nI <= kRmsRegSteps) {
+        // static indices (guarded, no early exit) keep the arrays in registers
+        uint2 u[kRmsRegSteps], g[kRmsRegSteps];
+#pragma unroll
+        for (int i = 0; i < kRmsRegSteps; ++i) {
+            u[i] = make_uint2(0u, 0u);
+            g[i] = make_uint2(0u, 0u);
+            if (i < nI) {
+                u[i] = *reinterpret_cast<const uint2*>(xr + 256 * i + 4 * lane);
+                g[i] = *reinterpret_cast<const uint2*>(gamma + 256 * i + 4 * lane);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kRmsRegSteps; ++i) {
+            if (i < nI) {
+                const float v0 = bf16_lo(u[i].x), v1 = bf16_hi(u[i].x), v2 = bf16_lo(u[i].y),
+                            v3 = bf16_hi(u[i].y);
+                p = __builtin_fmaf(v0, v0, p);
+                p = __builtin_fmaf(v1, v1, p);
+                p = __builtin_fmaf(v2, v2, p);
+                p = __builtin_fmaf(v3, v3, p);
+            }
+        }
+#pragma unroll
+        for (int s = 1; s < 64; s <<= 1) p = p + __shfl_xor(p, s, 64);
+        const float inv = rms_inv(p, H, eps);
+#pragma unroll
+        for (int i = 0; i < kRmsRegSteps; ++i)
+            if (i < nI) *reinterpret_cast<uint2*>(out + 256 * i + 4 * lane) = rms_scale4(u[i], g[i], inv);
+        return;
+    }
+    // longer rows: two passes, loads of 8 steps issued together
+    constexpr int B = 8;
+    for (int i0 = 0; i0 < nI; i0 += B) {
+        uint2 u[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+            u[b] = i0 + b < nI ? *reinterpret_cast<const uint2*>(xr + 256 * (i0 + b) + 4 * lane)
+                               : make_uint2(0u, 0u);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (i0 + b >= nI) break;
+            const float v0 = bf16_lo(u[b].x), v1 = bf16_hi(u[b].x), v2 = bf16_lo(u[b].y),
+                        v3 = bf16_hi(u[b].y);
+            p = __builtin_fmaf(v0, v0, p);
+            p = __builtin_fmaf(v1, v1, p);
+            p = __builtin_fmaf(v2, v2, p);
+            p = __builtin_fmaf(v3, v3, p);
+        }
     }
 #pragma unroll
     for (int s = 1; s < 64; s <<= 1) p = p + __shfl_xor(p, s, 64);
-    const float ms = p / (float)H;
-    const float inv = 1.0f / __builtin_sqrtf(ms + eps);
-    uint16_t* out = xn + (size_t)t * H;
+    const float inv = rms_inv(p, H, eps);
     for (int i = 0; i < nI; ++i) {
         const int c = 256 * i + 4 * lane;
-        const uint2 u = *reinterpret_cast<const uint2*>(xr + c);
-        const uint2 g = *reinterpret_cast<const uint2*>(gamma + c);
-        const float v0 = (bf16_lo(u.x) * inv) * bf16_lo(g.x);
-        const float v1 = (bf16_hi(u.x) * inv) * bf16_hi(g.x);
-        const float v2 = (bf16_lo(u.y) * inv) * bf16_lo(g.y);
-        const float v3 = (bf16_hi(u.y) * inv) * bf16_hi(g.y);
-        uint2 o;
-        o.x = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
-        o.y = (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
-        *reinterpret_cast<uint2*>(out + c) = o;
+        *reinterpret_cast<uint2*>(out + c) = rms_scale4(*reinterpret_cast<const uint2*>(xr + c),
+                                                        *reinterpret_cast<const uint2*>(gamma + c), inv);
     }
 }
 
