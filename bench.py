@@ -58,7 +58,7 @@ class Hip:
         return float(ms.value)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_prefill.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_moe_kernels_all_workloads.txt")
 KERNEL_SOURCES = {
     "gemv": ["mixture_experts_ffn_06_amd/csrc/gemv.hip", "mixture_experts_ffn_06_amd/csrc/common.h"],
     "pipe": ["mixture_experts_ffn_06_amd/csrc/mfma_pipe.hip", "mixture_experts_ffn_06_amd/csrc/common.h"],
@@ -133,10 +133,16 @@ def roofline_for(w, counts, stage_ms):
         kernel = ("expert_mfma_pipe_kernel<true,256|128|64|32>" if w.fmt == "bf16"
                   else "expert_mfma_w4_kernel<true,128|64|32> + shared expert_mfma_pipe_kernel")
         ms = stage_ms["gu_mfma"]
-        traffic = None
         if w.fmt == "bf16":
             traffic = measured_traffic(
                 w.name, [f"moe::expert_mfma_pipe_kernel<true,{bm}>" for bm in (256, 128, 64, 32)])
+        else:
+            # the 4-bit launches, plus the one bf16 launch that holds the shared
+            # expert's rows (its tile height follows T)
+            sh_bm = 256 if w.T > 128 else 128 if w.T > 64 else 64 if w.T > 32 else 32
+            traffic = measured_traffic(
+                w.name, [f"moe::expert_mfma_w4_kernel<true,{bm}>" for bm in (128, 64, 32)]
+                + [f"moe::expert_mfma_pipe_kernel<true,{sh_bm}>"])
         # rows on the GEMV path (groups of 1..8 rows) are not in this launch
         small = counts[(counts > 0) & (counts <= 8)]
         n_touched -= int(small.numel())
