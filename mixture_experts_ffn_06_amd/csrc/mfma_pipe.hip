@@ -23,6 +23,8 @@
 // by the group's other row tiles.
 #include "common.h"
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
@@ -197,6 +199,10 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
     for (int s = 0; s < C::S - 1; ++s)
         if (s < KT) issue(s);
 
+    // The step loop, compiled twice: with every 16-row subtile of this wave
+    // live (no branches: the compiler schedules the LDS reads among the
+    // MFMAs) and with the per-subtile checks of a partial last tile.
+    auto steps = [&](auto all_live) {
     for (int kt = 0; kt < KT; ++kt) {
         // Stage kt is complete once at most (stages issued after it) x L of
         // this wave's loads are still in flight.
@@ -218,7 +224,7 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         // (wave-uniform: a partial last tile of a large group)
         bool live[C::MT];
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i) live[i] = wm * (BM / C::WM) + 16 * i < rows;
+        for (int i = 0; i < C::MT; ++i) live[i] = decltype(all_live)::value || wm * (BM / C::WM) + 16 * i < rows;
         // the operand reads of both halves of the step first, then their
         // MFMAs (one half at a time for the 128 x 64 wave tile: registers)
         constexpr int KH = C::MT + C::NT <= 8 ? 2 : 1;
@@ -246,6 +252,11 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
                     }
         }
     }
+    };
+    if (wm * (BM / C::WM) + 16 * (C::MT - 1) < rows)
+        steps(std::true_type{});
+    else
+        steps(std::false_type{});
 
     // Epilogue.  Lane holds D[4 (lane >> 4) + v][lane & 15] of each 16x16 subtile.
     if (GATEUP) {
