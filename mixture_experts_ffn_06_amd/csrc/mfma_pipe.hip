@@ -54,8 +54,14 @@ struct PipeCfg {
     static constexpr int LB = BN / 8 / NW;                        // B loads per wave per stage
     static constexpr int L = LA + LB;                             // all loads per wave per stage
     static constexpr int ATile = BM * kBK * 2;
-    static constexpr int Stage = ATile + BN * kBK * 2;
-    static constexpr int Lds = S * Stage;
+    static constexpr int BTile = BN * kBK * 2;
+    static constexpr int Stage = ATile + BTile;
+    // 128 x 128: separate rings, A two slots deep and B (the weights, read
+    // from HBM) three, so B is issued two steps ahead within 80 KiB
+    static constexpr bool Split = BM == 128;
+    static constexpr int SA = Split ? 2 : S;
+    static constexpr int SB = Split ? 3 : S;
+    static constexpr int Lds = Split ? SA * ATile + SB * BTile : S * Stage;
     static constexpr int PerCU = Lds <= 80 * 1024 ? 2 : 1;
     static constexpr int Threads = 64 * NW;
     static_assert(ALoads % NW == 0, "A loads per wave");
@@ -149,16 +155,32 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         bsrc[j] = wbase + (size_t)brow * K + 8 * c;
     }
 
-    auto issue = [&](int kt) {
-        lds_u8* st = smem + (kt % C::S) * C::Stage;
+    // A and B slots of step kt: one ring of [A | B] stages, or (Split) an A
+    // ring followed by a B ring
+    auto a_slot = [&](int kt) -> lds_u8* {
+        return C::Split ? smem + (kt % C::SA) * C::ATile : smem + (kt % C::S) * C::Stage;
+    };
+    auto b_slot = [&](int kt) -> lds_u8* {
+        return C::Split ? smem + C::SA * C::ATile + (kt % C::SB) * C::BTile
+                        : smem + (kt % C::S) * C::Stage + C::ATile;
+    };
+    auto issue_a = [&](int kt) {
+        lds_u8* st = a_slot(kt);
         const int k0 = kt * kBK;
 #pragma unroll
         for (int j = 0; j < C::LA; ++j)
             __builtin_amdgcn_global_load_lds(asrc[j] + k0, st + (wave + C::NW * j) * 1024, 16, 0, 0);
+    };
+    auto issue_b = [&](int kt) {
+        lds_u8* st = b_slot(kt);
+        const int k0 = kt * kBK;
 #pragma unroll
         for (int j = 0; j < C::LB; ++j)
-            __builtin_amdgcn_global_load_lds(bsrc[j] + k0, st + C::ATile + (wave + C::NW * j) * 1024,
-                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(bsrc[j] + k0, st + (wave + C::NW * j) * 1024, 16, 0, 0);
+    };
+    auto issue = [&](int kt) {
+        issue_a(kt);
+        issue_b(kt);
     };
 
     f32x4_p acc[C::MT][C::NT];
@@ -187,7 +209,7 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
             rb = wn * (C::BN / C::WN) + 16 * j;
         }
         rb += lane & 15;
-        boff[j] = C::ATile + rb * 128;
+        boff[j] = rb * 128;
         bx[j] = rb & 7;
     }
 
@@ -195,31 +217,52 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
     // wait for every load in flight and undo the pipeline.  LDS reads are
     // complete before the barrier because the MFMAs consumed them.
     __builtin_amdgcn_s_barrier();  // every wave is done with the previous tile's stages
+    if (C::Split) {
+        // issue order A_0, B_0, B_1, then per step kt: A_{kt+1}, B_{kt+2}
+        if (KT > 0) issue(0);
+        if (KT > 1) issue_b(1);
+    } else {
 #pragma unroll
-    for (int s = 0; s < C::S - 1; ++s)
-        if (s < KT) issue(s);
+        for (int s = 0; s < C::S - 1; ++s)
+            if (s < KT) issue(s);
+    }
 
     // The step loop, compiled twice: with every 16-row subtile of this wave
     // live (no branches: the compiler schedules the LDS reads among the
     // MFMAs) and with the per-subtile checks of a partial last tile.
     auto steps = [&](auto all_live) {
     for (int kt = 0; kt < KT; ++kt) {
-        // Stage kt is complete once at most (stages issued after it) x L of
-        // this wave's loads are still in flight.
-        const int after = min(C::S - 2, KT - 1 - kt);
-        if (after >= 4)
-            wait_vmcnt<4 * C::L>();
-        else if (after == 3)
-            wait_vmcnt<3 * C::L>();
-        else if (after == 2)
-            wait_vmcnt<2 * C::L>();
-        else if (after == 1)
-            wait_vmcnt<C::L>();
-        else
-            wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();  // stage kt visible to all waves; stage kt-1 free
-        if (kt + C::S - 1 < KT) issue(kt + C::S - 1);
-        const lds_u8* st = smem + (kt % C::S) * C::Stage;
+        if (C::Split) {
+            // loads return in issue order: A_kt and B_kt have landed once at
+            // most the loads of B_{kt+1} (issued after A_kt) are in flight
+            if (kt + 1 < KT)
+                wait_vmcnt<C::LB>();
+            else
+                wait_vmcnt<0>();
+        } else {
+            // Stage kt is complete once at most (stages issued after it) x L
+            // of this wave's loads are still in flight.
+            const int after = min(C::S - 2, KT - 1 - kt);
+            if (after >= 4)
+                wait_vmcnt<4 * C::L>();
+            else if (after == 3)
+                wait_vmcnt<3 * C::L>();
+            else if (after == 2)
+                wait_vmcnt<2 * C::L>();
+            else if (after == 1)
+                wait_vmcnt<C::L>();
+            else
+                wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();  // step kt visible to all waves; step kt-1's slots free
+        if (C::Split) {
+            if (kt + 1 < KT) issue_a(kt + 1);
+            if (kt + 2 < KT) issue_b(kt + 2);
+        } else if (kt + C::S - 1 < KT) {
+            issue(kt + C::S - 1);
+        }
+        const lds_u8* sa = a_slot(kt);
+        const lds_u8* sb = b_slot(kt);
         // 16-row subtiles wholly past the group's rows do no MFMA work
         // (wave-uniform: a partial last tile of a large group)
         bool live[C::MT];
@@ -236,9 +279,9 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
                 const int q = (k0 + kh) * 4 + (lane >> 4);  // logical 16-byte chunk of the operand
 #pragma unroll
                 for (int i = 0; i < C::MT; ++i)
-                    if (live[i]) af[kh][i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
+                    if (live[i]) af[kh][i] = *(lds_bf16x8*)(sa + aoff[i] + ((q ^ ax[i]) << 4));
 #pragma unroll
-                for (int j = 0; j < C::NT; ++j) bfr[kh][j] = *(lds_bf16x8*)(st + boff[j] + ((q ^ bx[j]) << 4));
+                for (int j = 0; j < C::NT; ++j) bfr[kh][j] = *(lds_bf16x8*)(sb + boff[j] + ((q ^ bx[j]) << 4));
             }
 #pragma unroll
             for (int kh = 0; kh < KH; ++kh)
