@@ -270,6 +270,55 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
         for (int i = 0; i < C::MT; ++i) live[i] = decltype(all_live)::value || wm * (BM / C::WM) + 16 * i < rows;
         // the operand reads of both halves of the step first, then their
         // MFMAs (one half at a time for the 128 x 64 wave tile: registers)
+        if constexpr (decltype(all_live)::value && BM == 256) {
+            // Every subtile live: the step's MFMAs in groups of two 16-row
+            // subtiles x all column subtiles, each group's A fragments (and a
+            // new 32-deep half's B fragments) read from LDS while the
+            // previous group's MFMAs run (two register sets each).
+            constexpr int KS = kBK / 32, NP = C::MT / 2, NG = KS * NP;
+            bf16x8_p ga[2][2], gb[2][C::NT];
+            auto read_a = [&](int g, bf16x8_p* dst) {
+                const int q = (g / NP) * 4 + (lane >> 4);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int i = 2 * (g % NP) + m;
+                    dst[m] = *(lds_bf16x8*)(sa + aoff[i] + ((q ^ ax[i]) << 4));
+                }
+            };
+            auto read_b = [&](int h, bf16x8_p* dst) {
+                const int q = h * 4 + (lane >> 4);
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) dst[j] = *(lds_bf16x8*)(sb + boff[j] + ((q ^ bx[j]) << 4));
+            };
+            read_b(0, gb[0]);
+            read_a(0, ga[0]);
+            // the scheduler keeps this order: each group's LDS reads ahead of
+            // the previous group's MFMAs (sched_group_barrier masks: 0x100 LDS
+            // reads, 0x8 MFMA)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 + C::NT, 0);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                if (g + 1 < NG) {
+                    read_a(g + 1, ga[(g + 1) & 1]);
+                    if ((g + 1) % NP == 0) {
+                        read_b((g + 1) / NP, gb[((g + 1) / NP) & 1]);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2 + C::NT, 0);
+                    } else {
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int i = 2 * (g % NP) + m;
+#pragma unroll
+                    for (int j = 0; j < C::NT; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga[g & 1][m], gb[(g / NP) & 1][j],
+                                                                            acc[i][j], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x8, 2 * C::NT, 0);
+            }
+            continue;
+        }
         constexpr int KH = C::MT + C::NT <= 8 ? 2 : 1;
 #pragma unroll
         for (int k0 = 0; k0 < kBK / 32; k0 += KH) {
