@@ -385,49 +385,35 @@ __device__ void pipe_tile(const ExpertArgs& a, lds_u8* smem, const Group& g, int
     }
 }
 
+// The 256-row list.  A large group has several 256-row tiles: column tile nt
+// of all of them runs on XCD nt mod 8 (NT and the grid are multiples of 8 at
+// the usual widths), whose L2 then serves the shared weight rows.  Every tile
+// gets the same number of column tiles (the larger of the routed and shared
+// widths); items past a group's width are skipped.
 template <bool GATEUP, int BM>
 __global__ __launch_bounds__(PipeCfg<BM>::Threads) void expert_mfma_pipe_kernel(ExpertArgs a) {
+    static_assert(BM == 256, "the 128-, 64- and 32-row lists run in expert_mfma_small_kernel");
     using C = PipeCfg<BM>;
     using CN = PipeCfg<BM, 128>;  // 256 x 128 items when 256 x 256 ones are too few
     constexpr int kLds = C::Lds > CN::Lds ? C::Lds : CN::Lds;
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kLds];
     lds_u8* smem = (lds_u8*)smem_raw;
-    constexpr int list = BM == 256 ? 3 : (BM == 128 ? 0 : (BM == 64 ? 1 : 2));
-    const int ntiles = a.plan_counts[1 + list];
-    const int32_t* tl = a.mfma_list + 2 * (size_t)list * a.mfma_cap;
-    if (BM == 256) {
-        // A large group has several 256-row tiles: column tile nt of all of
-        // them runs on XCD nt mod 8 (NT and the grid are multiples of 8 at
-        // the usual widths), whose L2 then serves the shared weight rows.
-        // Every tile gets the same number of column tiles (the larger of the
-        // routed and shared widths); items past a group's width are skipped.
-        const bool narrow = (long long)ntiles * C::col_tiles(GATEUP, a.I > a.Is ? a.I : a.Is, a.H) < gridDim.x;
-        const int NTr = narrow ? CN::col_tiles(GATEUP, a.I, a.H) : C::col_tiles(GATEUP, a.I, a.H);
-        const int NTs = narrow ? CN::col_tiles(GATEUP, a.Is, a.H) : C::col_tiles(GATEUP, a.Is, a.H);
-        const int NT = NTr > NTs ? NTr : NTs;
-        const int total = ntiles * NT;
-        for (int item = blockIdx.x; item < total; item += gridDim.x) {
-            const int tile = item / NT, nt = item % NT;
-            const Group g = a.groups[tl[2 * tile]];
-            if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
-            if (a.fmt != 0 && g.expert >= 0) continue;  // 4-bit experts: expert_mfma_w4_kernel
-            if (narrow)
-                pipe_tile<GATEUP, BM, 128>(a, smem, g, tl[2 * tile + 1], nt);
-            else
-                pipe_tile<GATEUP, BM, C::BN>(a, smem, g, tl[2 * tile + 1], nt);
-        }
-    } else {
-        const int NTr = C::col_tiles(GATEUP, a.I, a.H);
-        const int NTs = C::col_tiles(GATEUP, a.Is, a.H);
-        const int NT = NTr > NTs ? NTr : NTs;
-        XcdWalk w(ntiles, NT);
-        int tile, nt;
-        while (w.next(&tile, &nt)) {
-            const Group g = a.groups[tl[2 * tile]];
-            if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
-            if (a.fmt != 0 && g.expert >= 0) continue;  // 4-bit experts: expert_mfma_w4_kernel
+    const int ntiles = a.plan_counts[4];
+    const int32_t* tl = a.mfma_list + 2 * (size_t)3 * a.mfma_cap;
+    const bool narrow = (long long)ntiles * C::col_tiles(GATEUP, a.I > a.Is ? a.I : a.Is, a.H) < gridDim.x;
+    const int NTr = narrow ? CN::col_tiles(GATEUP, a.I, a.H) : C::col_tiles(GATEUP, a.I, a.H);
+    const int NTs = narrow ? CN::col_tiles(GATEUP, a.Is, a.H) : C::col_tiles(GATEUP, a.Is, a.H);
+    const int NT = NTr > NTs ? NTr : NTs;
+    const int total = ntiles * NT;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int tile = item / NT, nt = item % NT;
+        const Group g = a.groups[tl[2 * tile]];
+        if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
+        if (a.fmt != 0 && g.expert >= 0) continue;  // 4-bit experts: expert_mfma_w4_kernel
+        if (narrow)
+            pipe_tile<GATEUP, BM, 128>(a, smem, g, tl[2 * tile + 1], nt);
+        else
             pipe_tile<GATEUP, BM, C::BN>(a, smem, g, tl[2 * tile + 1], nt);
-        }
     }
 }
 
@@ -442,19 +428,63 @@ static void launch_pipe_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
     expert_mfma_pipe_kernel<GATEUP, BM><<<(int)grid, C::Threads, 0, st>>>(a);
 }
 
+// The 128-, 64- and 32-row lists in one launch: the same block shape (4
+// waves, 128 columns, at most 80 KiB of LDS, two blocks per CU), walked as
+// one list, so the launch has one tail instead of three.
+constexpr int kSmallLds = PipeCfg<128>::Lds > PipeCfg<64>::Lds
+                              ? (PipeCfg<128>::Lds > PipeCfg<32>::Lds ? PipeCfg<128>::Lds : PipeCfg<32>::Lds)
+                              : (PipeCfg<64>::Lds > PipeCfg<32>::Lds ? PipeCfg<64>::Lds : PipeCfg<32>::Lds);
+
+// It is the only caller of the 128-, 64- and 32-row tile functions (the
+// host compilation pass rejects a second kernel calling a specialization of
+// pipe_tile that another kernel already instantiated).
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void expert_mfma_small_kernel(ExpertArgs a) {
+    using C = PipeCfg<128>;  // column tiling (128 columns) is the same for all three
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kSmallLds];
+    lds_u8* smem = (lds_u8*)smem_raw;
+    const int n128 = a.plan_counts[1], n64 = a.plan_counts[2], n32 = a.plan_counts[3];
+    const int NTr = C::col_tiles(GATEUP, a.I, a.H);
+    const int NTs = C::col_tiles(GATEUP, a.Is, a.H);
+    const int NT = NTr > NTs ? NTr : NTs;
+    XcdWalk w(n128 + n64 + n32, NT);
+    int v, nt;
+    while (w.next(&v, &nt)) {
+        const int list = v < n128 ? 0 : (v < n128 + n64 ? 1 : 2);
+        const int tile = v - (list == 0 ? 0 : (list == 1 ? n128 : n128 + n64));
+        const int32_t* tl = a.mfma_list + 2 * (size_t)list * a.mfma_cap;
+        const Group g = a.groups[tl[2 * tile]];
+        if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
+        if (a.fmt != 0 && g.expert >= 0) continue;  // 4-bit experts: expert_mfma_w4_kernel
+        if (list == 0)
+            pipe_tile<GATEUP, 128, 128>(a, smem, g, tl[2 * tile + 1], nt);
+        else if (list == 1)
+            pipe_tile<GATEUP, 64, 128>(a, smem, g, tl[2 * tile + 1], nt);
+        else
+            pipe_tile<GATEUP, 32, 128>(a, smem, g, tl[2 * tile + 1], nt);
+    }
+}
+
+template <bool GATEUP>
+static void launch_small(const ExpertArgs& a, int num_cu, hipStream_t st) {
+    const int NT = PipeCfg<128>::col_tiles(GATEUP, a.I > a.Is ? a.I : a.Is, a.H);
+    long long grid = (long long)num_cu * 2;
+    const long long ub = 3LL * a.mfma_cap * NT;
+    if (ub < grid) grid = ub;
+    grid = grid < 8 ? 8 : grid & ~7LL;  // the XCD walk deals blocks in groups of 8
+    expert_mfma_small_kernel<GATEUP><<<(int)grid, 256, 0, st>>>(a);
+}
+
 void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st) {
     if (gateup) {
         launch_pipe_bm<true, 256>(a, num_cu, st);
-        launch_pipe_bm<true, 128>(a, num_cu, st);
-        launch_pipe_bm<true, 64>(a, num_cu, st);
-        launch_pipe_bm<true, 32>(a, num_cu, st);
+        launch_small<true>(a, num_cu, st);
     } else {
         launch_pipe_bm<false, 256>(a, num_cu, st);
-        launch_pipe_bm<false, 128>(a, num_cu, st);
-        launch_pipe_bm<false, 64>(a, num_cu, st);
-        launch_pipe_bm<false, 32>(a, num_cu, st);
+        launch_small<false>(a, num_cu, st);
     }
 }
+
 
 // ---- 4-bit experts ---------------------------------------------------------
 //
@@ -748,17 +778,15 @@ void launch_mfma_w4(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st
         launch_w4_bm<false, 32>(a, num_cu, st);
     }
     // the bf16 shared expert: one group of T rows, so one tile list (9 <= T
-    // since no MFMA launch runs at T <= 8)
+    // since no MFMA launch runs at T <= 8); the small-list launch walks the
+    // three lists and skips the 4-bit groups
     if (a.Is > 0) {
         if (a.T > 128)
             gateup ? launch_pipe_bm<true, 256>(a, num_cu, st) : launch_pipe_bm<false, 256>(a, num_cu, st);
-        else if (a.T > 64)
-            gateup ? launch_pipe_bm<true, 128>(a, num_cu, st) : launch_pipe_bm<false, 128>(a, num_cu, st);
-        else if (a.T > 32)
-            gateup ? launch_pipe_bm<true, 64>(a, num_cu, st) : launch_pipe_bm<false, 64>(a, num_cu, st);
         else
-            gateup ? launch_pipe_bm<true, 32>(a, num_cu, st) : launch_pipe_bm<false, 32>(a, num_cu, st);
+            gateup ? launch_small<true>(a, num_cu, st) : launch_small<false>(a, num_cu, st);
     }
 }
+
 
 }  // namespace moe
