@@ -405,9 +405,28 @@ __global__ __launch_bounds__(PipeCfg<BM>::Threads) void expert_mfma_pipe_kernel(
     const int NTs = narrow ? CN::col_tiles(GATEUP, a.Is, a.H) : C::col_tiles(GATEUP, a.Is, a.H);
     const int NT = NTr > NTs ? NTr : NTs;
     const int total = ntiles * NT;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
-        const int tile = item / NT, nt = item % NT;
-        const Group g = a.groups[tl[2 * tile]];
+    // Items in rounds of g8 (the blocks of one XCD), round r on XCD r mod 8.
+    // Within a group the items run column chunk by column chunk (kChunk
+    // column tiles wide), all of the group's row tiles per chunk, so the
+    // blocks of a round share a few A tiles and a few weight column tiles in
+    // their XCD's L2.
+    constexpr int kChunk = 4;
+    const int g8 = gridDim.x >> 3, x = blockIdx.x & 7, l = blockIdx.x >> 3;
+    for (int rd = x;; rd += 8) {
+        const int item = rd * g8 + l;
+        if (item >= total) break;
+        // the group of the item: its tiles are consecutive in the list and
+        // own items NT * first tile .. NT * (first tile + tiles) - 1
+        const int t = item / NT;
+        const Group g = a.groups[tl[2 * t]];
+        const int tf = t - tl[2 * t + 1] / 256;
+        const int R = (g.n + 255) / 256;
+        const int j = item - tf * NT;
+        const int cc = j / (R * kChunk);
+        const int c0 = cc * kChunk;
+        const int wd = NT - c0 < kChunk ? NT - c0 : kChunk;
+        const int rem = j - cc * R * kChunk;
+        const int tile = tf + rem / wd, nt = c0 + rem % wd;
         if (nt >= (g.expert < 0 ? NTs : NTr)) continue;
         if (a.fmt != 0 && g.expert >= 0) continue;  // 4-bit experts: expert_mfma_w4_kernel
         if (narrow)
