@@ -48,40 +48,38 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
     }
 }
 
-// Exclusive scans of N values over the 1024 threads of a block at once (fixed
-// order, deterministic): wave scans by shuffles, then wave 0 scans the 16
-// wave totals the same way.  s_tmp holds 17 N ints.
+// Inclusive sum over the lanes of a wave (lane l gets v_0 + .. + v_l): four
+// row shifts sum within each row of 16 lanes, then two row broadcasts carry
+// the row totals (DPP moves: no LDS round trip per step).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// Exclusive scans of N values over the 1024 threads of a block at once
+// (integer sums: the result does not depend on the order): wave scans, then
+// wave 0 scans the 16 wave totals.  s_tmp holds 17 N ints.
 template <int N>
 __device__ void block_exclusive_scan_n(const int (&v)[N], int (&res)[N], int (&total)[N], int* s_tmp) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int inc[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) inc[i] = v[i];
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1)
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int o = __shfl_up(inc[i], d, 64);
-            if (lane >= d) inc[i] += o;
-        }
+    for (int i = 0; i < N; ++i) inc[i] = wave_incl_scan(v[i]);
     if (lane == 63)
 #pragma unroll
         for (int i = 0; i < N; ++i) s_tmp[wave * N + i] = inc[i];
     __syncthreads();
     if (wave == 0) {
-        int w[N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) w[i] = lane < 16 ? s_tmp[lane * N + i] : 0;
-#pragma unroll
-        for (int d = 1; d < 16; d <<= 1)
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int o = __shfl_up(w[i], d, 64);
-                if (lane >= d) w[i] += o;
-            }
-        if (lane < 16)
-#pragma unroll
-            for (int i = 0; i < N; ++i) s_tmp[lane * N + i] = w[i];  // inclusive over waves
+        for (int i = 0; i < N; ++i) {
+            const int w = wave_incl_scan(lane < 16 ? s_tmp[lane * N + i] : 0);
+            if (lane < 16) s_tmp[lane * N + i] = w;  // inclusive over waves
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -248,7 +246,8 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
 
 // All of the dispatch in one block when every row fits in one block of 256
 // rows (decode): masks, counts, scan, plan and placement without a kernel
-// boundary in between.  1024 threads; threads 0..255 own the rows.
+// boundary in between.  1024 threads; threads 0..255 own the rows of the
+// masks, the placement takes one thread per pick.
 __device__ __forceinline__ void dispatch_small_body(
     const int32_t* __restrict__ ids, int T, int k, int lo, int nb, bool has_shared,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
@@ -283,17 +282,16 @@ __device__ __forceinline__ void dispatch_small_body(
     if (tid == 0) offsets[nb] = total;
     build_plan(cnt, run, nb, T, lo, has_shared, groups, gemv_list, mfma_list, mfma_cap,
                plan_counts, s_tmp);  // its scans hold barriers: s_off is visible
-    const int t = tid;
-    if (t >= T) return;
-    const int wave = tid >> 6, lane = tid & 63;
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int j = 0; j < k; ++j) {
-        const int p = t * k + j;
+    // one thread per pick: its slot is the expert's offset + the picks of
+    // earlier rows (earlier waves' masks, then the bits below its row)
+    for (int p = tid; p < T * k; p += blockDim.x) {
+        const int t = p / k;
         const int e = ids[p] - lo;
         if (e >= 0 && e < nb) {
+            const int wave = t >> 6, row = t & 63;
             int slot = s_off[e];
             for (int w = 0; w < wave; ++w) slot += __popcll(masks[w * nb + e]);
-            slot += __popcll(masks[wave * nb + e] & below);
+            slot += __popcll(masks[wave * nb + e] & ((1ull << row) - 1ull));
             perm[slot] = p;
             pos[p] = slot;
         } else {

@@ -18,7 +18,6 @@
 namespace moe {
 
 // One wave computes a tile of RB rows x EB experts.
-// One wave computes a tile of RB rows x EB experts.
 // The loads of BATCH steps of i are issued before any of them is used.
 template <int RB, int EB, int BATCH>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
@@ -222,13 +221,13 @@ void launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int T, 
 void launch_router_logits(const uint16_t* x, const float* wr, const float* bias, int T, int H,
                           int E, float* logits, hipStream_t st) {
     // Up to 64 rows: one wave per block, so the E (or a few times E) waves
-    // spread over every CU; larger batches: four waves per block.
+    // spread over every CU; larger batches: four waves per block.  Up to 8
+    // rows, a wave takes one or two rows and issues all 24 steps' loads of
+    // H = 6144 at once (one memory round trip).
     if (T <= 1) {
-        router_logits_kernel<1, 1, 12><<<E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
-    } else if (T <= 2) {
-        router_logits_kernel<2, 1, 12><<<E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
-    } else if (T <= 4) {
-        router_logits_kernel<4, 1, 8><<<E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
+        router_logits_kernel<1, 1, 24><<<E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
+    } else if (T <= 8) {
+        router_logits_kernel<2, 1, 24><<<((T + 1) / 2) * E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else if (T <= 64) {
         router_logits_kernel<8, 1, 6><<<((T + 7) / 8) * E, 64, 0, st>>>(x, wr, bias, T, H, E, logits);
     } else {

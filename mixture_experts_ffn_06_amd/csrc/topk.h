@@ -12,42 +12,47 @@
 
 namespace moe {
 
-// (value, id) keys: a larger value wins, equal values go to the lower id;
-// id 0x7fffffff marks "nothing left" and always loses.
-__device__ __forceinline__ bool key_better(float v2, int i2, float v1, int i1) {
-    return i2 != 0x7fffffff && (i1 == 0x7fffffff || v2 > v1 || (v2 == v1 && i2 < i1));
+// (value, id) keys: a larger value wins, equal values go to the lower id.
+// Both fit one unsigned 64-bit key: the high word is the value's bits made
+// monotonic (negative values inverted, the sign bit set on the others; -0.0
+// is first turned into +0.0), the low word is ~id.  Values are finite or
+// infinite (the router produces no NaN from finite inputs).  Key 0 is below
+// every real key and marks "nothing left".
+__device__ __forceinline__ uint64_t topk_key(float v, int id) {
+    uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)b << 32) | (uint32_t)~id;
+}
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+    const uint32_t b = (uint32_t)(key >> 32);
+    return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+__device__ __forceinline__ int topk_key_id(uint64_t key) { return (int)~(uint32_t)key; }
+
+// One DPP step of the wave maximum: lanes of the rows in ROWMASK compare
+// with the lane CTRL names; other lanes keep their key.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t key_max_step(uint64_t k) {
+    const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xf, false);
+    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xf, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > k ? o : k;
 }
 
-template <int CTRL>
-__device__ __forceinline__ void key_step(float& v, int& i) {
-    const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-    const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xf, 0xf, false);
-    if (key_better(ov, oi, v, i)) {
-        v = ov;
-        i = oi;
-    }
-}
-
-// Best key of the wave: four DPP steps give every lane its row's best, then
-// the four row winners are combined.  Every lane gets the result.
-__device__ __forceinline__ void wave_best(float& v, int& i) {
-    key_step<0xB1>(v, i);   // quad_perm [1,0,3,2]
-    key_step<0x4E>(v, i);   // quad_perm [2,3,0,1]
-    key_step<0x141>(v, i);  // row_half_mirror
-    key_step<0x140>(v, i);  // row_mirror
-    float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
-        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-        if (key_better(rv, ri, bv, bi)) {
-            bv = rv;
-            bi = ri;
-        }
-    }
-    v = bv;
-    i = bi;
+// Largest key of the wave: four steps give every lane its row's maximum, two
+// row broadcasts carry rows 0-1 into row 3 (the maximum of a total order does
+// not depend on the tree), and lane 63's key goes to every lane.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+    k = key_max_step<0xB1, 0xf>(k);   // quad_perm [1,0,3,2]
+    k = key_max_step<0x4E, 0xf>(k);   // quad_perm [2,3,0,1]
+    k = key_max_step<0x141, 0xf>(k);  // row_half_mirror
+    k = key_max_step<0x140, 0xf>(k);  // row_mirror
+    k = key_max_step<0x142, 0xa>(k);  // row_bcast:15 into rows 1 and 3
+    k = key_max_step<0x143, 0xc>(k);  // row_bcast:31 into rows 2 and 3
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // The sigmoid router's fixed fp32 sigmoid ([P5] "What exists now": GLM's
@@ -92,19 +97,18 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ logits, const
                                          int32_t* __restrict__ ids, float* __restrict__ w, int32_t* sids) {
 #pragma clang fp contract(off)
     const int lane = threadIdx.x & 63;
-    float v[PER], sc[PER];
-    uint32_t taken = 0;
+    float sc[PER];
+    uint64_t key[PER];
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-        int e = lane + 64 * m;
-        v[m] = (e < E) ? logits[(size_t)t * E + e] : -INFINITY;
+        const int e = lane + 64 * m;
+        float v = (e < E) ? logits[(size_t)t * E + e] : 0.0f;
         sc[m] = 0.0f;
         if (sigmoid && e < E) {
-            sc[m] = sigmoid_c(v[m]);
-            float key = bias ? sc[m] + bias[e] : sc[m];
-            v[m] = key == 0.0f ? 0.0f : key;
+            sc[m] = sigmoid_c(v);
+            v = bias ? sc[m] + bias[e] : sc[m];
         }
-        if (e >= E) taken |= 1u << m;
+        key[m] = e < E ? topk_key(v, e) : 0ull;
     }
     float sel_v[16];
     int sel_id[16];
@@ -116,20 +120,16 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ logits, const
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         if (j >= k) break;
-        float bv = -INFINITY;
-        int bid = 0x7fffffff;
+        uint64_t best = key[0];
 #pragma unroll
-        for (int m = 0; m < PER; ++m) {
-            if (taken >> m & 1u) continue;
-            // ids grow with m inside a lane, so a strict compare keeps the lower id on ties
-            if (bid == 0x7fffffff || v[m] > bv) {
-                bv = v[m];
-                bid = lane + 64 * m;
-            }
-        }
-        wave_best(bv, bid);
-        if ((bid & 63) == lane) taken |= 1u << (bid >> 6);
-        sel_v[j] = bv;
+        for (int m = 1; m < PER; ++m) best = key[m] > best ? key[m] : best;
+        best = wave_max_key(best);
+        const int bid = topk_key_id(best);
+        // the lane that held the pick takes it out
+#pragma unroll
+        for (int m = 0; m < PER; ++m)
+            if (lane + 64 * m == bid) key[m] = 0ull;
+        sel_v[j] = topk_key_value(best);
         sel_id[j] = bid;
         if (sigmoid) {
             // the pick's raw score, from the lane that holds it

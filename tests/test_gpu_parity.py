@@ -97,6 +97,30 @@ def test_decode_full_size():
     assert torch.equal(y, y2)
 
 
+@pytest.fixture(scope="module")
+def decode_wide_batch():
+    # decode-sized experts with 65 rows of input; the cases below take the
+    # first T rows
+    w = W["decode"].with_(T=65)
+    return w, gpu_inputs(w)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 64, 65])
+def test_router_launch_shapes_full_width(decode_wide_batch, T):
+    """Each router launch shape (one or two rows per wave with every step's
+    loads in flight, eight rows per wave, 8 x 8 tiles) at the full width
+    H = 6144, E = 256: ids and the dispatch bit-exact, weights to fp32."""
+    w0, d0 = decode_wide_batch
+    w = w0.with_(T=T)
+    d = dict(d0, x=d0["x"][:T].contiguous())
+    log(f"case T={T}")
+    side = OracleSide(w, d)
+    y, ex = run_gpu(w, d)
+    check_routing(ex, side, 0, w.E)
+    if T <= 3:
+        compare(y, side.layer(list(range(T)), 0, w.E), f"T={T}")
+
+
 def test_prefill_full_size_sampled():
     w = W["prefill"]
     log(f"case {w}")
