@@ -33,16 +33,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int t = blockIdx.x / ctiles;
     const int c = ((blockIdx.x - t * ctiles) * 256 + threadIdx.x) * 4;
     if (c >= H) return;
+    // every pick's slot and weight first, then all of its rows' loads, then
+    // the sum in pick order (the loads overlap instead of queueing)
+    int p[16];
+    float wj[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        p[j] = j < k ? pos[(size_t)t * k + j] : -1;
+        wj[j] = p[j] >= 0 ? w[(size_t)t * k + j] : 0.0f;
+    }
+    float4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (p[j] >= 0) v[j] = *reinterpret_cast<const float4*>(y_r + (size_t)p[j] * H + c);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int p = pos[(size_t)t * k + j];
-        if (p < 0) continue;
-        const float wj = w[(size_t)t * k + j];
-        const float4 v = *reinterpret_cast<const float4*>(y_r + (size_t)p * H + c);
-        acc.x = __builtin_fmaf(wj, v.x, acc.x);
-        acc.y = __builtin_fmaf(wj, v.y, acc.y);
-        acc.z = __builtin_fmaf(wj, v.z, acc.z);
-        acc.w = __builtin_fmaf(wj, v.w, acc.w);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (p[j] < 0) continue;
+        acc.x = __builtin_fmaf(wj[j], v[j].x, acc.x);
+        acc.y = __builtin_fmaf(wj[j], v[j].y, acc.y);
+        acc.z = __builtin_fmaf(wj[j], v[j].z, acc.z);
+        acc.w = __builtin_fmaf(wj[j], v[j].w, acc.w);
     }
     if (y_s) {
         const float4 v = *reinterpret_cast<const float4*>(y_s + (size_t)t * H + c);
