@@ -106,7 +106,7 @@ def _expert_gu_bytes(w):
     return 2 * w.I * (w.H // 2) + 2 * 2 * w.I * (w.H // 32) * 2  # codes + bf16 scales and zeros
 
 
-def roofline_for(w, counts, stage_ms):
+def roofline_for(w, counts, stage_ms, counted=True):
     """Dominant kernel and its algorithmic bytes and flops per launch.
 
     The gate/up projection dominates every workload.  Its algorithmic bytes:
@@ -118,7 +118,9 @@ def roofline_for(w, counts, stage_ms):
     path) take the GEMV launch; larger ones the MFMA launches (one per tile
     height), whose time is summed.  The bound is whichever of HBM bytes at
     8 TB/s and flops at the bf16 dense MFMA peak takes longer; the MFMA
-    fraction is reported beside it for every workload."""
+    fraction is reported beside it for every workload.  counted: the committed
+    counters were taken on this configuration (not with another routing or a
+    tensor-parallel slice), so their traffic applies."""
     n_touched = int((counts > 0).sum())
     routed = int(counts.sum())
     sh_rows = w.T if w.Is else 0
@@ -130,19 +132,18 @@ def roofline_for(w, counts, stage_ms):
         kernel, ms = f"gateup_gemv_kernel<{0 if w.fmt == 'bf16' else 1},12>", stage_ms["gu_gemv"]
         traffic = measured_traffic(w.name, [f"moe::{kernel}"])
     else:
-        kernel = ("expert_mfma_pipe_kernel<true,256|128|64|32>" if w.fmt == "bf16"
-                  else "expert_mfma_w4_kernel<true,128|64|32> + shared expert_mfma_pipe_kernel")
+        kernel = ("expert_mfma_pipe_kernel<true,256> + expert_mfma_small_kernel<true>" if w.fmt == "bf16"
+                  else "expert_mfma_w4_kernel<true,128|64|32> + shared-expert bf16 launch")
         ms = stage_ms["gu_mfma"]
         if w.fmt == "bf16":
             traffic = measured_traffic(
-                w.name, [f"moe::expert_mfma_pipe_kernel<true,{bm}>" for bm in (256, 128, 64, 32)])
+                w.name, ["moe::expert_mfma_pipe_kernel<true,256>", "moe::expert_mfma_small_kernel<true>"])
         else:
             # the 4-bit launches, plus the one bf16 launch that holds the shared
-            # expert's rows (its tile height follows T)
-            sh_bm = 256 if w.T > 128 else 128 if w.T > 64 else 64 if w.T > 32 else 32
+            # expert's rows (256-row tiles above 128 rows, else the small-tile launch)
+            sh = "expert_mfma_pipe_kernel<true,256>" if w.T > 128 else "expert_mfma_small_kernel<true>"
             traffic = measured_traffic(
-                w.name, [f"moe::expert_mfma_w4_kernel<true,{bm}>" for bm in (128, 64, 32)]
-                + [f"moe::expert_mfma_pipe_kernel<true,{sh_bm}>"])
+                w.name, [f"moe::expert_mfma_w4_kernel<true,{bm}>" for bm in (128, 64, 32)] + [f"moe::{sh}"])
         # rows on the GEMV path (groups of 1..8 rows) are not in this launch
         small = counts[(counts > 0) & (counts <= 8)]
         n_touched -= int(small.numel())
@@ -151,6 +152,8 @@ def roofline_for(w, counts, stage_ms):
         act = (routed_m + sh_rows) * w.H * 2 + routed_m * w.I * 2 + sh_rows * w.Is * 2
         nbytes = wbytes + act
         flops = 2.0 * routed_m * 2 * w.I * w.H + 2.0 * sh_rows * 2 * w.Is * w.H
+    if not counted:
+        traffic = None
     sec = ms * 1e-3
     gbs = nbytes / sec / 1e9
     tfs = flops / sec / 1e12
@@ -337,7 +340,8 @@ def main():
         for s_ in range(len(names) - 1):
             stage[names[s_]] += hip.elapsed_ms(ev[i][s_], ev[i][s_ + 1]) / nstage
     counts = ex["counts"].cpu()
-    roof = roofline_for(w, counts, stage)
+    # the counters were taken with the default routing on the whole layer
+    roof = roofline_for(w, counts, stage, counted=args.tp == 1 and args.router == "softmax")
 
     reduce_info = None
     if args.reduce_parts:

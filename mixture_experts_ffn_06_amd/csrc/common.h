@@ -138,9 +138,10 @@ void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_
                      int mfma_cap, int32_t* plan_counts, hipStream_t st);
 void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
-// bf16 experts: the direct-to-LDS pipelined tiles of 256, 128, 64 and 32
-// rows (gate/up or down), one launch per tile height.  With 4-bit experts
-// these launches run the (bf16) shared expert's tiles only.
+// bf16 experts: the direct-to-LDS pipelined tiles, one launch for the
+// 256-row tiles and one for the 128-, 64- and 32-row tiles (gate/up or
+// down).  With 4-bit experts these launches run the (bf16) shared expert's
+// tiles only.
 void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st);
 // 4-bit experts: the same pipeline with the codes dequantized in LDS, tiles
 // of 128 (and 256 as two halves), 64 and 32 rows; then the shared expert.

@@ -745,8 +745,8 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
 }
 
 // Routed 4-bit groups only (the shared expert is bf16 and runs in
-// expert_mfma_pipe_kernel).  BM = 128 also takes the 256-row list, each tile
-// as two 128-row halves.
+// expert_mfma_pipe_kernel or expert_mfma_small_kernel).  BM = 128 also takes
+// the 256-row list, each tile as two 128-row halves.
 template <bool GATEUP, int BM>
 __global__ __launch_bounds__(W4Cfg<BM>::Threads, W4Cfg<BM>::PerCU) void expert_mfma_w4_kernel(ExpertArgs a) {
     using C = W4Cfg<BM>;
@@ -806,6 +806,5 @@ void launch_mfma_w4(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st
             gateup ? launch_small<true>(a, num_cu, st) : launch_small<false>(a, num_cu, st);
     }
 }
-
 
 }  // namespace moe
