@@ -93,12 +93,26 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
             }
         }
     }
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1)
+    // The xor rounds 1, 2, 4, .., 32 over the lane partials.  A few values:
+    // by DPP moves and four row totals (wave_sum: after each round every lane
+    // of a block of 2^j lanes holds the same value, so the DPP partner lane
+    // of the pair, quad, half-row and row mirrors stands in for the xor
+    // partner and the adds meet the same operands).  Many values: by
+    // shuffles, which keep the many independent chains free of DPP wait
+    // states.
+    if constexpr (RB * EB <= 8) {
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int e = 0; e < EB; ++e) acc[r][e] = acc[r][e] + __shfl_xor(acc[r][e], s, 64);
+            for (int e = 0; e < EB; ++e) acc[r][e] = wave_sum(acc[r][e]);
+    } else {
+#pragma unroll
+        for (int s = 1; s < 64; s <<= 1)
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int e = 0; e < EB; ++e) acc[r][e] = acc[r][e] + __shfl_xor(acc[r][e], s, 64);
+    }
 
 #pragma unroll
     for (int r = 0; r < RB; ++r)
@@ -176,8 +190,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
                 p = __builtin_fmaf(v3, v3, p);
             }
         }
-#pragma unroll
-        for (int s = 1; s < 64; s <<= 1) p = p + __shfl_xor(p, s, 64);
+        p = wave_sum(p);  // the xor rounds, as in the router
         const float inv = rms_inv(p, H, eps);
 #pragma unroll
         for (int i = 0; i < kRmsRegSteps; ++i)
@@ -203,8 +216,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t* __restrict
             p = __builtin_fmaf(v3, v3, p);
         }
     }
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) p = p + __shfl_xor(p, s, 64);
+    p = wave_sum(p);  // the xor rounds, as in the router
     const float inv = rms_inv(p, H, eps);
     for (int i = 0; i < nI; ++i) {
         const int c = 256 * i + 4 * lane;
