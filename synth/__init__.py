@@ -44,7 +44,7 @@ class Workload:
     I: int
     Is: int  # 0 = no shared expert
     fmt: str = "bf16"  # "bf16" | "w4"
-    bias: Optional[str] = None  # None | "zipf" | "band0" | "one_expert"
+    bias: Optional[str] = None  # None | "zipf" | "band0" | "one_expert" | "first_k"
     band: tuple = (0, 0)  # (lo, hi); hi = 0 means the full band [0, E)
     seed: int = 0
     w_std: float = 0.02  # expert / shared weights ~ N(0, w_std)
@@ -64,7 +64,8 @@ class Workload:
 
 # The five workloads: tiny, decode, prefill (Zipf-skewed groups), expert bands
 # on one GPU (plus the adversarial all-picks-in-band-0 case), and 4-bit
-# group-affine experts at one row and at 2048 rows.
+# group-affine experts at one row and at 2048 rows; plus a compute-bound
+# probe of the shared expert alone at prefill size.
 WORKLOADS = {
     "tiny": Workload("tiny", T=4, H=256, E=8, topk=2, I=128, Is=128),
     "decode": Workload("decode", T=8, H=6144, E=256, topk=8, I=2048, Is=2048),
@@ -75,6 +76,12 @@ WORKLOADS = {
     ),
     "w4_t1": Workload("w4_t1", T=1, H=6144, E=256, topk=8, I=2048, Is=2048, fmt="w4"),
     "w4_t2048": Workload("w4_t2048", T=2048, H=6144, E=256, topk=8, I=2048, Is=2048, fmt="w4"),
+    # Compute-bound probe: prefill sizes with every pick on experts 0..7 and
+    # the band [8, 256), so no routed pick is in the band and the MFMA work
+    # is the shared expert's 4096 rows alone.
+    "shared_probe": Workload(
+        "shared_probe", T=4096, H=6144, E=256, topk=8, I=2048, Is=2048, bias="first_k", band=(8, 256)
+    ),
 }
 
 BAND_WIDTH = 32  # the expert-band workload runs bands [32b, 32b + 32)
@@ -149,6 +156,12 @@ def make_bias(w: Workload) -> Optional[torch.Tensor]:
         # +10 on experts [0, 32): with top-8, every row picks 8 of those 32.
         b = torch.zeros(w.E, dtype=torch.float32)
         b[:BAND_WIDTH] = 10.0
+        return b
+    if w.bias == "first_k":
+        # +1000 on the first topk experts: far beyond any logit of these
+        # weights at any T, so every row picks exactly them
+        b = torch.zeros(w.E, dtype=torch.float32)
+        b[: w.topk] = 1000.0
         return b
     if w.bias == "one_expert":
         # +10 on the first topk experts: every row picks exactly them.

@@ -136,6 +136,21 @@ def test_prefill_full_size_sampled():
     assert torch.equal(y, y2)
 
 
+def test_shared_probe_full_size_sampled():
+    """The compute-bound probe: every pick outside the band [8, 256), so the
+    layer is the shared expert's 4096 rows alone (one 256-row group per
+    column tile on every CU)."""
+    w = W["shared_probe"]
+    log(f"case {w}")
+    d = gpu_inputs(w)
+    side = OracleSide(w, d)
+    y, ex = run_gpu(w, d)
+    check_routing(ex, side, w.band_lo, w.band_hi)
+    assert int(ex["counts"][: w.band_hi - w.band_lo].sum()) == 0
+    rows = sample_rows(w.T, 10, seed=4)
+    compare(y[rows], side.layer(rows, w.band_lo, w.band_hi), "shared probe sampled rows")
+
+
 def test_bands_full_size():
     w = W["bands"]
     log(f"case {w}")
