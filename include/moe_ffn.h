@@ -26,7 +26,8 @@
  *      c inner, fused multiply-adds from +0.0, then six pairwise rounds
  *      l xor 1, 2, 4, 8, 16, 32), -0.0 normalised to +0.0;
  *   2. top-k: experts ordered by (logit descending, id ascending), the first
- *      topk in that pick order; weights w_j = exp(l_j - l_0) / sum_i exp(l_i -
+ *      topk in that pick order (the order is unspecified for NaN logits,
+ *      which only non-finite inputs produce); weights w_j = exp(l_j - l_0) / sum_i exp(l_i -
  *      l_0) over the picks (softmax renormalised over the picks);
  *   3. dispatch of the in-band picks by expert (counts, offsets, a stable
  *      permutation ascending in row, and its inverse);
