@@ -59,12 +59,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
             const int i = min(i0 + b, nI - 1);  // steps past the end reload the last one, unused
+            // wave-uniform row pointers plus an unsigned 32-bit lane offset:
+            // scalar-base addressing, no 64-bit address arithmetic per load
+            const uint32_t k0 = 256u * (uint32_t)i + 4u * (uint32_t)lane;
 #pragma unroll
             for (int r = 0; r < RB; ++r)
-                xu[b][r] = *reinterpret_cast<const uint2*>(xp[r] + 256 * i + 4 * lane);
+                xu[b][r] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(xp[r]) + 2u * k0);
 #pragma unroll
             for (int e = 0; e < EB; ++e)
-                wf[b][e] = *reinterpret_cast<const float4*>(wp[e] + 256 * i + 4 * lane);
+                wf[b][e] = *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(wp[e]) + 4u * k0);
         }
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
