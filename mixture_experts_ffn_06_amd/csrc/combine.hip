@@ -24,6 +24,16 @@ __device__ __forceinline__ float4 add_res(float4 acc, const uint16_t* r) {
                        acc.w + bf16_hi(b.y));
 }
 
+// The expert outputs, the shared output and the partials are each read once
+// here: their loads carry the non-temporal hint (the `nt` cache-policy bit),
+// so they do not hold cache lines in preference to data that is reused
+// (prefill pick-order combine 206 -> 167 us).
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 cload(const float* p) {
+    const f32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_r,
                                                      const float* __restrict__ y_s,
                                                      const uint16_t* __restrict__ res,
@@ -45,7 +55,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float4 v[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-        if (p[j] >= 0) v[j] = *reinterpret_cast<const float4*>(y_r + (size_t)p[j] * H + c);
+        if (p[j] >= 0) v[j] = cload(y_r + (size_t)p[j] * H + c);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
@@ -56,7 +66,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         acc.w = __builtin_fmaf(wj[j], v[j].w, acc.w);
     }
     if (y_s) {
-        const float4 v = *reinterpret_cast<const float4*>(y_s + (size_t)t * H + c);
+        const float4 v = cload(y_s + (size_t)t * H + c);
         acc.x = acc.x + v.x;
         acc.y = acc.y + v.y;
         acc.z = acc.z + v.z;
@@ -206,12 +216,12 @@ __global__ __launch_bounds__(256) void combine_tree_kernel(const float* __restri
                 const int p = __builtin_amdgcn_readfirstlane(s_p[i]);
                 const float wi = __builtin_bit_cast(
                     float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, s_w[i])));
-                const float4 v = *reinterpret_cast<const float4*>(y_r + (size_t)p * H + c);
+                const float4 v = cload(y_r + (size_t)p * H + c);
                 cur = make_float4(wi * v.x, wi * v.y, wi * v.z, wi * v.w);
             }
         }
         if (rootnorm) cur = norm4(cur);
-        if (y_s) cur = add4(cur, *reinterpret_cast<const float4*>(y_s + (size_t)t * H + c));
+        if (y_s) cur = add4(cur, cload(y_s + (size_t)t * H + c));
         if (res) cur = add_res(cur, res + (size_t)t * H + c);
         *reinterpret_cast<float4*>(out + (size_t)t * H + c) = cur;
     }
@@ -244,9 +254,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceProgram pg, const flo
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
         float4 acc;
         if (pg.order == 0) {
-            acc = reinterpret_cast<const float4*>(pg.part[0])[i];
+            acc = cload(pg.part[0] + 4 * i);
             for (int p = 1; p < pg.nparts; ++p)
-                acc = add4(acc, reinterpret_cast<const float4*>(pg.part[p])[i]);
+                acc = add4(acc, cload(pg.part[p] + 4 * i));
         } else {
             float4 pend[kTreeLevels];
             const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -254,7 +264,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceProgram pg, const flo
             for (int lev = 0; lev < kTreeLevels; ++lev) pend[lev] = zero;
             for (int o = 0; o < pg.nops; ++o) {
                 const int pi = pg.op_part[o], l0 = pg.op_l0[o], l1 = pg.op_l1[o];
-                float4 v = pi >= 0 ? reinterpret_cast<const float4*>(pg.part[pi])[i] : zero;
+                float4 v = pi >= 0 ? cload(pg.part[pi] + 4 * i) : zero;
 #pragma unroll
                 for (int lev = 0; lev < kTreeLevels; ++lev)
                     if (lev >= l0 && lev < l1) v = add4(pend[lev], v);
@@ -267,7 +277,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceProgram pg, const flo
             for (int lev = 0; lev < kTreeLevels; ++lev)
                 if (lev == pg.root_level) acc = pend[lev];
         }
-        if (y_s) acc = add4(acc, reinterpret_cast<const float4*>(y_s)[i]);
+        if (y_s) acc = add4(acc, cload(y_s + 4 * i));
         if (res) acc = add_res(acc, res + 4 * i);
         reinterpret_cast<float4*>(y)[i] = acc;
     }

@@ -23,6 +23,16 @@
 
 namespace moe {
 
+// Weight loads.  Every weight byte is read once per call, so the loads carry
+// the non-temporal hint (the `nt` cache-policy bit): the lines are not kept
+// in preference to reused data.  Measured on the decode GEMVs: 6.0 -> 6.8
+// TB/s.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 wload(const void* p) {
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 constexpr int kGemvThreads = 512;
 constexpr int kGemvWaves = kGemvThreads / 64;
 
@@ -171,8 +181,8 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
                     const int k = 512 * (q0 + qq) + 8 * lane;
                     ok[qq] = (q0 + qq < nch) && (k < H);
                     kk[qq] = ok[qq] ? k : 0;
-                    wg[qq] = *reinterpret_cast<const uint4*>(gr + kk[qq]);
-                    wu[qq] = *reinterpret_cast<const uint4*>(ur + kk[qq]);
+                    wg[qq] = wload(gr + kk[qq]);
+                    wu[qq] = wload(ur + kk[qq]);
                 }
 #pragma unroll
                 for (int qq = 0; qq < CB; ++qq) {
@@ -201,8 +211,8 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
                     const int k = 2048 * (q0 + qq) + 32 * lane;
                     ok[qq] = (q0 + qq < nch) && (k < H);
                     kk[qq] = ok[qq] ? k : 0;
-                    qg[qq] = *reinterpret_cast<const uint4*>(gq + kk[qq] / 2);
-                    qu[qq] = *reinterpret_cast<const uint4*>(uq + kk[qq] / 2);
+                    qg[qq] = wload(gq + kk[qq] / 2);
+                    qu[qq] = wload(uq + kk[qq] / 2);
                     sg[qq] = gs[kk[qq] / 32];
                     zg[qq] = gz[kk[qq] / 32];
                     su[qq] = us[kk[qq] / 32];
@@ -309,8 +319,8 @@ __device__ ItemMeta gateup_fast(const ExpertArgs& a, const ItemMeta& m, bool res
         uint4 wg[CB], wu[CB];
 #pragma unroll
         for (int q = 0; q < CB; ++q) {
-            wg[q] = *reinterpret_cast<const uint4*>(gr + 512 * q);
-            wu[q] = *reinterpret_cast<const uint4*>(ur + 512 * q);
+            wg[q] = wload(gr + 512 * q);
+            wu[q] = wload(ur + 512 * q);
         }
         if (cc == 0) {
             if (has_next) mn = load_meta(a, itn, nrouted, TR);
@@ -471,7 +481,7 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int u = 0; u < U; ++u) wv[u][q] = *reinterpret_cast<const uint4*>(wrow + (size_t)u * K + 512 * q);
+            for (int u = 0; u < U; ++u) wv[u][q] = wload(wrow + (size_t)u * K + 512 * q);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -502,7 +512,7 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
                 kk[qq] = ok[qq] ? k : 0;
 #pragma unroll
                 for (int u = 0; u < U; ++u)
-                    wv[u][qq] = *reinterpret_cast<const uint4*>(wbase + (size_t)(cbase + u) * K + kk[qq]);
+                    wv[u][qq] = wload(wbase + (size_t)(cbase + u) * K + kk[qq]);
             }
 #pragma unroll
             for (int qq = 0; qq < CB; ++qq) {
@@ -534,7 +544,7 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const size_t row = rbase + cbase + u;
-                qv[u] = *reinterpret_cast<const uint4*>(a.qd + row * (K / 2) + kq / 2);
+                qv[u] = wload(a.qd + row * (K / 2) + kq / 2);
                 sv[u] = a.sd[row * (K / 32) + kq / 32];
                 zv[u] = a.zd[row * (K / 32) + kq / 32];
             }
