@@ -445,7 +445,14 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
                 gateup_dispatch_rows<1, CB>(a, g, m.tile * kGuCols, xs, xsum);
             else
                 gateup_dispatch_rows<0, CB>(a, g, m.tile * kGuCols, xs, xsum);
-            __syncthreads();  // the next staging may overwrite these rows
+            // The next item overwrites these rows only if it stages others
+            // (or takes the fast path, whose buffers overlap them); one-row
+            // groups of the same token and format keep them, and need no
+            // barrier (every 4-bit item at T = 1).
+            const bool w4n = W4 && mn.g.expert >= 0;
+            const bool keeps = has_next && mn.g.n == 1 && key >= 0 && 2 * mn.tok0 + (w4n ? 1 : 0) == key &&
+                               !(!w4n && mn.g.n <= 2 && fast_ok);
+            if (!keeps) __syncthreads();
             cur = -1;
         }
         if (!has_next) break;
