@@ -233,6 +233,9 @@ def main():
                          "columns split over N ranks (whole units, remainder on the lowest ranks)")
     ap.add_argument("--tp-rank", type=int, default=0)
     ap.add_argument("--tp-unit", type=int, default=64)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the layer captured once in a HIP graph (the eviction "
+                         "stays outside the graph) instead of eager calls")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB five times (a known byte "
                          "count for calibrating HBM byte counters), then exit")
@@ -316,13 +319,35 @@ def main():
     # launch stream (the cache eviction before it is not part of the layer).
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    graph = None
+    if args.graph:
+        # capture one call (after a warm-up on the capture stream); the
+        # replays below run on the same stream as the eager calls would
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
+                        w.band_hi, w.topk, out=out, workspace=ws, **opts)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
+                        w.band_hi, w.topk, out=out, workspace=ws, **opts)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            evict()
+            graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         evict()
         starts[i].record(stream)
-        moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
-                    w.band_hi, w.topk, out=out, workspace=ws, **opts)
+        if graph is not None:
+            graph.replay()
+        else:
+            moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
+                        w.band_hi, w.topk, out=out, workspace=ws, **opts)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -386,6 +411,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "topk": w.topk, "I": w.I,
                    "Is": w.Is, "fmt": w.fmt, "band": [w.band_lo, w.band_hi],
                    "combine": args.combine, "tp": tp_info, "router": args.router,
+                   "launch": "hip graph replay" if args.graph else "eager",
                    "norm": "rmsnorm eps 1e-5 + residual" if args.norm else None,
                    "l2_mall_eviction": {"read": "1 GiB read", "write": "1 GiB write",
                                         "none": None}[args.flush]},
