@@ -202,8 +202,18 @@ def cpu_baseline(w, d, ex, rows_budget, min_seconds=10.0, modes=None):
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(reps * len(rows) / dt, 3), "unit": "rows/s", "cores": min(threads, len(rows)),
-            "threads_available": threads, "kind": "oracle",
+            "threads_available": threads, "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model,
+            "kind": "oracle",
             "sample": f"rows 0..{len(rows) - 1} of the {w.name} workload, run {reps} times "
                       f"(fp64 per-row oracle, OpenMP over rows), {dt:.2f} s"}
 
