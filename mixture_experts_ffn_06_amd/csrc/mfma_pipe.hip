@@ -33,8 +33,6 @@ typedef uint32_t u32x4_p __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) const bf16x8_p lds_bf16x8;
 
-constexpr int kBTileBytes = kBN * kBK * 2;  // 16 KiB of 128 weight rows per stage
-
 // BM x BN tiles.  256 x 256: 8 waves of 128 x 64 (fewer LDS operand bytes
 // per MFMA than 64 x 64 wave tiles; LDS bandwidth bounds the 64 x 64 layout
 // at full MFMA rate), two 64 KiB stages, one block per CU.  256 x 128 (when

@@ -401,16 +401,6 @@ extern "C" int32_t moe_tp_shares(int32_t dim, int32_t unit, int32_t ranks, int32
 
 namespace {
 
-// rows [r0, r0 + n) of each of `blocks` blocks of `rows_per_block` rows of
-// `row_bytes` bytes -> consecutive blocks of n rows
-hipError_t copy_rows(void* dst, const void* src, size_t blocks, size_t rows_per_block, size_t r0,
-                     size_t n, size_t row_bytes, hipStream_t st) {
-    return hipMemcpy2DAsync(dst, n * row_bytes,
-                            static_cast<const unsigned char*>(src) + r0 * row_bytes,
-                            rows_per_block * row_bytes, n * row_bytes, blocks,
-                            hipMemcpyDeviceToDevice, st);
-}
-
 // bytes [b0, b0 + nb) of every row of `rows` rows of `row_bytes` bytes
 hipError_t copy_cols(void* dst, const void* src, size_t rows, size_t row_bytes, size_t b0, size_t nb,
                      hipStream_t st) {

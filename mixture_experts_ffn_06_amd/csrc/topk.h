@@ -110,16 +110,11 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ logits, const
         }
         key[m] = e < E ? topk_key(v, e) : 0ull;
     }
-    float sel_v[16];
-    int sel_id[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        sel_v[j] = 0.0f;
-        sel_id[j] = 0;
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j >= k) break;
+    // lane j keeps pick j (its value and id), so no register array is
+    // indexed by the runtime pick number
+    float my_v = 0.0f;
+    int my_id = 0;
+    for (int j = 0; j < k; ++j) {
         uint64_t best = key[0];
 #pragma unroll
         for (int m = 1; m < PER; ++m) best = key[m] > best ? key[m] : best;
@@ -129,47 +124,33 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ logits, const
 #pragma unroll
         for (int m = 0; m < PER; ++m)
             if (lane + 64 * m == bid) key[m] = 0ull;
-        sel_v[j] = topk_key_value(best);
-        sel_id[j] = bid;
+        float v = topk_key_value(best);
         if (sigmoid) {
             // the pick's raw score, from the lane that holds it
             float mine = 0.0f;
 #pragma unroll
             for (int m = 0; m < PER; ++m)
                 if (m == (bid >> 6)) mine = sc[m];
-            sel_v[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), bid & 63));
+            v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), bid & 63));
+        }
+        if (lane == j) {
+            my_v = v;
+            my_id = bid;
         }
     }
+    if (lane >= k) return;
+    ids[(size_t)t * k + lane] = my_id;
+    if (sids) sids[t * k + lane] = my_id;
     if (sigmoid) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            if (j >= k) break;
-            if (lane == j) {
-                ids[(size_t)t * k + j] = sel_id[j];
-                w[(size_t)t * k + j] = sel_v[j];
-                if (sids) sids[t * k + j] = sel_id[j];
-            }
-        }
+        w[(size_t)t * k + lane] = my_v;
         return;
     }
-    const float m0 = sel_v[0];
-    float a[16];
+    // softmax over the picks: a_j = exp(l_j - l_0), summed in pick order
+    const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_v), 0));
+    const float a = expf(my_v - m0);
     float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j >= k) break;
-        a[j] = expf(sel_v[j] - m0);
-        s = s + a[j];
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j >= k) break;
-        if (lane == j) {
-            ids[(size_t)t * k + j] = sel_id[j];
-            w[(size_t)t * k + j] = a[j] / s;
-            if (sids) sids[t * k + j] = sel_id[j];
-        }
-    }
+    for (int j = 0; j < k; ++j) s = s + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), j));
+    w[(size_t)t * k + lane] = a / s;
 }
 
 }  // namespace moe
