@@ -572,6 +572,72 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
     }
 }
 
+// A bf16 item of a group of one or two rows with K = 2048 (every routed
+// group at decode): the group's rows, when they change, are read into
+// registers and written to LDS buffer xb (one of two, alternating) after the
+// first pass's weight loads are issued, so the row fetch and the barrier
+// overlap the weight stream.  Same per-column order as down_item.
+template <int NR>
+__device__ void down_fast(const ExpertArgs& a, const Group& g, int n0, bool restage, uint16_t* xb) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool shared = g.expert < 0;
+    constexpr int K = 512 * 4;
+    constexpr int c8n = K / 8;
+    static_assert(NR * c8n <= kGemvThreads, "one 16-byte chunk of the rows per thread");
+    const int H = a.H;
+    constexpr int U = kDnCols / kGemvWaves / 2;
+    uint4 xc = make_uint4(0, 0, 0, 0);
+    const int r_ = tid / c8n, c8 = tid - r_ * c8n;
+    if (restage && tid < NR * c8n) {
+        const uint16_t* src = shared ? a.h_s + (size_t)r_ * K : a.h_r + (size_t)(g.row0 + r_) * K;
+        xc = *reinterpret_cast<const uint4*>(src + 8 * c8);
+    }
+    const uint16_t* xl = xb + 8 * lane;
+#pragma nounroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int cbase = n0 + 2 * U * wave + U * pass;
+        const uint16_t* wrow = (shared ? a.swd : a.wd + (size_t)g.expert * H * K) + (size_t)cbase * K + 8 * lane;
+        uint4 wv[U][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int u = 0; u < U; ++u) wv[u][q] = wload(wrow + (size_t)u * K + 512 * q);
+        if (pass == 0 && restage) {
+            if (tid < NR * c8n) *reinterpret_cast<uint4*>(xb + (size_t)r_ * K + 8 * c8) = xc;
+            wait_lgkm0();
+            __builtin_amdgcn_s_barrier();
+        }
+        float acc[U][NR];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[u][r] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(xl + r * K + 512 * q);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float t = acc[u][r];
+                    t = dot2_bf16(wv[u][q].x, xv.x, t);
+                    t = dot2_bf16(wv[u][q].y, xv.y, t);
+                    t = dot2_bf16(wv[u][q].z, xv.z, t);
+                    t = dot2_bf16(wv[u][q].w, xv.w, t);
+                    acc[u][r] = t;
+                }
+            }
+        float* yout = shared ? a.y_s : a.y_r + (size_t)g.row0 * H;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const float v = wave_sum(acc[u][r]);
+                if (lane == ((u * NR + r) & 63)) yout[(size_t)r * H + cbase + u] = v;
+            }
+    }
+}
+
 template <int W4>
 __device__ __forceinline__ void down_dispatch_rows(const ExpertArgs& a, const Group& g, int n0,
                                                    const uint16_t* xs, const float* xsum) {
@@ -588,33 +654,54 @@ __device__ __forceinline__ void down_dispatch_rows(const ExpertArgs& a, const Gr
 }
 
 template <int W4>
-__global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, int max_rows,
+__global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, int lds_rows,
                                                                  int kmax) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-    float* xsum = reinterpret_cast<float*>(smem + (size_t)max_rows * kmax * 2);
+    float* xsum = reinterpret_cast<float*>(smem + (size_t)lds_rows * kmax * 2);
     const int ngv = a.plan_counts[0];
     if (ngv == 0) return;
     const bool sh_last = a.groups[a.gemv_list[ngv - 1]].expert < 0;
     const int nrouted = ngv - (sh_last ? 1 : 0);
     const int TR = a.H / kDnCols;
     const int total = (nrouted + (sh_last ? 1 : 0)) * TR;
-    int cur = -1;
+    // fcur: the group in the current fast-path buffer; scur: the group staged
+    // across the LDS area by the synchronous path (which overlaps the fast
+    // path's buffers, so each path forgets the other's rows)
+    int fcur = -1, scur = -1, buf = 0;
+    bool prev_slow = false;
     for (int it = blockIdx.x; it < total; it += gridDim.x) {
         const int gi = it / TR, tile = it - gi * TR;
         const Group g = a.groups[a.gemv_list[gi]];
         const bool w4 = W4 && g.expert >= 0;
         const int K = g.expert < 0 ? a.Is : a.I;
-        if (gi != cur) {
+        // (not in the 4-bit kernel: its registers would spill)
+        if (!W4 && g.n <= 2 && K == 512 * 4) {
+            if (prev_slow) __syncthreads();  // the synchronous item's LDS reads are done
+            const bool restage = gi != fcur;
+            if (restage) buf ^= 1;
+            uint16_t* xb = xs + (size_t)buf * 2 * K;
+            if (g.n == 1)
+                down_fast<1>(a, g, tile * kDnCols, restage, xb);
+            else
+                down_fast<2>(a, g, tile * kDnCols, restage, xb);
+            fcur = gi;
+            scur = -1;
+            prev_slow = false;
+            continue;
+        }
+        if (gi != scur) {
             __syncthreads();
             stage_rows(a, g, true, K, g.n, w4, xs, xsum);
             __syncthreads();
-            cur = gi;
+            scur = gi;
         }
         if (w4)
             down_dispatch_rows<1>(a, g, tile * kDnCols, xs, xsum);
         else
             down_dispatch_rows<0>(a, g, tile * kDnCols, xs, xsum);
+        fcur = -1;
+        prev_slow = true;
     }
 }
 
@@ -658,14 +745,16 @@ void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStre
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st) {
     const int max_rows = a.T < kSmallRows ? a.T : kSmallRows;
     const int kmax = a.I > a.Is ? a.I : a.Is;
-    const size_t lds = (size_t)max_rows * kmax * 2 + (a.fmt ? (size_t)max_rows * (kmax / 32) * 4 : 0);
+    // rows of LDS: the largest group, and at least two buffers of two rows
+    const int lds_rows = max_rows > 4 ? max_rows : 4;
+    const size_t lds = (size_t)lds_rows * kmax * 2 + (a.fmt ? (size_t)max_rows * (kmax / 32) * 4 : 0);
     const int grid = gemv_grid(lds, num_cu, (long long)max_groups * (a.H / kDnCols));
     if (a.fmt) {
         allow_lds(down_gemv_kernel<1>, lds);
-        down_gemv_kernel<1><<<grid, kGemvThreads, lds, st>>>(a, max_rows, kmax);
+        down_gemv_kernel<1><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
     } else {
         allow_lds(down_gemv_kernel<0>, lds);
-        down_gemv_kernel<0><<<grid, kGemvThreads, lds, st>>>(a, max_rows, kmax);
+        down_gemv_kernel<0><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
     }
 }
 
