@@ -115,7 +115,9 @@ def roofline_for(w, counts, stage_ms, counted=True):
     expert's, the routed and shared rows of x it reads and the bf16
     intermediate it writes.  Its flops: 2*(2I)*H per routed row and
     2*(2Is)*H per shared row.  Decode-sized batches (every group on the GEMV
-    path) take the GEMV launch; larger ones the MFMA launches (one per tile
+    path) take the GEMV launch, without the shared expert when the top-k /
+    dispatch launch computes its gate/up (T <= 8, H a multiple of 512, its
+    rows within 128 KiB); larger ones the MFMA launches (one per tile
     height), whose time is summed.  The bound is whichever of HBM bytes at
     8 TB/s and flops at the bf16 dense MFMA peak takes longer; the MFMA
     fraction is reported beside it for every workload.  counted: the committed
@@ -131,6 +133,12 @@ def roofline_for(w, counts, stage_ms, counted=True):
     if w.T <= 8:
         kernel, ms = f"gateup_gemv_kernel<{0 if w.fmt == 'bf16' else 1},12>", stage_ms["gu_gemv"]
         traffic = measured_traffic(w.name, [f"moe::{kernel}"])
+        if w.Is and w.H % 512 == 0 and w.T * w.H * 2 <= 128 * 1024:
+            # the shared expert's gate/up ran in the top-k/dispatch launch
+            wbytes = n_touched * _expert_gu_bytes(w)
+            act = routed * w.H * 2 + routed * w.I * 2
+            nbytes = wbytes + act
+            flops = 2.0 * routed * 2 * w.I * w.H
     else:
         kernel = ("expert_mfma_pipe_kernel<true,256> + expert_mfma_small_kernel<true>" if w.fmt == "bf16"
                   else "expert_mfma_w4_kernel<true,128|64|32> + shared-expert bf16 launch")

@@ -309,9 +309,97 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
                         mfma_list, mfma_cap, plan_counts);
 }
 
+// The shared expert's gate/up for NR rows in one block of 16 waves: each wave
+// takes gate/up column pairs c = wave * nblocks + block, then c + 16 nblocks,
+// ... (so every block has work when the columns are few), with the rows staged
+// in LDS.  A wave's first weight loads are issued before the staging and its
+// barrier, and each next column's first loads before the current column's
+// lane sums.  A column's two dots follow the GEMV path's order: lane l
+// accumulates the inputs 512 q + 8 l .. +7 over q = 0, 1, .. (dot2 pairs in
+// order), then the lanes are summed by wave_sum.
+template <int NR>
+__device__ void shared_gateup_rows(const SharedGateUp& s, int block, int nblocks) {
+    extern __shared__ uint4 xs4[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(xs4);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = s.H, c8n = H / 8;
+    constexpr int QB = 6;  // lane steps of 512 inputs per block of loads
+    const int nq = H / 512;
+    uint4 wg[QB], wu[QB];
+    auto issue = [&](int c, int q0) {
+        const uint16_t* gr = s.w + (size_t)c * H + 8 * lane;
+        const uint16_t* ur = gr + (size_t)s.Is * H;
+#pragma unroll
+        for (int qq = 0; qq < QB; ++qq) {
+            const int q = q0 + qq < nq ? q0 + qq : nq - 1;  // past the row: reload, unused
+            wg[qq] = wload(gr + 512 * q);
+            wu[qq] = wload(ur + 512 * q);
+        }
+    };
+    int c = wave * nblocks + block;
+    const int step = nblocks * (int)(blockDim.x >> 6);
+    if (c < s.Is) issue(c, 0);
+    for (int idx = tid; idx < NR * c8n; idx += blockDim.x) {
+        const int r = idx / c8n, c8 = idx - r * c8n;
+        *reinterpret_cast<uint4*>(xs + (size_t)r * H + 8 * c8) =
+            *reinterpret_cast<const uint4*>(s.x + (size_t)r * H + 8 * c8);
+    }
+    __syncthreads();
+    const uint16_t* xl = xs + 8 * lane;
+    while (c < s.Is) {
+        float ag[NR], au[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) ag[r] = au[r] = 0.0f;
+        for (int q0 = 0; q0 < nq; q0 += QB) {
+            if (q0 > 0) issue(c, q0);
+#pragma unroll
+            for (int qq = 0; qq < QB; ++qq) {
+                if (q0 + qq >= nq) break;  // wave-uniform
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const uint4 xv = *reinterpret_cast<const uint4*>(xl + (size_t)r * H + 512 * (q0 + qq));
+                    float sg = ag[r], su = au[r];
+                    sg = dot2_bf16(wg[qq].x, xv.x, sg);
+                    sg = dot2_bf16(wg[qq].y, xv.y, sg);
+                    sg = dot2_bf16(wg[qq].z, xv.z, sg);
+                    sg = dot2_bf16(wg[qq].w, xv.w, sg);
+                    su = dot2_bf16(wu[qq].x, xv.x, su);
+                    su = dot2_bf16(wu[qq].y, xv.y, su);
+                    su = dot2_bf16(wu[qq].z, xv.z, su);
+                    su = dot2_bf16(wu[qq].w, xv.w, su);
+                    ag[r] = sg;
+                    au[r] = su;
+                }
+            }
+        }
+        const int cn = c + step;
+        if (cn < s.Is) issue(cn, 0);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const float g = wave_sum(ag[r]);
+            const float u = wave_sum(au[r]);
+            if (lane == r) s.h[(size_t)r * s.Is + c] = f32_to_bf16_bits(silu_mul(g, u));
+        }
+        c = cn;
+    }
+}
+
+__device__ void shared_gateup_block(const SharedGateUp& s, int block, int nblocks) {
+    switch (s.T) {
+        case 1: shared_gateup_rows<1>(s, block, nblocks); break;
+        case 2: shared_gateup_rows<2>(s, block, nblocks); break;
+        case 3: shared_gateup_rows<3>(s, block, nblocks); break;
+        case 4: shared_gateup_rows<4>(s, block, nblocks); break;
+        case 5: shared_gateup_rows<5>(s, block, nblocks); break;
+        case 6: shared_gateup_rows<6>(s, block, nblocks); break;
+        case 7: shared_gateup_rows<7>(s, block, nblocks); break;
+        default: shared_gateup_rows<8>(s, block, nblocks); break;
+    }
+}
+
 // Batches of at most 16 rows: top-k (wave t takes row t) and the dispatch in
-// one block; the picks go to the outputs and to LDS, where the dispatch reads
-// them.
+// block 0; the picks go to the outputs and to LDS, where the dispatch reads
+// them.  Blocks 1 .. sg.blocks compute the shared expert's gate/up meanwhile.
 template <int PER>
 __global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(
     const float* __restrict__ logits, const float* __restrict__ bias, int sigmoid, int E,
@@ -319,7 +407,11 @@ __global__ __launch_bounds__(1024) void topk_dispatch_small_kernel(
     int T, int k, int lo, int nb, bool has_shared, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
     Group* __restrict__ groups, int32_t* __restrict__ gemv_list, int32_t* __restrict__ mfma_list,
-    int mfma_cap, int32_t* __restrict__ plan_counts) {
+    int mfma_cap, int32_t* __restrict__ plan_counts, SharedGateUp sg) {
+    if (blockIdx.x > 0) {
+        shared_gateup_block(sg, blockIdx.x - 1, sg.blocks);
+        return;
+    }
     __shared__ int32_t s_ids[16 * 16];  // rows x picks (at most 16 each)
     const int wave = threadIdx.x >> 6;
     if (wave < T) topk_row<PER>(logits, bias, sigmoid, wave, E, k, ids, wts, s_ids);
@@ -332,14 +424,19 @@ void launch_topk_dispatch_small(const float* logits, const float* bias, int sigm
                                 int32_t* ids, int T, int k,
                                 int lo, int hi, bool has_shared, int32_t* counts, int32_t* offsets,
                                 int32_t* perm, int32_t* pos, Group* groups, int32_t* gemv_list,
-                                int32_t* mfma_list, int mfma_cap, int32_t* plan_counts, hipStream_t st) {
+                                int32_t* mfma_list, int mfma_cap, int32_t* plan_counts,
+                                const SharedGateUp& sg, hipStream_t st) {
     const int nb = hi - lo;
-    const size_t lds = sizeof(unsigned long long) * 4 * (size_t)nb + sizeof(int) * ((size_t)nb + 1);
+    size_t lds = sizeof(unsigned long long) * 4 * (size_t)nb + sizeof(int) * ((size_t)nb + 1);
+    if (sg.blocks > 0 && (size_t)sg.T * sg.H * 2 > lds) lds = (size_t)sg.T * sg.H * 2;
     const int per = (E + 63) / 64;
 #define MOE_TOPK_DISPATCH(P)                                                                          \
-    topk_dispatch_small_kernel<P><<<1, 1024, lds, st>>>(logits, bias, sigmoid, E, wts, ids, T, k, lo, nb, has_shared, \
-                                                         counts, offsets, perm, pos, groups, gemv_list, \
-                                                         mfma_list, mfma_cap, plan_counts)
+    do {                                                                                              \
+        allow_lds(topk_dispatch_small_kernel<P>, lds);                                                \
+        topk_dispatch_small_kernel<P><<<1 + sg.blocks, 1024, lds, st>>>(                              \
+            logits, bias, sigmoid, E, wts, ids, T, k, lo, nb, has_shared, counts, offsets, perm, pos, \
+            groups, gemv_list, mfma_list, mfma_cap, plan_counts, sg);                                 \
+    } while (0)
     if (per <= 1)
         MOE_TOPK_DISPATCH(1);
     else if (per <= 2)

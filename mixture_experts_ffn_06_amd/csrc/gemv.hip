@@ -23,16 +23,6 @@
 
 namespace moe {
 
-// Weight loads.  Every weight byte is read once per call, so the loads carry
-// the non-temporal hint (the `nt` cache-policy bit): the lines are not kept
-// in preference to reused data.  Measured on the decode GEMVs: 6.0 -> 6.8
-// TB/s.
-typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 wload(const void* p) {
-    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 constexpr int kGemvThreads = 512;
 constexpr int kGemvWaves = kGemvThreads / 64;
 
@@ -402,7 +392,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
     if (ngv == 0) return;
     const bool sh_last = a.groups[a.gemv_list[ngv - 1]].expert < 0;
     const int nrouted = ngv - (sh_last ? 1 : 0);
-    const int TR = a.I / kGuCols, TS = sh_last ? a.Is / kGuCols : 0;
+    const int TR = a.I / kGuCols, TS = sh_last && !a.shared_gu_done ? a.Is / kGuCols : 0;
     const int total = nrouted * TR + TS;
     // Items are dealt round-robin: at any moment the blocks stream neighbouring
     // column tiles of the same experts, so HBM sees a few long sequential runs

@@ -229,12 +229,29 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     const float* sel_bias = sigmoid ? router_w->bias : nullptr;
     mark(MOE_EV_TOPK);
     const int mfma_cap = max_mfma_tiles(T, E, topk);
+    // With at most kSmallRows rows the shared expert is a GEMV group; its
+    // gate/up then runs inside the top-k/dispatch launch (its rows staged in
+    // at most 128 KiB of LDS).
+    moe::SharedGateUp sg;
+    memset(&sg, 0, sizeof sg);
+    if (has_shared && T <= moe::kSmallRows && H % 512 == 0 && (size_t)T * H * 2 <= 128 * 1024) {
+        sg.x = xin;
+        sg.w = static_cast<const uint16_t*>(shared->w_gate_up);
+        sg.h = reinterpret_cast<uint16_t*>(ws + L.h_s);
+        sg.T = T;
+        sg.H = H;
+        sg.Is = Is;
+        // one block per remaining CU (its LDS holds the rows: one block per
+        // CU), fewer when there are fewer column pairs than blocks
+        const int free_cu = num_cu - 1 > 1 ? num_cu - 1 : 1;
+        sg.blocks = Is < free_cu ? (Is > 0 ? Is : 1) : free_cu;
+    }
     if (T <= 16) {
-        // one block: top-k (a wave per row) and the dispatch
+        // block 0: top-k (a wave per row) and the dispatch
         mark(MOE_EV_DISPATCH);
         moe::launch_topk_dispatch_small(logits, sel_bias, sigmoid, E, wts, ids, T, topk, band_lo, band_hi, has_shared, counts,
                                         offsets, perm, pos, groups, gemv_list, mfma_list, mfma_cap,
-                                        plan_counts, st);
+                                        plan_counts, sg, st);
     } else {
         moe::launch_router_topk(logits, sel_bias, sigmoid, T, E, topk, ids, wts, st);
         mark(MOE_EV_DISPATCH);
@@ -273,6 +290,7 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
     a.y_r = out->y_picks ? out->y_picks : reinterpret_cast<float*>(ws + L.y_r);
     const bool shared_apart = has_shared && out->y_shared;
     a.y_s = shared_apart ? out->y_shared : reinterpret_cast<float*>(ws + L.y_s);
+    a.shared_gu_done = sg.blocks > 0 ? 1 : 0;
 
     // Groups on each path: a group has at most T rows (a row picks an expert
     // at most once), so with T <= 8 nothing reaches the MFMA path.
