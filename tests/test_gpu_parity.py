@@ -273,6 +273,23 @@ def test_empty_band_gives_zero_or_shared():
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "w4"])
+@pytest.mark.parametrize("Is", [192, 640])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_shared_gateup_beside_the_dispatch(T, Is, fmt):
+    # With at most 8 rows and H a multiple of 512 the shared expert's gate/up
+    # runs in the blocks of the top-k/dispatch launch beyond the first, one
+    # row-count specialisation per T; Is = 192 leaves most blocks one column
+    # pair, Is = 640 gives some waves two.  Whole layer against the oracle.
+    w = synth.Workload("sh_fused", T=T, H=1024, E=32, topk=4, I=128, Is=Is, fmt=fmt)
+    log(f"case {w}")
+    d = gpu_inputs(w)
+    side = OracleSide(w, d)
+    y, ex = run_gpu(w, d)
+    check_routing(ex, side, 0, w.E)
+    compare(y, side.layer(list(range(w.T)), 0, w.E), f"shared beside the dispatch T={T} Is={Is}/{fmt}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "w4"])
 @pytest.mark.parametrize("T", [16, 17])
 def test_small_batch_topk_dispatch_boundary(T, fmt):
     # Up to 16 rows the top-k and the dispatch run in one block, with the
