@@ -312,9 +312,9 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(
 // The shared expert's gate/up for NR rows in one block of 16 waves: each wave
 // takes gate/up column pairs c = wave * nblocks + block, then c + 16 nblocks,
 // ... (so every block has work when the columns are few), with the rows staged
-// in LDS.  A wave's first weight loads are issued before the staging and its
-// barrier, and each next column's first loads before the current column's
-// lane sums.  A column's two dots follow the GEMV path's order: lane l
+// in LDS by direct global->LDS loads issued ahead of the weights.  A wave's
+// first weight loads are issued before the staging's wait and barrier, and
+// each next column's first loads before the current column's lane sums.  A column's two dots follow the GEMV path's order: lane l
 // accumulates the inputs 512 q + 8 l .. +7 over q = 0, 1, .. (dot2 pairs in
 // order), then the lanes are summed by wave_sum.
 template <int NR>
@@ -337,14 +337,26 @@ __device__ void shared_gateup_rows(const SharedGateUp& s, int block, int nblocks
         }
     };
     int c = wave * nblocks + block;
-    const int step = nblocks * (int)(blockDim.x >> 6);
-    if (c < s.Is) issue(c, 0);
-    for (int idx = tid; idx < NR * c8n; idx += blockDim.x) {
-        const int r = idx / c8n, c8 = idx - r * c8n;
-        *reinterpret_cast<uint4*>(xs + (size_t)r * H + 8 * c8) =
-            *reinterpret_cast<const uint4*>(s.x + (size_t)r * H + 8 * c8);
+    const int nwaves = blockDim.x >> 6;
+    const int step = nblocks * nwaves;
+    // The rows (contiguous, NR * H / 8 16-byte chunks: a multiple of 64 since
+    // H is a multiple of 512) go straight to LDS, 64 chunks per wave load,
+    // before the weight loads; each wave then waits until only its weight
+    // loads are in flight (loads return in issue order), and a plain barrier
+    // (no fence: it would wait for the weights too) makes the rows visible.
+    typedef __attribute__((address_space(3))) unsigned char lds_byte;
+    lds_byte* xl8 = (lds_byte*)xs4;
+    for (int c0 = 64 * wave; c0 < NR * c8n; c0 += 64 * nwaves)
+        __builtin_amdgcn_global_load_lds(s.x + (size_t)(c0 + lane) * 8, xl8 + (size_t)c0 * 16, 16, 0, 0);
+    const bool first = c < s.Is;
+    if (first) {
+        issue(c, 0);
+        // (0xf << 8) | (7 << 4): lgkm and exp counts unconstrained; vmcnt 2 QB
+        __builtin_amdgcn_s_waitcnt((2 * QB & 0xf) | (0x7 << 4) | (0xf << 8) | (((2 * QB) >> 4) << 14));
+    } else {
+        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
     }
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
     const uint16_t* xl = xs + 8 * lane;
     while (c < s.Is) {
         float ag[NR], au[NR];
