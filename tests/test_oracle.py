@@ -303,6 +303,104 @@ def test_w4_codes_one_above_zero_give_group_scale():
     assert torch.equal(m, s[0].double().repeat_interleave(32, dim=1))
 
 
+# The down projection [H, I] decodes the same way along I.  Its codes, scales
+# and zeros are drawn apart from the gate/up ones (other seeds, other
+# values), so a down matrix read through the gate/up arrays, or with the
+# scale and zero swapped, fails these.
+
+def _w4_both(H, I, gu, dn):
+    """4-bit experts (E = 1) with gate/up (q, s, z) = gu over [2I, H] and down
+    (q, s, z) = dn over [H, I]."""
+    return {"fmt": "w4", "q_gate_up": _pack(gu[0]), "s_gate_up": gu[1], "z_gate_up": gu[2],
+            "q_down": _pack(dn[0]), "s_down": dn[1], "z_down": dn[2]}
+
+
+def _w4_noise(N, K, g):
+    q = torch.randint(0, 16, (1, N, K), generator=g)
+    s = bf16(torch.rand(1, N, K // 32, generator=g) * 0.015 + 0.005)
+    z = bf16(torch.rand(1, N, K // 32, generator=g) * 2 + 7)
+    return q, s, z
+
+
+def test_w4_down_unit_scale_zero_offset_is_codes():
+    # s = 1, z = 0 on the down matrix: it is its codes, in input (I) order.
+    H, I = 64, 96
+    g = torch.Generator().manual_seed(21)
+    q = torch.randint(0, 16, (1, H, I), generator=g)
+    dn = (q, bf16(torch.ones(1, H, I // 32)), bf16(torch.zeros(1, H, I // 32)))
+    ex = orc.Experts(_w4_both(H, I, _w4_noise(2 * I, H, g), dn), 1, H, I)
+    assert torch.equal(orc.expert_matrix(ex, 0, 1), q[0].double())
+
+
+def test_w4_down_codes_equal_zero_points_vanish():
+    H, I = 64, 128
+    g = torch.Generator().manual_seed(22)
+    zint = torch.randint(0, 16, (1, H, I // 32), generator=g)
+    dn = (zint.repeat_interleave(32, dim=2), bf16(torch.full((1, H, I // 32), 0.01)), bf16(zint.float()))
+    ex = orc.Experts(_w4_both(H, I, _w4_noise(2 * I, H, g), dn), 1, H, I)
+    assert (orc.expert_matrix(ex, 0, 1) == 0).all()
+    # ... while the gate/up matrix of the same experts is not zero
+    assert (orc.expert_matrix(ex, 0, 0) != 0).any()
+
+
+def test_w4_down_codes_one_above_zero_give_group_scale():
+    H, I = 64, 128
+    g = torch.Generator().manual_seed(23)
+    zint = torch.randint(0, 15, (1, H, I // 32), generator=g)
+    s = bf16(torch.rand(1, H, I // 32, generator=g) * 0.015 + 0.005)
+    dn = ((zint + 1).repeat_interleave(32, dim=2), s, bf16(zint.float()))
+    ex = orc.Experts(_w4_both(H, I, _w4_noise(2 * I, H, g), dn), 1, H, I)
+    assert torch.equal(orc.expert_matrix(ex, 0, 1), s[0].double().repeat_interleave(32, dim=1))
+
+
+def test_w4_scale_and_zero_not_interchangeable():
+    # One group of each matrix with scale 2 and zero 3: code 7 decodes to
+    # (7 - 3) * 2 = 8, where a swapped pair would give (7 - 2) * 3 = 15.
+    H, I = 256, 64
+    q_gu = torch.full((1, 2 * I, H), 7)
+    q_dn = torch.full((1, H, I), 7)
+    gu = (q_gu, bf16(torch.full((1, 2 * I, H // 32), 2.0)), bf16(torch.full((1, 2 * I, H // 32), 3.0)))
+    dn = (q_dn, bf16(torch.full((1, H, I // 32), 2.0)), bf16(torch.full((1, H, I // 32), 3.0)))
+    ex = orc.Experts(_w4_both(H, I, gu, dn), 1, H, I)
+    assert (orc.expert_matrix(ex, 0, 0) == 8.0).all()
+    assert (orc.expert_matrix(ex, 0, 1) == 8.0).all()
+
+
+def _w4_onehot(N, K, pick, zint, s):
+    """4-bit [1, N, K] matrix whose row n is s[n] at input pick[n] and 0
+    elsewhere: codes equal the (integer) zero everywhere except zero + 1 at
+    pick[n]; scale s[n] and zero zint[n] on every group of row n."""
+    q = zint[:, None].repeat(1, K).clone()
+    q[torch.arange(N), pick] += 1
+    return (q[None], bf16(s[:, None].repeat(1, K // 32)[None]),
+            bf16(zint[:, None].repeat(1, K // 32).float()[None]))
+
+
+def test_w4_expert_ffn_closed_form_through_both_matrices():
+    # Gate row i = a_i e_{pg[i]}, up row i = b_i e_{pu[i]}, down row c =
+    # d_c e_{sigma[c]}, all as 4-bit codes one above an integer zero:
+    # y[c] = d_c silu(a_s x[pg[s]]) b_s x[pu[s]], s = sigma[c].  This runs the
+    # down decode through the expert FFN itself (a down matrix read as the
+    # gate/up one, transposed, or with its scale from the wrong group fails).
+    H, I = 256, 64
+    g = torch.Generator().manual_seed(24)
+    pg, pu = torch.randint(0, H, (I,), generator=g), torch.randint(0, H, (I,), generator=g)
+    sigma = torch.randint(0, I, (H,), generator=g)
+    sc = bf16(torch.rand(2 * I + H, generator=g) * 0.75 + 0.25).float()
+    zi = torch.randint(0, 15, (2 * I + H,), generator=g)
+    gu = _w4_onehot(2 * I, H, torch.cat([pg, pu]), zi[:2 * I], sc[:2 * I])
+    dn = _w4_onehot(H, I, sigma, zi[2 * I:], sc[2 * I:])
+    ex = orc.Experts(_w4_both(H, I, gu, dn), 1, H, I)
+    x = bf16(torch.randn(H, generator=g)).double()
+    y = orc.expert_ffn(x, ex, 0)
+    for c in range(H):
+        s_ = int(sigma[c])
+        gate = float(sc[s_]) * float(x[pg[s_]])
+        up = float(sc[I + s_]) * float(x[pu[s_]])
+        ref = float(sc[2 * I + c]) * _silu(gate) * up
+        assert y[c].item() == pytest.approx(ref, rel=1e-14, abs=1e-300)
+
+
 # --------------------------------------------------------------------------
 # The whole layer on constructed weights (closed form), and the band gates.
 # --------------------------------------------------------------------------
