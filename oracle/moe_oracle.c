@@ -604,90 +604,140 @@ static int layer_rows(const uint16_t* x, int T, int H, const float* wr, const fl
     if (use_band && (lo < 0 || hi > E || lo >= hi)) return OR_EINVAL;
     if (!rows && nrows != T) return OR_EINVAL;
     int status = OR_OK;
-#pragma omp parallel
-    {
-        float* xf = (float*)malloc(sizeof(float) * (size_t)H);
-        double* xd = (double*)malloc(sizeof(double) * (size_t)H);
-        double* xres = (double*)malloc(sizeof(double) * (size_t)H);
-        float* l = (float*)malloc(sizeof(float) * (size_t)E);
-        int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
-        double* w = (double*)malloc(sizeof(double) * (size_t)k);
-        double* y = (double*)malloc(sizeof(double) * (size_t)H);
-        double* leaf = (double*)malloc(sizeof(double) * (size_t)k * H);
-        int32_t* leaf_id = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
-        double* col = (double*)malloc(sizeof(double) * (size_t)k);
-#pragma omp for schedule(dynamic, 1)
-        for (int r = 0; r < nrows; ++r) {
-            int t = rows ? rows[r] : r;
-            if (t < 0 || t >= T) {
-#pragma omp atomic write
-                status = OR_EINVAL;
-                continue;
-            }
-            for (int c = 0; c < H; ++c) xf[c] = bf16_to_f32(x[(size_t)t * H + c]);
-            if (gamma) {
-                /* the layer sees the normed rows; the residual is the raw row */
-                float r = rms_inv(xf, H, eps);
-                for (int c = 0; c < H; ++c) {
-                    xres[c] = (double)xf[c];
-                    float v = xf[c] * r;
-                    v = v * bf16_to_f32(gamma[c]);
-                    xf[c] = bf16_to_f32(f32_to_bf16_rne(v));
-                }
-            } else {
-                for (int c = 0; c < H; ++c) xres[c] = (double)xf[c];
-            }
-            for (int c = 0; c < H; ++c) xd[c] = (double)xf[c];
-            for (int e = 0; e < E; ++e) {
-                float v = oracle_dot_r(xf, wr + (size_t)e * H, H);
-                if (bias && router == 0) v = v + bias[e];
-                if (v == 0.0f) v = 0.0f;
-                l[e] = v;
-            }
-            if (router == 0)
-                topk_row(l, E, k, ids, w);
-            else
-                topk_sigmoid_row(l, bias, E, k, ids, w);
-            double* acc = out + (size_t)r * H;
-            for (int c = 0; c < H; ++c) acc[c] = 0.0;
-            int m = 0;
-            for (int j = 0; j < k; ++j) {
-                if (use_band && (ids[j] < lo || ids[j] >= hi)) continue;
-                oracle_expert_ffn(xd, ex, ids[j], y);
-                if (combine == 0) {
-                    for (int c = 0; c < H; ++c) acc[c] += w[j] * y[c];
-                } else {
-                    for (int c = 0; c < H; ++c) leaf[(size_t)m * H + c] = w[j] * y[c];
-                    leaf_id[m++] = ids[j];
-                }
-            }
-            if (combine == 1)
-                for (int c = 0; c < H; ++c) {
-                    for (int i = 0; i < m; ++i) col[i] = leaf[(size_t)i * H + c];
-                    acc[c] = tree_value_d(node_lo, node_lev, leaf_id, col, m);
-                }
-            if (sh_wgu && sh_wd) {
-                shared_ffn(xd, sh_wgu, sh_wd, H, Is, y);
-                for (int c = 0; c < H; ++c) acc[c] += y[c];
-            }
-            if (residual)
-                for (int c = 0; c < H; ++c) acc[c] += xres[c];
-            if (ids_out)
-                for (int j = 0; j < k; ++j) ids_out[(size_t)r * k + j] = ids[j];
-            if (w_out)
-                for (int j = 0; j < k; ++j) w_out[(size_t)r * k + j] = w[j];
-        }
-        free(xf);
-        free(xd);
-        free(xres);
-        free(l);
-        free(ids);
-        free(w);
-        free(y);
-        free(leaf);
-        free(leaf_id);
-        free(col);
+    for (int r = 0; r < nrows; ++r) {
+        int t = rows ? rows[r] : r;
+        if (t < 0 || t >= T) return OR_EINVAL;
     }
+    /* Three steps per chunk of rows, each a plain loop that OpenMP spreads
+     * over the host's cores: (1) per row, the normed row, the logits and the
+     * picks; (2) per (row, in-band pick) and per (row, shared expert), that
+     * expert's FFN on the row -- so a few rows still keep every core busy;
+     * (3) per row, the weighted sum in pick order (or along the tree), then
+     * the shared expert, then the residual.  The arithmetic of each output is
+     * the same as a row-at-a-time loop would do, in the same order. */
+    const int slots = k + 1; /* the row's picks, then its shared expert */
+    int chunk = (int)((size_t)(64u << 20) / ((size_t)slots * (size_t)H * sizeof(double)));
+    if (chunk < 1) chunk = 1;
+    if (chunk > nrows) chunk = nrows > 0 ? nrows : 1;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)chunk * H);
+    double* xres = (double*)malloc(sizeof(double) * (size_t)chunk * H);
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)chunk * k);
+    double* w = (double*)malloc(sizeof(double) * (size_t)chunk * k);
+    double* ys = (double*)malloc(sizeof(double) * (size_t)chunk * slots * H);
+    int32_t* task = (int32_t*)malloc(sizeof(int32_t) * (size_t)chunk * slots);
+    const int has_shared = sh_wgu && sh_wd;
+    for (int r0 = 0; r0 < nrows; r0 += chunk) {
+        const int nr = nrows - r0 < chunk ? nrows - r0 : chunk;
+        /* (1) routing */
+#pragma omp parallel
+        {
+            float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+            float* l = (float*)malloc(sizeof(float) * (size_t)E);
+#pragma omp for schedule(dynamic, 1)
+            for (int i = 0; i < nr; ++i) {
+                int t = rows ? rows[r0 + i] : r0 + i;
+                double* xdi = xd + (size_t)i * H;
+                double* xri = xres + (size_t)i * H;
+                for (int c = 0; c < H; ++c) xf[c] = bf16_to_f32(x[(size_t)t * H + c]);
+                if (gamma) {
+                    /* the layer sees the normed rows; the residual is the raw row */
+                    float ri = rms_inv(xf, H, eps);
+                    for (int c = 0; c < H; ++c) {
+                        xri[c] = (double)xf[c];
+                        float v = xf[c] * ri;
+                        v = v * bf16_to_f32(gamma[c]);
+                        xf[c] = bf16_to_f32(f32_to_bf16_rne(v));
+                    }
+                } else {
+                    for (int c = 0; c < H; ++c) xri[c] = (double)xf[c];
+                }
+                for (int c = 0; c < H; ++c) xdi[c] = (double)xf[c];
+                for (int e = 0; e < E; ++e) {
+                    float v = oracle_dot_r(xf, wr + (size_t)e * H, H);
+                    if (bias && router == 0) v = v + bias[e];
+                    if (v == 0.0f) v = 0.0f;
+                    l[e] = v;
+                }
+                if (router == 0)
+                    topk_row(l, E, k, ids + (size_t)i * k, w + (size_t)i * k);
+                else
+                    topk_sigmoid_row(l, bias, E, k, ids + (size_t)i * k, w + (size_t)i * k);
+            }
+            free(xf);
+            free(l);
+        }
+        /* (2) one expert FFN per task: slot j < k is pick j (when in the
+         * band), slot k the shared expert */
+        int ntask = 0;
+        for (int i = 0; i < nr; ++i)
+            for (int j = 0; j < slots; ++j) {
+                if (j < k) {
+                    int e = ids[(size_t)i * k + j];
+                    if (use_band && (e < lo || e >= hi)) continue;
+                } else if (!has_shared) {
+                    continue;
+                }
+                task[ntask++] = i * slots + j;
+            }
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int q = 0; q < ntask; ++q) {
+            int i = task[q] / slots, j = task[q] % slots;
+            double* y = ys + (size_t)task[q] * H;
+            if (j < k)
+                oracle_expert_ffn(xd + (size_t)i * H, ex, ids[(size_t)i * k + j], y);
+            else
+                shared_ffn(xd + (size_t)i * H, sh_wgu, sh_wd, H, Is, y);
+        }
+        /* (3) the sums */
+#pragma omp parallel
+        {
+            double* leaf = (double*)malloc(sizeof(double) * (size_t)k * H);
+            int32_t* leaf_id = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+            double* col = (double*)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+            for (int i = 0; i < nr; ++i) {
+                const int32_t* idi = ids + (size_t)i * k;
+                const double* wi = w + (size_t)i * k;
+                double* acc = out + (size_t)(r0 + i) * H;
+                for (int c = 0; c < H; ++c) acc[c] = 0.0;
+                int m = 0;
+                for (int j = 0; j < k; ++j) {
+                    if (use_band && (idi[j] < lo || idi[j] >= hi)) continue;
+                    const double* y = ys + ((size_t)i * slots + j) * H;
+                    if (combine == 0) {
+                        for (int c = 0; c < H; ++c) acc[c] += wi[j] * y[c];
+                    } else {
+                        for (int c = 0; c < H; ++c) leaf[(size_t)m * H + c] = wi[j] * y[c];
+                        leaf_id[m++] = idi[j];
+                    }
+                }
+                if (combine == 1)
+                    for (int c = 0; c < H; ++c) {
+                        for (int q = 0; q < m; ++q) col[q] = leaf[(size_t)q * H + c];
+                        acc[c] = tree_value_d(node_lo, node_lev, leaf_id, col, m);
+                    }
+                if (has_shared) {
+                    const double* y = ys + ((size_t)i * slots + k) * H;
+                    for (int c = 0; c < H; ++c) acc[c] += y[c];
+                }
+                if (residual)
+                    for (int c = 0; c < H; ++c) acc[c] += xres[(size_t)i * H + c];
+                if (ids_out)
+                    for (int j = 0; j < k; ++j) ids_out[(size_t)(r0 + i) * k + j] = idi[j];
+                if (w_out)
+                    for (int j = 0; j < k; ++j) w_out[(size_t)(r0 + i) * k + j] = wi[j];
+            }
+            free(leaf);
+            free(leaf_id);
+            free(col);
+        }
+    }
+    free(xd);
+    free(xres);
+    free(ids);
+    free(w);
+    free(ys);
+    free(task);
     return status;
 }
 
