@@ -56,8 +56,11 @@
  * is a run of such nodes.
  *
  * Memory: every pointer is device memory owned by the caller, contiguous
- * row-major, 16-byte aligned.  The library never allocates device memory and
- * keeps no mutable global state; scratch lives in the caller's workspace.
+ * row-major, 16-byte aligned.  The library never allocates device memory;
+ * scratch lives in the caller's workspace.  Its only host-side state is
+ * per device and under a lock: the device's properties and the dynamic-LDS
+ * limit set per kernel and device
+ * (hipFuncSetAttribute, called again only for a larger size).
  * Execution: all work is enqueued asynchronously on `stream`; nothing is
  * copied back to the host and nothing waits for the GPU.  Calls on different
  * streams need different workspaces.

@@ -133,12 +133,14 @@ __device__ __forceinline__ uint4 wload(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Allow a kernel more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU).
+// Allow a kernel more than 64 KiB of dynamic LDS (gfx950 has 160 KiB per
+// CU): the attribute is raised only when a call needs more than was set
+// before for that kernel on this device (a host-side table, moe_ffn.cpp),
+// so the steady state makes no runtime call.
+void allow_lds_once(const void* kernel, size_t bytes);
 template <typename F>
 inline void allow_lds(F* kernel, size_t bytes) {
-    if (bytes > 64 * 1024)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (bytes > 64 * 1024) allow_lds_once(reinterpret_cast<const void*>(kernel), bytes);
 }
 
 // Host-side launchers (one per kernel family).

@@ -97,6 +97,17 @@ int32_t device_info(int* num_cu) {
     return MOE_OK;
 }
 
+// Kernels whose dynamic-LDS limit was raised: the largest size set per
+// kernel and device.
+std::mutex g_lds_mu;
+struct LdsEntry {
+    const void* kernel;
+    int dev;
+    size_t bytes;
+};
+LdsEntry g_lds[64];
+int g_nlds = 0;
+
 // Level of the smallest canonical-tree node containing [lo, hi).
 int tree_level(int lo, int hi) {
     int L = 0;
@@ -105,6 +116,30 @@ int tree_level(int lo, int hi) {
 }
 
 }  // namespace
+
+namespace moe {
+
+void allow_lds_once(const void* kernel, size_t bytes) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    std::lock_guard<std::mutex> lock(g_lds_mu);
+    LdsEntry* e = nullptr;
+    for (int i = 0; i < g_nlds; ++i)
+        if (g_lds[i].kernel == kernel && g_lds[i].dev == dev) e = &g_lds[i];
+    if (e && e->bytes >= bytes) return;
+    // on failure the error stays pending and the call reports MOE_E_HIP
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) !=
+        hipSuccess)
+        return;
+    if (!e && g_nlds < 64) {
+        e = &g_lds[g_nlds++];
+        e->kernel = kernel;
+        e->dev = dev;
+    }
+    if (e) e->bytes = bytes;
+}
+
+}  // namespace moe
 
 extern "C" size_t moe_ffn_workspace_bytes(int32_t T, int32_t H, int32_t E, int32_t I, int32_t Is,
                                           int32_t topk, int32_t fmt) {
@@ -131,9 +166,12 @@ extern "C" const char* moe_ffn_strerror(int32_t code) {
     }
 }
 
-extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
-                           const moe_shared* shared, int32_t band_lo, int32_t band_hi,
-                           int32_t topk, const moe_out* out, void* stream) {
+namespace {
+
+// The layer for moe_ffn.
+int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
+                  const moe_shared* shared, int32_t band_lo, int32_t band_hi, int32_t topk,
+                  const moe_out* out, void* stream) {
     // ---- argument checks: nothing is enqueued before all of them pass ----
     if (!x || !router_w || !experts || !out) return MOE_E_NULL;
     if (!x->ptr || !router_w->w || !out->y) return MOE_E_NULL;
@@ -173,8 +211,8 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
                           bf ? nullptr : experts->s_down, bf ? nullptr : experts->z_down,
                           shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
                           out->y, out->topk_ids, out->topk_w, out->counts, out->offsets,
-                          out->perm, out->pos, out->workspace, out->y_shared, out->y_picks,
-                          x->norm_w, out->xn};
+                          out->perm, out->pos, out->workspace,
+                          out->y_shared, out->y_picks, x->norm_w, out->xn};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MOE_E_ALIGN;
 
@@ -186,10 +224,11 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
         int32_t rc = device_info(&num_cu);
         if (rc != MOE_OK) return rc;
     }
+    void* ws_base = out->workspace;
 
     // ---- enqueue ----
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    unsigned char* ws = static_cast<unsigned char*>(out->workspace);
+    unsigned char* ws = static_cast<unsigned char*>(ws_base);
     float* logits = reinterpret_cast<float*>(ws + L.logits);
     int32_t* ids = out->topk_ids ? out->topk_ids : reinterpret_cast<int32_t*>(ws + L.ids);
     float* wts = out->topk_w ? out->topk_w : reinterpret_cast<float*>(ws + L.w);
@@ -328,6 +367,14 @@ extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe
 
     if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
+                           const moe_shared* shared, int32_t band_lo, int32_t band_hi,
+                           int32_t topk, const moe_out* out, void* stream) {
+    return run_layer(x, router_w, experts, shared, band_lo, band_hi, topk, out, stream);
 }
 
 extern "C" int32_t moe_ffn_reduce(const float* const* parts, int32_t nparts, const int32_t* band_lo,
