@@ -219,11 +219,211 @@ def cpu_baseline(w, d, ex, rows_budget, min_seconds=10.0, modes=None):
                     break
     except OSError:
         pass
-    return {"value": round(reps * len(rows) / dt, 3), "unit": "rows/s", "cores": min(threads, len(rows)),
+    # the oracle's widest step runs one expert FFN per (row, in-band pick)
+    # and per (row, shared expert), spread over the OpenMP threads
+    ids = ex["topk_ids"][: len(rows)].cpu()
+    tasks = int(((ids >= w.band_lo) & (ids < w.band_hi)).sum()) + (len(rows) if w.Is else 0)
+    return {"value": round(reps * len(rows) / dt, 3), "unit": "rows/s", "cores": min(threads, tasks),
             "threads_available": threads, "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model,
             "kind": "oracle",
             "sample": f"rows 0..{len(rows) - 1} of the {w.name} workload, run {reps} times "
-                      f"(fp64 per-row oracle, OpenMP over rows), {dt:.2f} s"}
+                      f"(fp64 oracle: routing per row, then {tasks} expert FFNs, one per "
+                      f"(row, pick) and per (row, shared expert), OpenMP over them), {dt:.2f} s"}
+
+
+def layer_work(w, counts):
+    """Algorithmic HBM bytes and flops of one whole layer call: each touched
+    in-band expert's weights once, the shared expert's, the router weight
+    (and bias), the rows read and the fp32 output written; flops 2*3*H*I per
+    in-band pick and 2*3*H*Is per shared row (the fp32 router's 2*T*E*H
+    apart)."""
+    from synth import expert_bytes, shared_bytes
+
+    n_touched = int((counts > 0).sum())
+    routed = int(counts.sum())
+    nbytes = (n_touched * expert_bytes(w) + shared_bytes(w) + w.E * w.H * 4 + w.T * w.H * 2 +
+              w.T * w.H * 4)
+    flops = 6.0 * w.H * w.I * routed + (6.0 * w.H * w.Is * w.T if w.Is else 0.0)
+    return nbytes, flops
+
+
+def layer_roofline(w, counts, ms):
+    nbytes, flops = layer_work(w, counts)
+    sec = ms * 1e-3
+    t_floor = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    return {"algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "GB_per_s": round(nbytes / sec / 1e9, 1), "hbm_frac": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOP_per_s": round(flops / sec / 1e12, 1),
+            "mfma_frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "floor_us": round(t_floor * 1e6, 2), "frac_of_floor": round(t_floor / sec, 4)}
+
+
+class Runner:
+    """Times whole-layer calls of one workload on the current stream: an
+    eviction read before every call, HIP events on the launch stream around
+    the call itself, and a separate set of calls with the library's stage
+    events for the per-stage breakdown."""
+
+    def __init__(self, args, hip, flush):
+        self.args, self.hip, self.flush = args, hip, flush
+
+    def evict(self):
+        import torch  # noqa: F401
+
+        if self.args.flush == "read":
+            self.flush.sum()  # reads 1 GiB, writes one scalar
+        elif self.args.flush == "write":
+            self.flush.fill_(1)
+
+    def run(self, w, d, opts, steps, warmup, band=None, ws=None, out=None, exports=True):
+        import torch
+
+        import mixture_experts_ffn_06_amd as moe
+
+        lo, hi = band if band is not None else (w.band_lo, w.band_hi)
+        dev = d["x"].device
+        stream = torch.cuda.current_stream(dev)
+        if out is None:
+            out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+        if ws is None:
+            ws = torch.empty((moe.workspace_bytes(w.T, w.H, w.E, w.I, w.Is, w.topk,
+                                                  0 if w.fmt == "bf16" else 1),),
+                             dtype=torch.uint8, device=dev)
+        ex = {} if exports else None
+
+        def call(**kw):
+            moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], lo, hi, w.topk,
+                        out=out, workspace=ws, **opts, **kw)
+
+        self.evict()
+        call(exports=ex)  # also exports the routing, for the roofline bookkeeping
+        for _ in range(warmup):
+            self.evict()
+            call()
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.evict()
+            starts[i].record(stream)
+            call()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        layer_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+        nstage = min(steps, 10)
+        ev = [self.hip.events(moe.MOE_NUM_EVENTS) for _ in range(nstage)]
+        for i in range(nstage):
+            self.evict()
+            call(events=ev[i])
+        torch.cuda.synchronize()
+        names = moe.EVENT_SLOTS
+        stage = {n: 0.0 for n in names[:-1]}
+        for i in range(nstage):
+            for s_ in range(len(names) - 1):
+                stage[names[s_]] += self.hip.elapsed_ms(ev[i][s_], ev[i][s_ + 1]) / nstage
+        return {"ms": sum(layer_ms) / len(layer_ms), "ms_min": min(layer_ms), "wall": wall,
+                "stage": stage, "ex": ex, "out": out, "ws": ws}
+
+
+def summary(w, r, counted=True):
+    """The compact per-workload object: time, rows/s, the whole layer against
+    its roofline, and the gate/up launches (the dominant kernel)."""
+    counts = r["ex"]["counts"].cpu()
+    roof = roofline_for(w, counts, r["stage"], counted=counted)
+    return {"us_per_layer": round(r["ms"] * 1e3, 2), "rows_per_s": round(w.T / (r["ms"] * 1e-3), 1),
+            "config": {"T": w.T, "H": w.H, "E": w.E, "topk": w.topk, "I": w.I, "Is": w.Is,
+                       "fmt": w.fmt, "band": [w.band_lo, w.band_hi], "bias": w.bias},
+            "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage"].items()},
+            "layer": layer_roofline(w, counts, r["ms"]),
+            "gate_up": {k: roof[k] for k in ("kernel", "kernel_us", "bound", "achieved", "unit", "frac",
+                                             "traffic", "algorithmic_bytes", "algorithmic_flops")}
+            | {"mfma_frac": roof["mfma"]["frac"]}}
+
+
+def extra_workloads(runner, d_bf16, dev, args):
+    """Every other workload of the set at its full size, timed in the same
+    process after the headline: prefill (its own object), the expert bands
+    (one after another, then the exchange step), the adversarial band case,
+    the compute-bound shared-expert probe, and the 4-bit experts at 1 and
+    2048 rows.  The bf16 workloads share the decode workload's experts (same
+    seeds and shapes); the 4-bit ones are drawn after those are freed."""
+    import torch
+
+    import mixture_experts_ffn_06_amd as moe
+    import synth
+
+    W = synth.WORKLOADS
+    steps, warmup = max(3, args.steps // 2), 2
+    res = {}
+
+    def inputs(w):
+        base = W["decode"]
+        assert (w.E, w.H, w.I, w.Is, w.fmt, w.seed) == (base.E, base.H, base.I, base.Is, base.fmt, base.seed)
+        d = synth.make_router(w, dev)
+        d["experts"], d["shared"] = d_bf16["experts"], d_bf16["shared"]
+        return d
+
+    # prefill, the probe
+    for name in ("prefill", "shared_probe"):
+        w = W[name]
+        print(f"bench: {name}", file=sys.stderr, flush=True)
+        r = runner.run(w, inputs(w), {}, steps, warmup)
+        res[name] = summary(w, r)
+        del r
+        torch.cuda.empty_cache()
+
+    # bands: the full band, then the 8 bands one after another and their sum
+    for name in ("bands", "bands_adversarial"):
+        w = W[name]
+        print(f"bench: {name}", file=sys.stderr, flush=True)
+        d = inputs(w)
+        r = runner.run(w, d, {}, steps, warmup)
+        o = summary(w, r)
+        per_band = []
+        parts = []
+        for b, (lo, hi) in enumerate(synth.bands(w)):
+            dd = dict(d)
+            if b > 0:
+                dd["shared"] = None  # the shared expert is band 0's
+            rb = runner.run(w, dd, {}, steps, warmup, band=(lo, hi), ws=r["ws"], exports=False)
+            per_band.append(round(rb["ms"] * 1e3, 2))
+            parts.append(rb["out"])
+        # the exchange step on one GPU: the 8 partials added in rank order
+        red_ms = []
+        for i in range(steps + 2):
+            runner.evict()
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            moe.reduce(parts, "rank")
+            b_.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                red_ms.append(a.elapsed_time(b_))
+        o["band_us"] = per_band
+        o["bands_sum_us"] = round(sum(per_band), 2)
+        o["reduce_rank_order_us"] = round(sum(red_ms) / len(red_ms) * 1e3, 2)
+        res[name] = o
+        del r, parts, d
+        torch.cuda.empty_cache()
+
+    # 4-bit experts (the bf16 ones are freed first)
+    d_bf16.clear()
+    torch.cuda.empty_cache()
+    w4 = None
+    for name in ("w4_t1", "w4_t2048"):
+        w = W[name]
+        print(f"bench: {name}", file=sys.stderr, flush=True)
+        d = synth.make_router(w, dev)
+        if w4 is None:
+            w4 = {"experts": synth.make_experts(w, dev), "shared": synth.make_shared(w, dev)}
+        d.update(w4)
+        r = runner.run(w, d, {}, steps if w.T > 1 else args.steps, warmup)
+        res[name] = summary(w, r)
+        del r
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -235,6 +435,9 @@ def main():
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="how L2 and MALL are evicted before each step (1 GiB scratch read or write)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --workload (by default the decode headline is followed by "
+                         "every other workload at full size, each in an object of the same line)")
     ap.add_argument("--cpu-rows", type=int, default=8)
     ap.add_argument("--combine", choices=["pick", "tree"], default="pick",
                     help="order of the routed sum: pick order or the canonical tree over expert ids")
@@ -310,81 +513,53 @@ def main():
 
     hip = Hip()
     stream = torch.cuda.current_stream(dev)
-    out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
-    ws = torch.empty((moe.workspace_bytes(w.T, w.H, w.E, w.I, w.Is, w.topk,
-                                          0 if w.fmt == "bf16" else 1),), dtype=torch.uint8, device=dev)
     flush = torch.ones((1 << 28,), dtype=torch.int32, device=dev)  # 1 GiB
+    runner = Runner(args, hip, flush)
 
-    def evict():
-        if args.flush == "read":
-            flush.sum()  # reads 1 GiB, writes one scalar
-        elif args.flush == "write":
-            flush.fill_(1)
-    ev = [hip.events(moe.MOE_NUM_EVENTS) for _ in range(min(args.steps, 10))]
-    ex = {}
-
-    def step(events=None, exports=None):
-        evict()
-        moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
-                    w.band_hi, w.topk, out=out, workspace=ws, events=events, exports=exports,
-                    **opts)
-
-    step(exports=ex)  # also exports the routing, for the roofline bookkeeping
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Timed region: K steps; the layer itself is bracketed by events on the
-    # launch stream (the cache eviction before it is not part of the layer).
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    graph = None
     if args.graph:
-        # capture one call (after a warm-up on the capture stream); the
-        # replays below run on the same stream as the eager calls would
+        # replays of one call captured in a HIP graph (the eviction stays
+        # outside the graph), on the same stream as eager calls would run
+        out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
+        ws = torch.empty((moe.workspace_bytes(w.T, w.H, w.E, w.I, w.Is, w.topk,
+                                              0 if w.fmt == "bf16" else 1),), dtype=torch.uint8, device=dev)
+
+        def call():
+            moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
+                        w.band_hi, w.topk, out=out, workspace=ws, **opts)
         cap = torch.cuda.Stream(dev)
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
-            moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
-                        w.band_hi, w.topk, out=out, workspace=ws, **opts)
+            call()
         stream.wait_stream(cap)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
-                        w.band_hi, w.topk, out=out, workspace=ws, **opts)
+            call()
         torch.cuda.synchronize()
         for _ in range(args.warmup):
-            evict()
+            runner.evict()
             graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evict()
-        starts[i].record(stream)
-        if graph is not None:
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            runner.evict()
+            starts[i].record(stream)
             graph.replay()
-        else:
-            moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
-                        w.band_hi, w.topk, out=out, workspace=ws, **opts)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    layer_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-    ms = sum(layer_ms) / len(layer_ms)
-
-    # Per-stage breakdown (separate steps: the stage events add a little time).
-    nstage = min(args.steps, 10)
-    for i in range(nstage):
-        step(events=ev[i])
-    torch.cuda.synchronize()
-    names = moe.EVENT_SLOTS
-    stage = {n: 0.0 for n in names[:-1]}
-    for i in range(nstage):
-        for s_ in range(len(names) - 1):
-            stage[names[s_]] += hip.elapsed_ms(ev[i][s_], ev[i][s_ + 1]) / nstage
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        layer_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+        # the routing and stage breakdown come from eager calls
+        r = runner.run(w, d, opts, min(args.steps, 10), 1, ws=ws, out=out)
+        r.update({"ms": sum(layer_ms) / len(layer_ms), "ms_min": min(layer_ms), "wall": wall})
+    else:
+        r = runner.run(w, d, opts, args.steps, args.warmup)
+    ms, ex, out = r["ms"], r["ex"], r["out"]
     counts = ex["counts"].cpu()
     # the counters were taken with the default routing on the whole layer
-    roof = roofline_for(w, counts, stage, counted=args.tp == 1 and args.router == "softmax")
+    roof = roofline_for(w, counts, r["stage"], counted=args.tp == 1 and args.router == "softmax")
 
     reduce_info = None
     if args.reduce_parts:
@@ -398,7 +573,7 @@ def main():
         r_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.steps)]
         for i in range(args.steps + 2):
-            evict()
+            runner.evict()
             if i >= 2:
                 r_ev[i - 2][0].record(stream)
             moe.reduce(parts, "tree", bands=bands, E=w.E, y_shared=out, residual=d["x"], out=red)
@@ -418,9 +593,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "ms_per_step_min": round(min(layer_ms), 4),
+        "ms_per_step_min": round(r["ms_min"], 4),
         "us_per_layer": round(ms * 1e3, 2),
-        "wall_ms_per_step_incl_eviction": round(wall / args.steps * 1e3, 4),
+        "wall_ms_per_step_incl_eviction": round(r["wall"] / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -433,8 +608,9 @@ def main():
                    "norm": "rmsnorm eps 1e-5 + residual" if args.norm else None,
                    "l2_mall_eviction": {"read": "1 GiB read", "write": "1 GiB write",
                                         "none": None}[args.flush]},
-        "stage_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "stage_us": {k: round(v * 1e3, 2) for k, v in r["stage"].items()},
         "roofline": roof,
+        "layer": layer_roofline(w, counts, ms),
     }
     if reduce_info is not None:
         line["reduce"] = reduce_info
@@ -443,7 +619,14 @@ def main():
             w, d, ex, args.cpu_rows,
             modes=dict(combine=args.combine, router=args.router,
                        norm=None if gamma is None else gamma.cpu(), residual=args.norm))
-    print(json.dumps(line), flush=True)
+    plain = (args.workload == "decode" and args.tp == 1 and args.router == "softmax" and
+             not args.norm and args.combine == "pick" and not args.graph and not args.reduce_parts)
+    if plain and not args.no_extra:
+        del r, out
+        extra = extra_workloads(runner, d, dev, args)
+        line["prefill"] = extra.pop("prefill")
+        line["workloads"] = extra
+    print(json.dumps(line, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":
