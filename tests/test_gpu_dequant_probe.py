@@ -1,0 +1,103 @@
+"""Bit-exact probe of the in-kernel 4-bit dequantisation of the down
+projection, on both expert paths.
+
+[P5] "GLM-5.3-Flash and full GLM-5.3 on the native CUDA engine (tracker)
+#593", "What exists now": glue kernels are fixed byte-exactly against host
+references; "The pieces, in order": W4A16 checkpoints, weight = (code - zero)
+* scale per 32-input group.
+
+Constructed 4-bit gate/up rows make each expert's intermediate h one-hot:
+with the rows x = e_{k_t} (one-hot inputs), gate row i0 decodes to 32 at every
+input and up row i0 to 1/32, every other gate/up row to exactly 0 (codes equal
+to an integer zero point).  So g = 32, silu(32) = 32 in fp32 (exp(-32) is far
+below half an ulp of 1), h[i0] = 32 * (1/32) = 1 and h[i] = 0 elsewhere, all
+exact in bf16.  The expert output y = W_down h is then column i0 of the
+dequantised down matrix, exported through y_picks.  The down matrix keeps
+random codes, scales ~U(.005, .02) and non-integer zeros ~U(7, 9), so
+(code - zero) * scale needs up to 17 significant bits: exact in fp32.
+
+Expected, from the oracle's exact (fp64) decode of the same stored bytes:
+  groups of <= 8 rows (GEMV path): the fp32 value itself, bit for bit;
+  larger groups (MFMA path, bf16 operands): round-to-nearest-even bf16 of it.
+"""
+
+import pytest
+import torch
+
+import mixture_experts_ffn_06_amd as moe
+from gpu_common import log
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+H, E, I, K = 512, 16, 256, 4
+
+
+def _pack(q):
+    q = q.to(torch.int32)
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).to(torch.uint8)
+
+
+def _inputs(T, i0, seed):
+    g = torch.Generator().manual_seed(seed)
+    # gate/up: zero point 8 everywhere, codes 8 (weight 0) except gate and up
+    # row i0[e] of every expert: codes 9 with scales 32 and 1/32
+    q_gu = torch.full((E, 2 * I, H), 8)
+    s_gu = torch.full((E, 2 * I, H // 32), 0.01)
+    for e in range(E):
+        q_gu[e, i0[e]] = 9
+        q_gu[e, I + i0[e]] = 9
+        s_gu[e, i0[e]] = 32.0
+        s_gu[e, I + i0[e]] = 1.0 / 32.0
+    z_gu = torch.full((E, 2 * I, H // 32), 8.0)
+    q_dn = torch.randint(0, 16, (E, H, I), generator=g)
+    s_dn = torch.rand(E, H, I // 32, generator=g) * 0.015 + 0.005
+    z_dn = torch.rand(E, H, I // 32, generator=g) * 2 + 7
+    bf = torch.bfloat16
+    experts = {"fmt": "w4", "q_gate_up": _pack(q_gu), "s_gate_up": s_gu.to(bf),
+               "z_gate_up": z_gu.to(bf), "q_down": _pack(q_dn), "s_down": s_dn.to(bf),
+               "z_down": z_dn.to(bf)}
+    # one-hot rows at random inputs; zero router with a bias that fixes each
+    # row's picks (experts 3, 7, 11, 14 in that order)
+    kt = torch.randint(0, H, (T,), generator=g)
+    x = torch.zeros(T, H)
+    x[torch.arange(T), kt] = 1.0
+    bias = torch.zeros(E)
+    for j, e in enumerate((3, 7, 11, 14)):
+        bias[e] = 10.0 - j
+    return x.to(bf), bias, experts
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 9, 20, 40, 100, 129, 300])
+def test_down_dequant_bit_exact(T):
+    i0 = [(37 * e + 11 * T) % I for e in range(E)]
+    x, bias, experts = _inputs(T, i0, seed=100 + T)
+    dev = "cuda"
+    xg = x.to(dev)
+    exg = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in experts.items()}
+    wr = torch.zeros(E, H, device=dev)
+    y_picks = torch.full((T * K, H), float("nan"), device=dev)
+    ex = {}
+    moe.moe_ffn(xg, wr, bias.to(dev), exg, None, 0, E, K, exports=ex, y_picks=y_picks)
+    torch.cuda.synchronize()
+    ids = ex["topk_ids"].cpu()
+    assert (ids == torch.tensor([3, 7, 11, 14], dtype=torch.int32)).all()
+    perm = ex["perm"].cpu()
+    yp = y_picks.cpu()
+    oe = orc.Experts(experts, E, H, I)
+    cols = {e: orc.expert_matrix(oe, e, 1)[:, i0[e]] for e in (3, 7, 11, 14)}
+    mfma = T > 8  # a group holds all T rows: GEMV path up to 8 rows
+    for r in range(T * K):
+        t, j = divmod(int(perm[r]), K)
+        e = int(ids[t, j])
+        exact32 = cols[e].float()
+        assert torch.equal(exact32.double(), cols[e]), "decoded value not exact in fp32"
+        want = exact32.to(torch.bfloat16).float() if mfma else exact32
+        got = yp[r]
+        if not torch.equal(got, want):
+            bad = int((got != want).sum())
+            raise AssertionError(f"T={T} pick row {r} (expert {e}, column {i0[e]}): {bad} of {H} "
+                                 f"values differ, e.g. got {got[got != want][:3].tolist()} want "
+                                 f"{want[got != want][:3].tolist()}")
+    log(f"T={T}: {T * K} pick rows x {H} values bit-exact "
+        f"({'bf16 RNE (MFMA path)' if mfma else 'fp32 (GEMV path)'})")
