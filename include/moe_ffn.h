@@ -57,9 +57,10 @@
  *
  * Memory: every pointer is device memory owned by the caller, contiguous
  * row-major, 16-byte aligned.  The library never allocates device memory;
- * scratch lives in the caller's workspace.  Its only host-side state is
- * per device and under a lock: the device's properties and the dynamic-LDS
- * limit set per kernel and device
+ * scratch lives in the caller's workspace (moe_ffn) or in one static array
+ * per GPU (moe_ffn_static).  Its only host-side state is write-once, per
+ * device and under a lock: the device's properties, the address of the
+ * static array, and the dynamic-LDS limit set per kernel and device
  * (hipFuncSetAttribute, called again only for a larger size).
  * Execution: all work is enqueued asynchronously on `stream`; nothing is
  * copied back to the host and nothing waits for the GPU.  Calls on different
@@ -94,6 +95,7 @@ extern "C" {
 #define MOE_E_DEVICE (-10)   /* the current device is not a gfx950 GPU */
 #define MOE_E_COMBINE (-11)  /* unknown combine mode or reduce order */
 #define MOE_E_ROUTER (-12)   /* unknown router mode */
+#define MOE_E_SCRATCH (-13)  /* moe_ffn_static: the sizes need more than MOE_STATIC_SCRATCH_BYTES */
 
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_PARTS 64 /* partials one moe_ffn_reduce call adds */
@@ -240,6 +242,25 @@ typedef struct moe_out {
 int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
                 const moe_shared* shared, int32_t band_lo, int32_t band_hi, int32_t topk,
                 const moe_out* out, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): moe_ffn
+ * with its scratch in a static array of MOE_STATIC_SCRATCH_BYTES bytes per
+ * GPU instead of a caller's workspace.  The array is part of the library's
+ * code object: each GPU the library runs on holds it from the first use
+ * until the process ends.  Arguments, results and errors are moe_ffn's,
+ * except that out->workspace and out->workspace_bytes are ignored and sizes
+ * whose workspace (moe_ffn_workspace_bytes) exceeds the array return
+ * MOE_E_SCRATCH before anything is enqueued.  It calls no allocating routine.
+ * Nothing in the array has to start at zero: every call writes each scratch
+ * value before reading it, so the previous call's contents do no harm.  All
+ * calls on one GPU share the array: calls that overlap on one GPU (on
+ * different streams, or from several threads without ordering) race and
+ * must be serialised by the caller. */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
+int32_t moe_ffn_static(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
+                       const moe_shared* shared, int32_t band_lo, int32_t band_hi, int32_t topk,
+                       const moe_out* out, void* stream);
 
 /* Workspace bytes a call with these sizes needs (Is = 0: no shared expert).
  * Returns 0 for sizes moe_ffn would reject. */

@@ -29,7 +29,9 @@ ERRORS = {
     0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_DIM", -4: "MOE_E_BAND",
     -5: "MOE_E_TOPK", -6: "MOE_E_FORMAT", -7: "MOE_E_WORKSPACE", -8: "MOE_E_ALIGN",
     -9: "MOE_E_HIP", -10: "MOE_E_DEVICE", -11: "MOE_E_COMBINE", -12: "MOE_E_ROUTER",
+    -13: "MOE_E_SCRATCH",
 }
+MOE_STATIC_SCRATCH_BYTES = 32 << 20
 MOE_ROUTER_SOFTMAX = 0
 MOE_ROUTER_SIGMOID = 1
 _ROUTER = {"softmax": MOE_ROUTER_SOFTMAX, "sigmoid": MOE_ROUTER_SIGMOID}
@@ -98,6 +100,8 @@ def load_library() -> ctypes.CDLL:
         lib.moe_ffn.argtypes = [ctypes.POINTER(MoeX), ctypes.POINTER(MoeRouter),
                                 ctypes.POINTER(MoeExperts), ctypes.POINTER(MoeShared), I32, I32,
                                 I32, ctypes.POINTER(MoeOut), P]
+        lib.moe_ffn_static.restype = I32
+        lib.moe_ffn_static.argtypes = lib.moe_ffn.argtypes
         lib.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
         lib.moe_ffn_workspace_bytes.argtypes = [I32] * 7
         lib.moe_ffn_strerror.restype = ctypes.c_char_p
@@ -179,6 +183,29 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
     weight (the layer runs on the normed rows, eps as given); residual: add
     the raw rows last; xn: bf16 [T,H] receiving the normed rows.
     """
+    return _layer(False, x, router_w, bias, experts, shared, band_lo, band_hi, topk, out, exports,
+                  workspace, stream, events, combine, y_shared, y_picks, router, norm, eps, residual,
+                  xn)
+
+
+def moe_ffn_static(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor],
+                   experts: dict, shared: Optional[dict], band_lo: int, band_hi: int, topk: int,
+                   out: Optional[torch.Tensor] = None, exports: Optional[dict] = None, stream=None,
+                   events=None, combine: str = "pick", y_shared: Optional[torch.Tensor] = None,
+                   y_picks: Optional[torch.Tensor] = None, router: str = "softmax",
+                   norm: Optional[torch.Tensor] = None, eps: float = 1e-5, residual: bool = False,
+                   xn: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_ffn with its scratch in the library's static per-GPU array
+    (MOE_STATIC_SCRATCH_BYTES): the library call allocates nothing.  Calls
+    that overlap on one GPU share that array and race.  Arguments as moe_ffn,
+    without a workspace; `out` and the exports are still the caller's (this
+    wrapper allocates them with torch when they are not given)."""
+    return _layer(True, x, router_w, bias, experts, shared, band_lo, band_hi, topk, out, exports,
+                  None, stream, events, combine, y_shared, y_picks, router, norm, eps, residual, xn)
+
+
+def _layer(static, x, router_w, bias, experts, shared, band_lo, band_hi, topk, out, exports,
+           workspace, stream, events, combine, y_shared, y_picks, router, norm, eps, residual, xn):
     if combine not in _COMBINE:
         raise MoeError(-11, f"combine must be one of {sorted(_COMBINE)}")
     lib = load_library()
@@ -199,7 +226,7 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
             "perm": torch.empty((T * topk,), dtype=torch.int32, device=dev),
             "pos": torch.empty((T * topk,), dtype=torch.int32, device=dev),
         }
-    if workspace is None:
+    if workspace is None and not static:
         nbytes = lib.moe_ffn_workspace_bytes(T, H, de.E, de.I, ds.Is if ds else 0, topk, de.fmt)
         workspace = torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=dev)
     ev_arr = None
@@ -207,16 +234,17 @@ def moe_ffn(x: torch.Tensor, router_w: torch.Tensor, bias: Optional[torch.Tensor
         ev_arr = (ctypes.c_void_p * MOE_NUM_EVENTS)(*events)
     dout = MoeOut(_p(out), _p(ex.get("topk_ids")), _p(ex.get("topk_w")), _p(ex.get("counts")),
                   _p(ex.get("offsets")), _p(ex.get("perm")), _p(ex.get("pos")),
-                  _p(workspace), workspace.numel(),
+                  _p(workspace), 0 if workspace is None else workspace.numel(),
                   ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
                   _p(y_shared), _p(y_picks), _COMBINE[combine], 1 if residual else 0, _p(xn))
     if stream is None:
         st = torch.cuda.current_stream(dev).cuda_stream if dev.type == "cuda" else 0
     else:
         st = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    rc = lib.moe_ffn(ctypes.byref(dx), ctypes.byref(dr), ctypes.byref(de),
-                     ctypes.byref(ds) if ds is not None else None, band_lo, band_hi, topk,
-                     ctypes.byref(dout), ctypes.c_void_p(st))
+    entry = lib.moe_ffn_static if static else lib.moe_ffn
+    rc = entry(ctypes.byref(dx), ctypes.byref(dr), ctypes.byref(de),
+               ctypes.byref(ds) if ds is not None else None, band_lo, band_hi, topk,
+               ctypes.byref(dout), ctypes.c_void_p(st))
     if rc != 0:
         raise MoeError(rc, strerror(rc))
     if exports is not None:
@@ -339,7 +367,7 @@ def tree_pieces(lo: int, hi: int, E: int):
     return out
 
 
-__all__ = ["moe_ffn", "reduce", "tree_pieces", "tp_shares", "tp_slice_experts", "tp_slice_shared", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
+__all__ = ["moe_ffn", "moe_ffn_static", "MOE_STATIC_SCRATCH_BYTES", "reduce", "tree_pieces", "tp_shares", "tp_slice_experts", "tp_slice_shared", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
            "MOE_BF16", "MOE_W4A16", "MOE_NUM_EVENTS", "EVENT_SLOTS", "make_descriptors",
            "MoeX", "MoeRouter", "MoeExperts", "MoeShared", "MoeOut", "MOE_COMBINE_PICK",
            "MOE_COMBINE_TREE", "MOE_REDUCE_RANK", "MOE_REDUCE_TREE", "MOE_MAX_PARTS",

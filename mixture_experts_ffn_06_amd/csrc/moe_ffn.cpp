@@ -97,6 +97,31 @@ int32_t device_info(int* num_cu) {
     return MOE_OK;
 }
 
+// The workspace of moe_ffn_static: one array per GPU, loaded with the code
+// object and held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: its address on each device
+// comes from hipGetSymbolAddress (static_scratch below).
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch[64];
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current.
+int32_t static_scratch(void** ptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_E_HIP;
+    if (dev < 0 || dev >= 64) return MOE_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_E_HIP;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return MOE_OK;
+}
+
 // Kernels whose dynamic-LDS limit was raised: the largest size set per
 // kernel and device.
 std::mutex g_lds_mu;
@@ -162,16 +187,18 @@ extern "C" const char* moe_ffn_strerror(int32_t code) {
         case MOE_E_DEVICE: return "the current device is not a gfx950 GPU";
         case MOE_E_COMBINE: return "unknown combine mode or reduce order";
         case MOE_E_ROUTER: return "unknown router mode";
+        case MOE_E_SCRATCH: return "sizes need more scratch than moe_ffn_static's array holds";
         default: return "unknown error code";
     }
 }
 
 namespace {
 
-// The layer for moe_ffn.
+// The layer for moe_ffn and moe_ffn_static.  static_ws: the workspace is
+// this device's `scratch` array instead of out->workspace.
 int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
                   const moe_shared* shared, int32_t band_lo, int32_t band_hi, int32_t topk,
-                  const moe_out* out, void* stream) {
+                  const moe_out* out, void* stream, bool static_ws) {
     // ---- argument checks: nothing is enqueued before all of them pass ----
     if (!x || !router_w || !experts || !out) return MOE_E_NULL;
     if (!x->ptr || !router_w->w || !out->y) return MOE_E_NULL;
@@ -211,13 +238,17 @@ int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts*
                           bf ? nullptr : experts->s_down, bf ? nullptr : experts->z_down,
                           shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
                           out->y, out->topk_ids, out->topk_w, out->counts, out->offsets,
-                          out->perm, out->pos, out->workspace,
+                          out->perm, out->pos, static_ws ? nullptr : out->workspace,
                           out->y_shared, out->y_picks, x->norm_w, out->xn};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MOE_E_ALIGN;
 
     const Layout L = make_layout(T, H, E, I, Is, topk);
-    if (!out->workspace || out->workspace_bytes < L.total) return MOE_E_WORKSPACE;
+    if (static_ws) {
+        if (L.total > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_E_SCRATCH;
+    } else if (!out->workspace || out->workspace_bytes < L.total) {
+        return MOE_E_WORKSPACE;
+    }
 
     int num_cu = 0;
     {
@@ -225,6 +256,10 @@ int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts*
         if (rc != MOE_OK) return rc;
     }
     void* ws_base = out->workspace;
+    if (static_ws) {
+        int32_t rc = static_scratch(&ws_base);
+        if (rc != MOE_OK) return rc;
+    }
 
     // ---- enqueue ----
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -374,7 +409,14 @@ int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts*
 extern "C" int32_t moe_ffn(const moe_x* x, const moe_router* router_w, const moe_experts* experts,
                            const moe_shared* shared, int32_t band_lo, int32_t band_hi,
                            int32_t topk, const moe_out* out, void* stream) {
-    return run_layer(x, router_w, experts, shared, band_lo, band_hi, topk, out, stream);
+    return run_layer(x, router_w, experts, shared, band_lo, band_hi, topk, out, stream, false);
+}
+
+extern "C" int32_t moe_ffn_static(const moe_x* x, const moe_router* router_w,
+                                  const moe_experts* experts, const moe_shared* shared,
+                                  int32_t band_lo, int32_t band_hi, int32_t topk,
+                                  const moe_out* out, void* stream) {
+    return run_layer(x, router_w, experts, shared, band_lo, band_hi, topk, out, stream, true);
 }
 
 extern "C" int32_t moe_ffn_reduce(const float* const* parts, int32_t nparts, const int32_t* band_lo,

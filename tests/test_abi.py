@@ -23,7 +23,7 @@ HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
 def test_library_exports_every_declared_symbol():
     text = open(HEADER).read()
     declared = set(re.findall(r"^\S.*?\b(moe_\w+)\s*\(", text, flags=re.M))
-    assert declared == {"moe_ffn", "moe_ffn_workspace_bytes", "moe_ffn_strerror", "moe_ffn_reduce",
+    assert declared == {"moe_ffn", "moe_ffn_static", "moe_ffn_workspace_bytes", "moe_ffn_strerror", "moe_ffn_reduce",
                         "moe_tp_shares", "moe_tp_slice_experts", "moe_tp_slice_shared"}
     out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -76,6 +76,8 @@ def test_constants_match_header():
     assert define("MOE_MAX_TOPK") == moe.MOE_MAX_TOPK
     assert define("MOE_MAX_E") == moe.MOE_MAX_E
     assert define("MOE_BF16") == moe.MOE_BF16 and define("MOE_W4A16") == moe.MOE_W4A16
+    m = re.search(r"#define MOE_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert int(m.group(1)) << int(m.group(2)) == moe.MOE_STATIC_SCRATCH_BYTES
 
 
 def test_strerror_every_code():
