@@ -583,9 +583,12 @@ __device__ __forceinline__ bf16x8_p dequant8(uint32_t c, float s, float n) {
     return __builtin_bit_cast(bf16x8_p, o);
 }
 
-template <bool GATEUP, int BM>
+// MTL: live 16-row subtiles of the tile (the group's rows past them take no
+// MFMA and no A fragment reads).
+template <bool GATEUP, int BM, int MTL>
 __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, int m0, int nt) {
     using C = W4Cfg<BM>;
+    static_assert(MTL >= 1 && MTL <= C::MT, "live subtiles");
     typedef __attribute__((address_space(3))) const uint32_t lds_u32;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -649,14 +652,14 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         issue_sz(kt / C::G + 1, 4 * (kt % C::G) + wave);
     };
 
-    f32x4_p acc[C::MT][C::NT];
+    f32x4_p acc[MTL][C::NT];
 #pragma unroll
-    for (int i = 0; i < C::MT; ++i)
+    for (int i = 0; i < MTL; ++i)
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) acc[i][j] = f32x4_p{0.f, 0.f, 0.f, 0.f};
-    int aoff[C::MT], ax[C::MT], brow[C::NT];
+    int aoff[MTL], ax[MTL], brow[C::NT];
 #pragma unroll
-    for (int i = 0; i < C::MT; ++i) {
+    for (int i = 0; i < MTL; ++i) {
         const int r = 16 * i + (lane & 15);
         aoff[i] = r * 128;
         ax[i] = r & 7;
@@ -693,7 +696,7 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         // Every LDS read of the step first (one wait), then the expansion,
         // then the MFMAs.
         uint32_t sw[C::NT], zw[C::NT], codes[2][C::NT];
-        bf16x8_p af[2][C::MT];
+        bf16x8_p af[2][MTL];
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) {
             const int off = (brow[j] / R) * 256 + (brow[j] % R) * 4;  // piece, row in piece
@@ -708,7 +711,7 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
                 codes[ks][j] = *(lds_u32*)(st + C::QOff + (brow[j] >> 5) * 1024 + (q >> 2) * 512 +
                                            (brow[j] & 31) * 16 + 4 * (q & 3));
 #pragma unroll
-            for (int i = 0; i < C::MT; ++i) af[ks][i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
+            for (int i = 0; i < MTL; ++i) af[ks][i] = *(lds_bf16x8*)(st + aoff[i] + ((q ^ ax[i]) << 4));
         }
         bf16x8_p bfr[2][C::NT];
 #pragma unroll
@@ -724,7 +727,7 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int i = 0; i < C::MT; ++i)
+            for (int i = 0; i < MTL; ++i)
 #pragma unroll
                 for (int j = 0; j < C::NT; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
@@ -734,7 +737,7 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         uint16_t* hout = a.h_r + (size_t)(g.row0 + m0) * a.I;
         const int c = nt * 64 + 16 * wave + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i)
+        for (int i = 0; i < MTL; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * i + 4 * (lane >> 4) + v;
@@ -743,7 +746,7 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     } else {
         float* yout = a.y_r + (size_t)(g.row0 + m0) * H;
 #pragma unroll
-        for (int i = 0; i < C::MT; ++i)
+        for (int i = 0; i < MTL; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * i + 4 * (lane >> 4) + v;
@@ -782,7 +785,29 @@ __global__ __launch_bounds__(W4Cfg<BM>::Threads, W4Cfg<BM>::PerCU) void expert_m
         if (g.expert < 0) continue;  // the shared expert is bf16
         const int m0 = tl[2 * tile + 1] + 128 * half;
         if (m0 >= g.n) continue;
-        pipe_tile_w4<GATEUP, BM>(a, smem, g, m0, nt);
+        // 16-row subtiles holding rows of the group (block-uniform)
+        const int live = (min(BM, g.n - m0) + 15) / 16;
+        if constexpr (BM == 128) {
+            if (live > 7)
+                pipe_tile_w4<GATEUP, BM, 8>(a, smem, g, m0, nt);
+            else if (live > 6)
+                pipe_tile_w4<GATEUP, BM, 7>(a, smem, g, m0, nt);
+            else if (live > 5)
+                pipe_tile_w4<GATEUP, BM, 6>(a, smem, g, m0, nt);
+            else if (live > 4)
+                pipe_tile_w4<GATEUP, BM, 5>(a, smem, g, m0, nt);
+            else if (live > 2)
+                pipe_tile_w4<GATEUP, BM, 4>(a, smem, g, m0, nt);
+            else
+                pipe_tile_w4<GATEUP, BM, 2>(a, smem, g, m0, nt);
+        } else if constexpr (BM == 64) {
+            if (live > 3)
+                pipe_tile_w4<GATEUP, BM, 4>(a, smem, g, m0, nt);
+            else
+                pipe_tile_w4<GATEUP, BM, 3>(a, smem, g, m0, nt);
+        } else {
+            pipe_tile_w4<GATEUP, BM, 2>(a, smem, g, m0, nt);
+        }
     }
 }
 
