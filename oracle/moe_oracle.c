@@ -465,17 +465,32 @@ int oracle_tp_shares(int dim, int unit, int ranks, int32_t* shares)
 /*       (4-bit weights, 16-bit activations) on the family; [P4] names the    */
 /*       group units.                                                         */
 /* ------------------------------------------------------------------------ */
+/* affine4: MLX's affine 4-bit format ([P5] "The pieces, in order": MLX      */
+/*       affine 4-bit checkpoints; [P4] comments: MLX's 64-input groups):     */
+/*       4-bit unsigned codes packed as above, a bf16 scale s and bias b per  */
+/*       64-wide group along k; the weight is s * q + b.                      */
+/* nvfp4: NVIDIA's NVFP4 read as stored ([P5]: NVFP4 checkpoint read as      */
+/*       stored, W4A16; [P4] comments: NVFP4's 16-input groups): each 4-bit  */
+/*       code is an FP4 E2M1 value (sign bit 3, exponent bits 2..1 with bias  */
+/*       1, mantissa bit 0; exponent 0 is subnormal: 0 or 0.5), packed two    */
+/*       per byte with the even k in the low nibble; one FP8 E4M3 scale per   */
+/*       16-wide group along k (sign, 4 exponent bits with bias 7, 3 mantissa */
+/*       bits; exponent 0 subnormal; the all-ones pattern is NaN) and one     */
+/*       fp32 scale per matrix (the gate, up and down matrices of an expert   */
+/*       each have their own); the weight is fp4(q) * e4m3(s) * g.           */
 typedef struct {
-    int32_t fmt; /* 0 = bf16, 1 = w4 (group 32) */
+    int32_t fmt; /* 0 = bf16, 1 = w4 (group 32), 2 = affine4 (group 64), 3 = nvfp4 (group 16) */
     int32_t E, H, I;
     const uint16_t* w_gate_up;
     const uint16_t* w_down;
     const uint8_t* q_gate_up;
-    const uint16_t* s_gate_up;
-    const uint16_t* z_gate_up;
+    const uint16_t* s_gate_up; /* w4 and affine4: bf16; nvfp4: E4M3 bytes */
+    const uint16_t* z_gate_up; /* w4: zero points; affine4: biases; nvfp4: unused */
     const uint8_t* q_down;
     const uint16_t* s_down;
     const uint16_t* z_down;
+    const float* g_gate_up; /* nvfp4: fp32 [E, 2] (gate, up) */
+    const float* g_down;    /* nvfp4: fp32 [E] */
 } oracle_experts;
 
 /* Row n of a [rows, K] matrix of expert e, as doubles. */
@@ -501,18 +516,71 @@ static void w4_row(const uint8_t* q, const uint16_t* s, const uint16_t* z, size_
     }
 }
 
+static int code_at(const uint8_t* qr, int k)
+{
+    uint8_t byte = qr[k / 2];
+    return (k % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+}
+
+static void affine4_row(const uint8_t* q, const uint16_t* s, const uint16_t* b, size_t rows,
+                        int K, int e, int n, double* out)
+{
+    size_t row = (size_t)e * rows + (size_t)n;
+    const uint8_t* qr = q + row * (size_t)(K / 2);
+    const uint16_t* sr = s + row * (size_t)(K / 64);
+    const uint16_t* br = b + row * (size_t)(K / 64);
+    for (int k = 0; k < K; ++k)
+        out[k] = (double)bf16_to_f32(sr[k / 64]) * (double)code_at(qr, k) +
+                 (double)bf16_to_f32(br[k / 64]);
+}
+
+/* FP4 E2M1: (-1)^sign * (exponent ? (1 + m/2) * 2^(exponent - 1) : m/2). */
+double oracle_fp4_e2m1(int code)
+{
+    int sign = (code >> 3) & 1, ex = (code >> 1) & 3, m = code & 1;
+    double mag = ex ? (1.0 + 0.5 * m) * ldexp(1.0, ex - 1) : 0.5 * m;
+    return sign ? -mag : mag;
+}
+
+/* FP8 E4M3: (-1)^sign * (exponent ? (1 + m/8) * 2^(exponent - 7) : m/8 * 2^-6);
+ * exponent 15 with mantissa 7 is NaN (there is no infinity). */
+double oracle_fp8_e4m3(int byte)
+{
+    int sign = (byte >> 7) & 1, ex = (byte >> 3) & 15, m = byte & 7;
+    if (ex == 15 && m == 7) return NAN;
+    double mag = ex ? (1.0 + m / 8.0) * ldexp(1.0, ex - 7) : (m / 8.0) * ldexp(1.0, -6);
+    return sign ? -mag : mag;
+}
+
+static void nvfp4_row(const uint8_t* q, const uint8_t* s, double g, size_t rows, int K, int e,
+                      int n, double* out)
+{
+    size_t row = (size_t)e * rows + (size_t)n;
+    const uint8_t* qr = q + row * (size_t)(K / 2);
+    const uint8_t* sr = s + row * (size_t)(K / 16);
+    for (int k = 0; k < K; ++k)
+        out[k] = oracle_fp4_e2m1(code_at(qr, k)) * oracle_fp8_e4m3(sr[k / 16]) * g;
+}
+
 static void gate_up_row(const oracle_experts* ex, int e, int n, double* out)
 {
     size_t rows = 2 * (size_t)ex->I;
     if (ex->fmt == 0) bf16_row(ex->w_gate_up, rows, ex->H, e, n, out);
-    else w4_row(ex->q_gate_up, ex->s_gate_up, ex->z_gate_up, rows, ex->H, e, n, out);
+    else if (ex->fmt == 1) w4_row(ex->q_gate_up, ex->s_gate_up, ex->z_gate_up, rows, ex->H, e, n, out);
+    else if (ex->fmt == 2)
+        affine4_row(ex->q_gate_up, ex->s_gate_up, ex->z_gate_up, rows, ex->H, e, n, out);
+    else /* the gate rows take the expert's gate scale, the up rows its up scale */
+        nvfp4_row(ex->q_gate_up, (const uint8_t*)ex->s_gate_up,
+                  (double)ex->g_gate_up[2 * (size_t)e + (n < ex->I ? 0 : 1)], rows, ex->H, e, n, out);
 }
 
 static void down_row(const oracle_experts* ex, int e, int n, double* out)
 {
     size_t rows = (size_t)ex->H;
     if (ex->fmt == 0) bf16_row(ex->w_down, rows, ex->I, e, n, out);
-    else w4_row(ex->q_down, ex->s_down, ex->z_down, rows, ex->I, e, n, out);
+    else if (ex->fmt == 1) w4_row(ex->q_down, ex->s_down, ex->z_down, rows, ex->I, e, n, out);
+    else if (ex->fmt == 2) affine4_row(ex->q_down, ex->s_down, ex->z_down, rows, ex->I, e, n, out);
+    else nvfp4_row(ex->q_down, (const uint8_t*)ex->s_down, (double)ex->g_down[e], rows, ex->I, e, n, out);
 }
 
 static double dot(const double* a, const double* b, int n)

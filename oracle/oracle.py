@@ -49,7 +49,13 @@ class _Experts(ctypes.Structure):
         ("q_down", ctypes.c_void_p),
         ("s_down", ctypes.c_void_p),
         ("z_down", ctypes.c_void_p),
+        ("g_gate_up", ctypes.c_void_p),
+        ("g_down", ctypes.c_void_p),
     ]
+
+
+# weight formats of the oracle (its own numbering)
+_FMT = {"bf16": 0, "w4": 1, "affine4": 2, "nvfp4": 3}
 
 
 _lib = None
@@ -74,6 +80,10 @@ def _load():
         lib.oracle_expert_ffn.argtypes = [P, ctypes.POINTER(_Experts), I32, P]
         lib.oracle_expert_matrix.restype = I32
         lib.oracle_expert_matrix.argtypes = [ctypes.POINTER(_Experts), I32, I32, P]
+        lib.oracle_fp4_e2m1.restype = ctypes.c_double
+        lib.oracle_fp4_e2m1.argtypes = [I32]
+        lib.oracle_fp8_e4m3.restype = ctypes.c_double
+        lib.oracle_fp8_e4m3.argtypes = [I32]
         layer = [P, I32, I32, P, P, I32, ctypes.POINTER(_Experts), P, P, I32]
         lib.oracle_moe_ffn.restype = I32
         lib.oracle_moe_ffn.argtypes = layer + [I32, I32, I32, I32, I32, P, ctypes.c_float, I32,
@@ -122,18 +132,32 @@ class Experts:
     def __init__(self, experts: dict, E: int, H: int, I: int):
         self.keep = {k: _cpu(v) for k, v in experts.items() if isinstance(v, torch.Tensor)}
         fmt = experts["fmt"]
-        want = ({"w_gate_up": (2 * I, H), "w_down": (H, I)} if fmt == "bf16" else
-                {"q_gate_up": (2 * I, H // 2), "s_gate_up": (2 * I, H // 32), "z_gate_up": (2 * I, H // 32),
-                 "q_down": (H, I // 2), "s_down": (H, I // 32), "z_down": (H, I // 32)})
+        gsz = {"w4": 32, "affine4": 64, "nvfp4": 16}.get(fmt, 0)
+        if fmt == "bf16":
+            want = {"w_gate_up": (2 * I, H), "w_down": (H, I)}
+        else:
+            want = {"q_gate_up": (2 * I, H // 2), "s_gate_up": (2 * I, H // gsz),
+                    "q_down": (H, I // 2), "s_down": (H, I // gsz)}
+            if fmt == "nvfp4":
+                want.update({"g_gate_up": (2,), "g_down": ()})
+            else:
+                want.update({"z_gate_up": (2 * I, H // gsz), "z_down": (H, I // gsz)})
         for name, shape in want.items():
             t = self.keep.get(name)
             if t is not None and (tuple(t.shape[1:]) != shape or t.shape[0] < E):
                 raise ValueError(f"oracle: {name} has shape {tuple(t.shape)}, want [{E}, {shape}]")
+        if fmt == "nvfp4":
+            for name in ("s_gate_up", "s_down"):
+                if self.keep.get(name) is not None and self.keep[name].dtype != torch.uint8:
+                    raise ValueError(f"oracle: nvfp4 {name} must be uint8 (E4M3 bytes)")
+            for name in ("g_gate_up", "g_down"):
+                if self.keep.get(name) is not None and self.keep[name].dtype != torch.float32:
+                    raise ValueError(f"oracle: nvfp4 {name} must be fp32")
         d = _Experts()
-        d.fmt = 0 if experts["fmt"] == "bf16" else 1
+        d.fmt = _FMT[fmt]
         d.E, d.H, d.I = E, H, I
         for name in ("w_gate_up", "w_down", "q_gate_up", "s_gate_up", "z_gate_up",
-                     "q_down", "s_down", "z_down"):
+                     "q_down", "s_down", "z_down", "g_gate_up", "g_down"):
             t = self.keep.get(name)
             setattr(d, name, None if t is None else t.data_ptr())
         self.desc = d
@@ -230,6 +254,16 @@ def expert_matrix(experts: Experts, e: int, which: int) -> torch.Tensor:
     return out
 
 
+def fp4_e2m1(code: int) -> float:
+    """Value of a 4-bit FP4 E2M1 code (the oracle's decode)."""
+    return float(_load().oracle_fp4_e2m1(int(code)))
+
+
+def fp8_e4m3(byte: int) -> float:
+    """Value of an FP8 E4M3 byte (the oracle's decode; NaN for the NaN codes)."""
+    return float(_load().oracle_fp8_e4m3(int(byte)))
+
+
 def tp_shares(dim: int, unit: int, ranks: int):
     """Tensor-parallel shares of dim: whole units, remainder on the lowest ranks."""
     out = torch.empty(max(ranks, 1), dtype=torch.int32)
@@ -253,13 +287,20 @@ def tp_slice(experts: dict, i_lo: int, i_hi: int) -> dict:
     q = experts["q_gate_up"]
     I = q.shape[-2] // 2
     rows = list(range(i_lo, i_hi)) + list(range(I + i_lo, I + i_hi))
-    return {"fmt": fmt,
-            "q_gate_up": q[..., rows, :].contiguous(),
-            "s_gate_up": experts["s_gate_up"][..., rows, :].contiguous(),
-            "z_gate_up": experts["z_gate_up"][..., rows, :].contiguous(),
-            "q_down": experts["q_down"][..., i_lo // 2:i_hi // 2].contiguous(),
-            "s_down": experts["s_down"][..., i_lo // 32:i_hi // 32].contiguous(),
-            "z_down": experts["z_down"][..., i_lo // 32:i_hi // 32].contiguous()}
+    gsz = {"w4": 32, "affine4": 64, "nvfp4": 16}[fmt]
+    out = {"fmt": fmt,
+           "q_gate_up": q[..., rows, :].contiguous(),
+           "s_gate_up": experts["s_gate_up"][..., rows, :].contiguous(),
+           "q_down": experts["q_down"][..., i_lo // 2:i_hi // 2].contiguous(),
+           "s_down": experts["s_down"][..., i_lo // gsz:i_hi // gsz].contiguous()}
+    if fmt == "nvfp4":
+        # the per-matrix scales are the whole matrix's: a slice keeps them
+        out["g_gate_up"] = experts["g_gate_up"].clone()
+        out["g_down"] = experts["g_down"].clone()
+    else:
+        out["z_gate_up"] = experts["z_gate_up"][..., rows, :].contiguous()
+        out["z_down"] = experts["z_down"][..., i_lo // gsz:i_hi // gsz].contiguous()
+    return out
 
 
 def tree_node(E: int, lo: int, hi: int):

@@ -24,6 +24,7 @@ import torch
 _IDX_X, _IDX_WR, _IDX_BIAS = 0, 1, 2
 _IDX_WGU, _IDX_WD, _IDX_SGU, _IDX_SD = 3, 4, 5, 6
 _IDX_QGU, _IDX_SGU4, _IDX_ZGU4, _IDX_QD, _IDX_SD4, _IDX_ZD4 = 7, 8, 9, 10, 11, 12
+_IDX_GGU, _IDX_GD = 13, 14
 
 # Scale on the log-Zipf router bias (see zipf_bias).  With this scale the
 # realised expert popularity of the prefill workload (top-8 of 256 experts,
@@ -43,7 +44,7 @@ class Workload:
     topk: int
     I: int
     Is: int  # 0 = no shared expert
-    fmt: str = "bf16"  # "bf16" | "w4"
+    fmt: str = "bf16"  # "bf16" | "w4" | "affine4" | "nvfp4"
     bias: Optional[str] = None  # None | "zipf" | "band0" | "one_expert" | "first_k"
     band: tuple = (0, 0)  # (lo, hi); hi = 0 means the full band [0, E)
     seed: int = 0
@@ -76,6 +77,13 @@ WORKLOADS = {
     ),
     "w4_t1": Workload("w4_t1", T=1, H=6144, E=256, topk=8, I=2048, Is=2048, fmt="w4"),
     "w4_t2048": Workload("w4_t2048", T=2048, H=6144, E=256, topk=8, I=2048, Is=2048, fmt="w4"),
+    # The other 4-bit checkpoint formats on the same shapes: MLX affine
+    # (64-input groups, s * q + b) and NVFP4 (E2M1 codes, an E4M3 scale per 16
+    # inputs and an fp32 scale per matrix).
+    "affine4_t1": Workload("affine4_t1", T=1, H=6144, E=256, topk=8, I=2048, Is=2048, fmt="affine4"),
+    "affine4_t2048": Workload("affine4_t2048", T=2048, H=6144, E=256, topk=8, I=2048, Is=2048, fmt="affine4"),
+    "nvfp4_t1": Workload("nvfp4_t1", T=1, H=6144, E=256, topk=8, I=2048, Is=2048, fmt="nvfp4"),
+    "nvfp4_t2048": Workload("nvfp4_t2048", T=2048, H=6144, E=256, topk=8, I=2048, Is=2048, fmt="nvfp4"),
     # Compute-bound probe: prefill sizes with every pick on experts 0..7 and
     # the band [8, 256), so no routed pick is in the band and the MFMA work
     # is the shared expert's 4096 rows alone.
@@ -130,6 +138,27 @@ def _codes_w4(shape, device, g) -> torch.Tensor:
     for e in range(E):
         q = torch.randint(0, 16, (N, K), generator=g, device=device, dtype=torch.int32)
         out[e].copy_((q[:, 0::2] | (q[:, 1::2] << 4)).to(torch.uint8))
+    return out
+
+
+def _affine_bias(scale: torch.Tensor, device, g) -> torch.Tensor:
+    """MLX affine biases: -scale * u with u ~ U(7, 9) per group (the affine
+    form of a zero point mid-range of the codes), rounded to bf16."""
+    out = torch.empty(scale.shape, dtype=torch.bfloat16, device=device)
+    for i in range(scale.shape[0]):
+        u = torch.empty(scale.shape[1:], dtype=torch.float32, device=device)
+        u.uniform_(7.0, 9.0, generator=g)
+        out[i].copy_(-scale[i].float() * u)
+    return out
+
+
+def _e4m3_bytes(shape, lo, hi, device, g) -> torch.Tensor:
+    """FP8 E4M3 bytes of values ~U(lo, hi) (rounded to nearest even), as uint8."""
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    for i in range(shape[0]):
+        u = torch.empty(shape[1:], dtype=torch.float32, device=device)
+        u.uniform_(lo, hi, generator=g)
+        out[i].copy_(u.to(torch.float8_e4m3fn).view(torch.uint8))
     return out
 
 
@@ -202,6 +231,34 @@ def make_experts(w: Workload, device="cpu") -> dict:
             "s_down": _uniform_bf16((E, H, I // 32), 0.005, 0.02, device, _gen(device, w.seed, _IDX_SD4), True),
             "z_down": _uniform_bf16((E, H, I // 32), 7.0, 9.0, device, _gen(device, w.seed, _IDX_ZD4), True),
         }
+    if w.fmt == "affine4":
+        s_gu = _uniform_bf16((E, 2 * I, H // 64), 0.005, 0.02, device, _gen(device, w.seed, _IDX_SGU4), True)
+        s_d = _uniform_bf16((E, H, I // 64), 0.005, 0.02, device, _gen(device, w.seed, _IDX_SD4), True)
+        return {
+            "fmt": "affine4",
+            "q_gate_up": _codes_w4((E, 2 * I, H), device, _gen(device, w.seed, _IDX_QGU)),
+            "s_gate_up": s_gu,
+            "z_gate_up": _affine_bias(s_gu, device, _gen(device, w.seed, _IDX_ZGU4)),
+            "q_down": _codes_w4((E, H, I), device, _gen(device, w.seed, _IDX_QD)),
+            "s_down": s_d,
+            "z_down": _affine_bias(s_d, device, _gen(device, w.seed, _IDX_ZD4)),
+        }
+    if w.fmt == "nvfp4":
+        # block scales in E4M3's normal range, per-matrix scales ~U(1/512, 1/256):
+        # weights up to 6 * 4 / 256 in magnitude
+        g_gu = torch.empty((E, 2), dtype=torch.float32, device=device)
+        g_gu.uniform_(1.0 / 512, 1.0 / 256, generator=_gen(device, w.seed, _IDX_GGU))
+        g_d = torch.empty((E,), dtype=torch.float32, device=device)
+        g_d.uniform_(1.0 / 512, 1.0 / 256, generator=_gen(device, w.seed, _IDX_GD))
+        return {
+            "fmt": "nvfp4",
+            "q_gate_up": _codes_w4((E, 2 * I, H), device, _gen(device, w.seed, _IDX_QGU)),
+            "s_gate_up": _e4m3_bytes((E, 2 * I, H // 16), 1.5, 4.0, device, _gen(device, w.seed, _IDX_SGU4)),
+            "q_down": _codes_w4((E, H, I), device, _gen(device, w.seed, _IDX_QD)),
+            "s_down": _e4m3_bytes((E, H, I // 16), 1.5, 4.0, device, _gen(device, w.seed, _IDX_SD4)),
+            "g_gate_up": g_gu,
+            "g_down": g_d,
+        }
     raise ValueError(f"unknown format {w.fmt!r}")
 
 
@@ -227,8 +284,11 @@ def expert_bytes(w: Workload) -> int:
     if w.fmt == "bf16":
         return 3 * w.H * w.I * 2
     codes = 3 * w.H * w.I // 2
-    scales = 2 * (3 * w.H * w.I // 32) * 2
-    return codes + scales
+    if w.fmt == "w4":
+        return codes + 2 * (3 * w.H * w.I // 32) * 2  # bf16 scale and zero per 32
+    if w.fmt == "affine4":
+        return codes + 2 * (3 * w.H * w.I // 64) * 2  # bf16 scale and bias per 64
+    return codes + 3 * w.H * w.I // 16 + 3 * 4  # E4M3 scale per 16, fp32 per matrix
 
 
 def shared_bytes(w: Workload) -> int:

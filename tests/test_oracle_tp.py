@@ -63,7 +63,7 @@ def _slice_inputs(d, sl):
     return dd, b - a, sb - sa
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "w4"])
+@pytest.mark.parametrize("fmt", ["bf16", "w4", "affine4", "nvfp4"])
 def test_rank_order_sum_of_slices_is_the_layer(fmt):
     # W (x) = sum over column slices of W_down[:, s] h[s]: exact in real
     # arithmetic; in fp64 the slice partials add up to the full layer up to
