@@ -100,10 +100,23 @@ def measured_traffic(workload, kernels):
     return total
 
 
+# the library's format codes, and the dtype label of each format's path
+# (bf16 activations, weights decoded from the stored form)
+FMT_CODE = {"bf16": 0, "w4": 1, "affine4": 2, "nvfp4": 3}
+FMT_DTYPE = {"bf16": "bf16", "w4": "w4a16", "affine4": "affine4a16", "nvfp4": "nvfp4a16"}
+
+
 def _expert_gu_bytes(w):
+    """Stored bytes of one expert's fused gate/up matrix (2I rows of H inputs)."""
+    rows = 2 * w.I
     if w.fmt == "bf16":
-        return 2 * w.I * w.H * 2
-    return 2 * w.I * (w.H // 2) + 2 * 2 * w.I * (w.H // 32) * 2  # codes + bf16 scales and zeros
+        return rows * w.H * 2
+    codes = rows * (w.H // 2)
+    if w.fmt == "w4":
+        return codes + rows * (w.H // 32) * 2 * 2  # bf16 scale and zero per 32 inputs
+    if w.fmt == "affine4":
+        return codes + rows * (w.H // 64) * 2 * 2  # bf16 scale and bias per 64 inputs
+    return codes + rows * (w.H // 16) + 2 * 4  # E4M3 scale per 16 inputs, two fp32 matrix scales
 
 
 def roofline_for(w, counts, stage_ms, counted=True):
@@ -131,7 +144,7 @@ def roofline_for(w, counts, stage_ms, counted=True):
     nbytes = wbytes + act
     flops = 2.0 * routed * 2 * w.I * w.H + 2.0 * sh_rows * 2 * w.Is * w.H
     if w.T <= 8:
-        kernel, ms = f"gateup_gemv_kernel<{0 if w.fmt == 'bf16' else 1},12>", stage_ms["gu_gemv"]
+        kernel, ms = f"gateup_gemv_kernel<{FMT_CODE[w.fmt]},12>", stage_ms["gu_gemv"]
         traffic = measured_traffic(w.name, [f"moe::{kernel}"])
         if w.Is and w.H % 512 == 0 and w.T * w.H * 2 <= 128 * 1024:
             # the shared expert's gate/up ran in the top-k/dispatch launch
@@ -141,7 +154,7 @@ def roofline_for(w, counts, stage_ms, counted=True):
             flops = 2.0 * routed * 2 * w.I * w.H
     else:
         kernel = ("expert_mfma_pipe_kernel<true,256> + expert_mfma_small_kernel<true>" if w.fmt == "bf16"
-                  else "expert_mfma_w4_kernel<true,128|64|32> + shared-expert bf16 launch")
+                  else f"expert_mfma_w4_kernel<{FMT_CODE[w.fmt]},true,128|64|32> + shared-expert bf16 launch")
         ms = stage_ms["gu_mfma"]
         if w.fmt == "bf16":
             traffic = measured_traffic(
@@ -151,7 +164,8 @@ def roofline_for(w, counts, stage_ms, counted=True):
             # expert's rows (256-row tiles above 128 rows, else the small-tile launch)
             sh = "expert_mfma_pipe_kernel<true,256>" if w.T > 128 else "expert_mfma_small_kernel<true>"
             traffic = measured_traffic(
-                w.name, [f"moe::expert_mfma_w4_kernel<true,{bm}>" for bm in (128, 64, 32)] + [f"moe::{sh}"])
+                w.name, [f"moe::expert_mfma_w4_kernel<{FMT_CODE[w.fmt]},true,{bm}>" for bm in (128, 64, 32)] +
+                [f"moe::{sh}"])
         # rows on the GEMV path (groups of 1..8 rows) are not in this launch
         small = counts[(counts > 0) & (counts <= 8)]
         n_touched -= int(small.numel())
@@ -287,7 +301,7 @@ class Runner:
             out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
         if ws is None:
             ws = torch.empty((moe.workspace_bytes(w.T, w.H, w.E, w.I, w.Is, w.topk,
-                                                  0 if w.fmt == "bf16" else 1),),
+                                                  FMT_CODE[w.fmt]),),
                              dtype=torch.uint8, device=dev)
         ex = {} if exports else None
 
@@ -408,20 +422,23 @@ def extra_workloads(runner, d_bf16, dev, args):
         del r, parts, d
         torch.cuda.empty_cache()
 
-    # 4-bit experts (the bf16 ones are freed first)
+    # 4-bit experts, one format at a time (the bf16 ones are freed first)
     d_bf16.clear()
     torch.cuda.empty_cache()
-    w4 = None
-    for name in ("w4_t1", "w4_t2048"):
-        w = W[name]
-        print(f"bench: {name}", file=sys.stderr, flush=True)
-        d = synth.make_router(w, dev)
-        if w4 is None:
-            w4 = {"experts": synth.make_experts(w, dev), "shared": synth.make_shared(w, dev)}
-        d.update(w4)
-        r = runner.run(w, d, {}, steps if w.T > 1 else args.steps, warmup)
-        res[name] = summary(w, r)
-        del r
+    for fam in ("w4", "affine4", "nvfp4"):
+        w4 = None
+        for name in (f"{fam}_t1", f"{fam}_t2048"):
+            w = W[name]
+            print(f"bench: {name}", file=sys.stderr, flush=True)
+            d = synth.make_router(w, dev)
+            if w4 is None:
+                w4 = {"experts": synth.make_experts(w, dev), "shared": synth.make_shared(w, dev)}
+            d.update(w4)
+            r = runner.run(w, d, {}, steps if w.T > 1 else args.steps, warmup)
+            res[name] = summary(w, r)
+            del r, d
+            torch.cuda.empty_cache()
+        del w4
         torch.cuda.empty_cache()
     return res
 
@@ -521,7 +538,7 @@ def main():
         # outside the graph), on the same stream as eager calls would run
         out = torch.empty((w.T, w.H), dtype=torch.float32, device=dev)
         ws = torch.empty((moe.workspace_bytes(w.T, w.H, w.E, w.I, w.Is, w.topk,
-                                              0 if w.fmt == "bf16" else 1),), dtype=torch.uint8, device=dev)
+                                              FMT_CODE[w.fmt]),), dtype=torch.uint8, device=dev)
 
         def call():
             moe.moe_ffn(d["x"], d["router_w"], d["bias"], d["experts"], d["shared"], w.band_lo,
@@ -599,7 +616,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.fmt == "bf16" else "w4a16",
+        "dtype": FMT_DTYPE[w.fmt],
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "topk": w.topk, "I": w.I,
                    "Is": w.Is, "fmt": w.fmt, "band": [w.band_lo, w.band_hi],

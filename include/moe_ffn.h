@@ -84,11 +84,12 @@ extern "C" {
 #define MOE_OK 0
 #define MOE_E_NULL (-1)      /* a required pointer is NULL */
 #define MOE_E_SHAPE (-2)     /* T < 1 or too large; H differs between arguments; H % 256 != 0;
-                                I or Is not a positive multiple of 64; E > MOE_MAX_E */
+                                I or Is not a positive multiple of 64 (I of MOE_AFFINE4
+                                experts: of 128); E > MOE_MAX_E */
 #define MOE_E_DIM (-3)       /* router E != experts E ([P1]: plan.Dim != NumExperts) */
 #define MOE_E_BAND (-4)      /* band_lo < 0, band_hi > E or band_lo >= band_hi */
 #define MOE_E_TOPK (-5)      /* topk < 1, topk > E or topk > MOE_MAX_TOPK */
-#define MOE_E_FORMAT (-6)    /* unknown weight format, or 4-bit group size != 32 */
+#define MOE_E_FORMAT (-6)    /* unknown weight format, or a group size other than the format's */
 #define MOE_E_WORKSPACE (-7) /* workspace NULL or smaller than moe_ffn_workspace_bytes() */
 #define MOE_E_ALIGN (-8)     /* a pointer is not 16-byte aligned */
 #define MOE_E_HIP (-9)       /* the HIP runtime reported an error while enqueuing */
@@ -102,9 +103,13 @@ extern "C" {
 #define MOE_MAX_E 1024
 #define MOE_MAX_T (1 << 20)
 
-/* Expert weight formats. */
-#define MOE_BF16 0  /* bf16 weights */
-#define MOE_W4A16 1 /* 4-bit unsigned codes, bf16 scale and zero per 32 inputs */
+/* Expert weight formats ([P5] "The pieces, in order": the family's 4-bit
+ * checkpoints -- W4A16, MLX affine 4-bit, NVIDIA's NVFP4 read as stored; [P4]
+ * comments: NVFP4's 16-input groups, MLX's 64).  Activations stay bf16. */
+#define MOE_BF16 0    /* bf16 weights */
+#define MOE_W4A16 1   /* 4-bit unsigned codes, bf16 scale and zero per 32 inputs */
+#define MOE_AFFINE4 2 /* MLX affine: 4-bit unsigned codes, bf16 scale and bias per 64 inputs */
+#define MOE_NVFP4 3   /* FP4 E2M1 codes, FP8 E4M3 scale per 16 inputs, fp32 scale per matrix */
 
 /* Rows: x is bf16 [T, H].  With norm_w (bf16 [H]) the layer runs on the
  * RMSNorm of the rows ([P2] "Per MoE layer": the expert side receives the
@@ -149,17 +154,28 @@ typedef struct moe_router {
  * MOE_BF16:  w_gate_up bf16 [E, 2I, H] -- rows 0..I-1 are the gate
  *            projection, rows I..2I-1 the up projection ([P5]: the fused
  *            gate/up rows are 2w wide); w_down bf16 [E, H, I].
- * MOE_W4A16: q_gate_up uint8 [E, 2I, H/2], s_gate_up and z_gate_up bf16
- *            [E, 2I, H/32]; q_down uint8 [E, H, I/2], s_down and z_down bf16
- *            [E, H, I/32].  Two 4-bit unsigned codes per byte, the even input
- *            index in the low nibble; weight = (code - zero) * scale with one
- *            (scale, zero) per 32 consecutive inputs ([P5] "The pieces, in
- *            order": W4A16 checkpoints).  Unused pointers of the other format
- *            are ignored. */
+ * The 4-bit formats store two codes per byte, the even input index in the low
+ * nibble: q_gate_up uint8 [E, 2I, H/2], q_down uint8 [E, H, I/2] (gate rows
+ * first, as above), with per-group arrays of G consecutive inputs:
+ * MOE_W4A16:   G = 32; s_gate_up, z_gate_up bf16 [E, 2I, H/32], s_down,
+ *              z_down bf16 [E, H, I/32]; weight = (code - zero) * scale.
+ * MOE_AFFINE4: G = 64 (MLX affine 4-bit); s_* bf16 scales, z_* bf16 biases,
+ *              [E, 2I, H/64] and [E, H, I/64]; weight = scale * code + bias;
+ *              I a multiple of 128 (whole 4-byte pieces of the down arrays).
+ * MOE_NVFP4:   G = 16 (NVIDIA's NVFP4 as stored); a code is an FP4 E2M1
+ *              value (bit 3 sign, bits 2..1 exponent with bias 1, bit 0
+ *              mantissa; exponent 0 gives 0 or 0.5); s_gate_up uint8
+ *              [E, 2I, H/16] and s_down uint8 [E, H, I/16] are FP8 E4M3
+ *              scales (bias 7, exponent 0 subnormal, 0x7f / 0xff NaN);
+ *              g_gate_up fp32 [E, 2] (each expert's gate, then up matrix
+ *              scale) and g_down fp32 [E]; weight = e2m1(code) * e4m3(scale)
+ *              * matrix scale; z_* unused.
+ * group must equal the format's G (ignored for MOE_BF16).  Unused pointers of
+ * the other formats are ignored. */
 typedef struct moe_experts {
     int32_t E, H, I;
-    int32_t fmt;   /* MOE_BF16 or MOE_W4A16 */
-    int32_t group; /* 32 for MOE_W4A16; ignored for MOE_BF16 */
+    int32_t fmt;   /* MOE_BF16, MOE_W4A16, MOE_AFFINE4 or MOE_NVFP4 */
+    int32_t group; /* 32, 64 or 16 for the 4-bit formats; ignored for MOE_BF16 */
     const void* w_gate_up;
     const void* w_down;
     const uint8_t* q_gate_up;
@@ -168,6 +184,8 @@ typedef struct moe_experts {
     const uint8_t* q_down;
     const void* s_down;
     const void* z_down;
+    const float* g_gate_up; /* MOE_NVFP4: fp32 [E, 2] */
+    const float* g_down;    /* MOE_NVFP4: fp32 [E] */
 } moe_experts;
 
 /* Shared expert (unrouted, weight 1, every row): bf16 w_gate_up [2Is, H]
@@ -309,10 +327,11 @@ int32_t moe_tp_shares(int32_t dim, int32_t unit, int32_t ranks, int32_t* shares)
 
 /* Copy intermediate columns [i_lo, i_hi) of every routed expert -- gate rows
  * i_lo..i_hi-1, up rows I+i_lo..I+i_hi-1 and the same inputs of the down
- * projection (codes, scales and zeros alike for MOE_W4A16) -- into dst, an
+ * projection (codes and per-group arrays alike for the 4-bit formats; the
+ * NVFP4 matrix scales are copied whole) -- into dst, an
  * expert set of the same E, H and format with I = i_hi - i_lo whose arrays
- * the caller allocated.  i_lo and i_hi are multiples of 64 with
- * 0 <= i_lo < i_hi <= I.  Device-to-device copies enqueued on stream; errors
+ * the caller allocated.  i_lo and i_hi are multiples of 64 (of 128 for
+ * MOE_AFFINE4) with 0 <= i_lo < i_hi <= I.  Device-to-device copies enqueued on stream; errors
  * as for moe_ffn (MOE_E_SHAPE for a slice outside the rule). */
 int32_t moe_tp_slice_experts(const moe_experts* src, int32_t i_lo, int32_t i_hi,
                              const moe_experts* dst, void* stream);

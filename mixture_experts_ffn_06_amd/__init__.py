@@ -19,6 +19,10 @@ LIB_PATH = os.path.join(_HERE, "libmoeffn.so")
 
 MOE_BF16 = 0
 MOE_W4A16 = 1
+MOE_AFFINE4 = 2
+MOE_NVFP4 = 3
+_FORMATS = {"bf16": MOE_BF16, "w4": MOE_W4A16, "affine4": MOE_AFFINE4, "nvfp4": MOE_NVFP4}
+_GROUP = {MOE_BF16: 0, MOE_W4A16: 32, MOE_AFFINE4: 64, MOE_NVFP4: 16}
 MOE_MAX_TOPK = 16
 MOE_MAX_E = 1024
 MOE_NUM_EVENTS = 9
@@ -67,7 +71,8 @@ class MoeExperts(ctypes.Structure):
                 ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("q_gate_up", ctypes.c_void_p), ("s_gate_up", ctypes.c_void_p),
                 ("z_gate_up", ctypes.c_void_p), ("q_down", ctypes.c_void_p),
-                ("s_down", ctypes.c_void_p), ("z_down", ctypes.c_void_p)]
+                ("s_down", ctypes.c_void_p), ("z_down", ctypes.c_void_p),
+                ("g_gate_up", ctypes.c_void_p), ("g_down", ctypes.c_void_p)]
 
 
 class MoeShared(ctypes.Structure):
@@ -133,7 +138,7 @@ def _p(t: Optional[torch.Tensor]):
 
 
 def _fmt_code(experts: dict) -> int:
-    return MOE_BF16 if experts["fmt"] == "bf16" else MOE_W4A16
+    return _FORMATS[experts["fmt"]]
 
 
 def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None, router="softmax",
@@ -148,11 +153,12 @@ def make_descriptors(x, router_w, bias, experts, shared, E=None, I=None, router=
     dx = MoeX(_p(x), T, H, _p(norm), eps)
     dr = MoeRouter(_p(router_w), _p(bias), router_w.shape[0], router_w.shape[1],
                    _ROUTER[router] if router in _ROUTER else int(router))
-    de = MoeExperts(E, H, I, fmt, 32 if fmt == MOE_W4A16 else 0,
+    de = MoeExperts(E, H, I, fmt, _GROUP[fmt],
                     _p(experts.get("w_gate_up")), _p(experts.get("w_down")),
                     _p(experts.get("q_gate_up")), _p(experts.get("s_gate_up")),
                     _p(experts.get("z_gate_up")), _p(experts.get("q_down")),
-                    _p(experts.get("s_down")), _p(experts.get("z_down")))
+                    _p(experts.get("s_down")), _p(experts.get("z_down")),
+                    _p(experts.get("g_gate_up")), _p(experts.get("g_down")))
     ds = None
     if shared is not None:
         ds = MoeShared(shared["w_down"].shape[1], shared["w_gate_up"].shape[1],
@@ -313,7 +319,9 @@ def tp_slice_experts(experts: dict, i_lo: int, i_hi: int, stream=None) -> dict:
         if not isinstance(t, torch.Tensor):
             continue
         shape = list(t.shape)
-        if name in _SLICE_GU:
+        if name in ("g_gate_up", "g_down"):
+            pass  # NVFP4 matrix scales: kept whole
+        elif name in _SLICE_GU:
             shape[1] = 2 * n
         else:  # down projection: inputs along the last dimension
             shape[2] = shape[2] * n // I
@@ -367,7 +375,7 @@ def tree_pieces(lo: int, hi: int, E: int):
     return out
 
 
-__all__ = ["moe_ffn", "moe_ffn_static", "MOE_STATIC_SCRATCH_BYTES", "reduce", "tree_pieces", "tp_shares", "tp_slice_experts", "tp_slice_shared", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
+__all__ = ["MOE_AFFINE4", "MOE_NVFP4", "moe_ffn", "moe_ffn_static", "MOE_STATIC_SCRATCH_BYTES", "reduce", "tree_pieces", "tp_shares", "tp_slice_experts", "tp_slice_shared", "workspace_bytes", "strerror", "load_library", "MoeError", "LIB_PATH",
            "MOE_BF16", "MOE_W4A16", "MOE_NUM_EVENTS", "EVENT_SLOTS", "make_descriptors",
            "MoeX", "MoeRouter", "MoeExperts", "MoeShared", "MoeOut", "MOE_COMBINE_PICK",
            "MOE_COMBINE_TREE", "MOE_REDUCE_RANK", "MOE_REDUCE_TREE", "MOE_MAX_PARTS",

@@ -38,15 +38,17 @@ struct ExpertArgs {
     int32_t T, H, topk;
     // routed experts
     int32_t I;
-    int32_t fmt;                // 0 bf16, 1 w4
+    int32_t fmt;                // 0 bf16, 1 W4A16 (G 32), 2 MLX affine (G 64), 3 NVFP4 (G 16)
     const uint16_t* wgu;        // bf16 [E, 2I, H]
     const uint16_t* wd;         // bf16 [E, H, I]
     const uint8_t* qgu;         // [E, 2I, H/2]
-    const uint16_t* sgu;        // [E, 2I, H/32]
+    const uint16_t* sgu;        // [E, 2I, H/G] (NVFP4: E4M3 bytes)
     const uint16_t* zgu;
     const uint8_t* qd;          // [E, H, I/2]
-    const uint16_t* sd;         // [E, H, I/32]
+    const uint16_t* sd;         // [E, H, I/G] (NVFP4: E4M3 bytes)
     const uint16_t* zd;
+    const float* ggu;           // NVFP4 matrix scales [E, 2] (gate, up), else null
+    const float* gd;            // NVFP4 matrix scales [E], else null
     // shared expert (bf16)
     int32_t Is;
     const uint16_t* swgu;       // [2Is, H]

@@ -348,6 +348,8 @@ __device__ void shared_gateup_rows(const SharedGateUp& s, int block, int nblocks
     lds_byte* xl8 = (lds_byte*)xs4;
     for (int c0 = 64 * wave; c0 < NR * c8n; c0 += 64 * nwaves)
         __builtin_amdgcn_global_load_lds(s.x + (size_t)(c0 + lane) * 8, xl8 + (size_t)c0 * 16, 16, 0, 0);
+    // the wait below counts on every row load issuing before the weight loads
+    __builtin_amdgcn_sched_barrier(0);
     const bool first = c < s.Is;
     if (first) {
         issue(c, 0);
@@ -357,6 +359,10 @@ __device__ void shared_gateup_rows(const SharedGateUp& s, int block, int nblocks
         __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
     }
     __builtin_amdgcn_s_barrier();
+    // no read of the staged rows may move above the barrier (a compiler-only
+    // memory barrier: it emits no wait for the weight loads in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
     const uint16_t* xl = xs + 8 * lane;
     while (c < s.Is) {
         float ag[NR], au[NR];

@@ -18,8 +18,16 @@
 // lane step covers exactly one 32-input group: the codes are widened to the
 // bf16 values 128 + code with two bit operations per pair, dotted with the
 // rows (inputs stored pairwise-permuted in LDS to match the nibble order), and
-// the group contributes scale * (dot - (128 + zero) * sum(inputs)).
+// the group contributes scale * (dot - (128 + zero) * sum(inputs)).  MLX
+// affine (scale * code + bias per 64 inputs) takes the same widening: a lane
+// step is half a group and contributes scale * (dot - 128 * sum) + bias * sum.
+// NVFP4 (E2M1 codes, an E4M3 scale per 16 inputs, an fp32 scale per matrix):
+// the hardware conversion turns two codes at a time into exact bf16 values,
+// dotted with the rows in their plain order; each 16-input block adds its
+// scale times its dot, and the matrix scale multiplies the finished sum.
 #include "common.h"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -137,6 +145,116 @@ __device__ __forceinline__ void dot_step_w4(const uint4& q, float sc, float zz, 
     for (int r = 0; r < NR; ++r) acc[r] += sc * (part[r] - z128 * xsum[r * (K / 32) + k / 32]);
 }
 
+// MLX affine 4-bit: 32 inputs (half a 64-input group) per lane step; same
+// widening and LDS layout as dot_step_w4.
+template <int NR>
+__device__ __forceinline__ void dot_step_affine(const uint4& q, float sc, float bias, const uint16_t* xs,
+                                                const float* xsum, int K, int k, float* acc) {
+    uint32_t qd[4] = {q.x, q.y, q.z, q.w};
+    float part[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) part[r] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t c = qd[d];
+        const uint32_t p0 = and_or(c, 0x000f000fu, 0x43004300u);
+        const uint32_t p1 = and_or(c >> 4, 0x000f000fu, 0x43004300u);
+        const uint32_t p2 = and_or(c >> 8, 0x000f000fu, 0x43004300u);
+        const uint32_t p3 = and_or(c >> 12, 0x000f000fu, 0x43004300u);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k + 8 * w4_chunk(k >> 5, d));
+            float s = part[r];
+            s = dot2_bf16(p0, xv.x, s);
+            s = dot2_bf16(p1, xv.y, s);
+            s = dot2_bf16(p2, xv.z, s);
+            s = dot2_bf16(p3, xv.w, s);
+            part[r] = s;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const float X = xsum[r * (K / 32) + k / 32];
+        acc[r] += fmaf(sc, part[r] - 128.0f * X, bias * X);
+    }
+}
+
+// Two E2M1 codes (byte B of c) -> two exact bf16 values, in input order.
+template <int B>
+__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t c) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, 1.0f, B));
+}
+
+// NVFP4: 32 inputs (two 16-input blocks, scales s0 and s1) per lane step; the
+// rows in LDS in their plain order.
+template <int NR>
+__device__ __forceinline__ void dot_step_nv(const uint4& q, float s0, float s1, const uint16_t* xs, int K,
+                                            int k, float* acc) {
+    const uint32_t qd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        float part[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) part[r] = 0.0f;
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) {
+            const int d = 2 * blk + dd;
+            const uint32_t c = qd[d];
+            const uint32_t p0 = fp4x2_bf16<0>(c), p1 = fp4x2_bf16<1>(c);
+            const uint32_t p2 = fp4x2_bf16<2>(c), p3 = fp4x2_bf16<3>(c);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                const uint4 xv = *reinterpret_cast<const uint4*>(xs + r * K + k + 8 * d);
+                float s = part[r];
+                s = dot2_bf16(p0, xv.x, s);
+                s = dot2_bf16(p1, xv.y, s);
+                s = dot2_bf16(p2, xv.z, s);
+                s = dot2_bf16(p3, xv.w, s);
+                part[r] = s;
+            }
+        }
+        const float sc = blk ? s1 : s0;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r] = fmaf(sc, part[r], acc[r]);
+    }
+}
+
+// Per-group arrays of row `row` (of K inputs) at lane step k: W4A16 (scale,
+// zero) and MLX affine (scale, bias) as bf16 bits; NVFP4 the two E4M3 bytes
+// of the step's blocks in s.
+template <int FMT>
+__device__ __forceinline__ void load_scales(const uint16_t* sb, const uint16_t* zb, size_t row, int K, int k,
+                                            uint32_t* s, uint32_t* z) {
+    if constexpr (FMT == 1) {
+        *s = sb[row * (K / 32) + k / 32];
+        *z = zb[row * (K / 32) + k / 32];
+    } else if constexpr (FMT == 2) {
+        *s = sb[row * (K / 64) + k / 64];
+        *z = zb[row * (K / 64) + k / 64];
+    } else {
+        *s = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sb) + row * (K / 16) + k / 16);
+        *z = 0;
+    }
+}
+
+// One 32-input lane step of a 4-bit format; !ok (a step past the row) adds
+// nothing.
+template <int FMT, int NR>
+__device__ __forceinline__ void quant_step(const uint4& q, uint32_t s, uint32_t z, bool ok, const uint16_t* xs,
+                                           const float* xsum, int K, int k, float* acc) {
+    if constexpr (FMT == 1) {
+        dot_step_w4<NR>(q, ok ? bf16_bits_to_f32(s) : 0.0f, bf16_bits_to_f32(z), xs, xsum, K, k, acc);
+    } else if constexpr (FMT == 2) {
+        dot_step_affine<NR>(q, ok ? bf16_bits_to_f32(s) : 0.0f, ok ? bf16_bits_to_f32(z) : 0.0f, xs, xsum, K, k,
+                            acc);
+    } else {
+        // (converted unconditionally: a conversion under the condition would
+        // become a branch)
+        const float f0 = __builtin_amdgcn_cvt_f32_fp8(s, 0), f1 = __builtin_amdgcn_cvt_f32_fp8(s, 1);
+        dot_step_nv<NR>(q, ok ? f0 : 0.0f, ok ? f1 : 0.0f, xs, K, k, acc);
+    }
+}
+
 // ---- gate/up ---------------------------------------------------------------
 
 // One work item: intermediate columns c0 .. c0+15 of group g; wave w owns
@@ -145,7 +263,7 @@ __device__ __forceinline__ void dot_step_w4(const uint4& q, float sc, float zz, 
 // row's first chunk and its weights are zeroed, so every load of a block is in
 // flight at once (a predicated load would make the compiler wait for the
 // previous one).  CB = lane steps per block (bf16: 512 inputs per step).
-template <int W4, int NR, int CB>
+template <int FMT, int NR, int CB>
 __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const uint16_t* xs,
                             const float* xsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -157,7 +275,7 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
         float ag[NR], au[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) ag[r] = au[r] = 0.0f;
-        if (!W4) {
+        if (FMT == 0) {
             const uint16_t* gr = shared ? a.swgu + (size_t)c * H
                                         : a.wgu + ((size_t)g.expert * 2 * Ig + c) * H;
             const uint16_t* ur = gr + (size_t)Ig * H;
@@ -185,10 +303,6 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
             const size_t grow = (size_t)g.expert * 2 * Ig + c, urow = grow + Ig;
             const uint8_t* gq = a.qgu + grow * (H / 2);
             const uint8_t* uq = a.qgu + urow * (H / 2);
-            const uint16_t* gs = a.sgu + grow * (H / 32);
-            const uint16_t* gz = a.zgu + grow * (H / 32);
-            const uint16_t* us = a.sgu + urow * (H / 32);
-            const uint16_t* uz = a.zgu + urow * (H / 32);
             constexpr int CB4 = 3;
             const int nch = (H + 2047) / 2048;
             for (int q0 = 0; q0 < nch; q0 += CB4) {
@@ -203,43 +317,48 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
                     kk[qq] = ok[qq] ? k : 0;
                     qg[qq] = wload(gq + kk[qq] / 2);
                     qu[qq] = wload(uq + kk[qq] / 2);
-                    sg[qq] = gs[kk[qq] / 32];
-                    zg[qq] = gz[kk[qq] / 32];
-                    su[qq] = us[kk[qq] / 32];
-                    zu[qq] = uz[kk[qq] / 32];
+                    load_scales<FMT>(a.sgu, a.zgu, grow, H, kk[qq], &sg[qq], &zg[qq]);
+                    load_scales<FMT>(a.sgu, a.zgu, urow, H, kk[qq], &su[qq], &zu[qq]);
                 }
 #pragma unroll
                 for (int qq = 0; qq < CB4; ++qq) {
-                    // a zero scale removes the contribution of a step past the end
-                    const float sgv = ok[qq] ? bf16_bits_to_f32(sg[qq]) : 0.0f;
-                    const float suv = ok[qq] ? bf16_bits_to_f32(su[qq]) : 0.0f;
-                    dot_step_w4<NR>(qg[qq], sgv, bf16_bits_to_f32(zg[qq]), xs, xsum, H, kk[qq], ag);
-                    dot_step_w4<NR>(qu[qq], suv, bf16_bits_to_f32(zu[qq]), xs, xsum, H, kk[qq], au);
+                    quant_step<FMT, NR>(qg[qq], sg[qq], zg[qq], ok[qq], xs, xsum, H, kk[qq], ag);
+                    quant_step<FMT, NR>(qu[qq], su[qq], zu[qq], ok[qq], xs, xsum, H, kk[qq], au);
                 }
             }
+        }
+        // NVFP4: the gate and up matrix scales multiply the finished sums
+        float mg = 1.0f, mu = 1.0f;
+        if (FMT == 3 && !shared) {
+            mg = a.ggu[2 * (size_t)g.expert];
+            mu = a.ggu[2 * (size_t)g.expert + 1];
         }
         uint16_t* hout = shared ? a.h_s : a.h_r + (size_t)g.row0 * a.I;
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const float gs_ = wave_sum(ag[r]);
-            const float us_ = wave_sum(au[r]);
+            float gs_ = wave_sum(ag[r]);
+            float us_ = wave_sum(au[r]);
+            if (FMT == 3) {
+                gs_ *= mg;
+                us_ *= mu;
+            }
             if (lane == r) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(gs_, us_));
         }
     }
 }
 
-template <int W4, int CB>
+template <int FMT, int CB>
 __device__ __forceinline__ void gateup_dispatch_rows(const ExpertArgs& a, const Group& g, int c0,
                                                      const uint16_t* xs, const float* xsum) {
     switch (g.n) {
-        case 1: gateup_item<W4, 1, CB>(a, g, c0, xs, xsum); break;
-        case 2: gateup_item<W4, 2, CB>(a, g, c0, xs, xsum); break;
-        case 3: gateup_item<W4, 3, CB>(a, g, c0, xs, xsum); break;
-        case 4: gateup_item<W4, 4, CB>(a, g, c0, xs, xsum); break;
-        case 5: gateup_item<W4, 5, CB>(a, g, c0, xs, xsum); break;
-        case 6: gateup_item<W4, 6, CB>(a, g, c0, xs, xsum); break;
-        case 7: gateup_item<W4, 7, CB>(a, g, c0, xs, xsum); break;
-        default: gateup_item<W4, 8, CB>(a, g, c0, xs, xsum); break;
+        case 1: gateup_item<FMT, 1, CB>(a, g, c0, xs, xsum); break;
+        case 2: gateup_item<FMT, 2, CB>(a, g, c0, xs, xsum); break;
+        case 3: gateup_item<FMT, 3, CB>(a, g, c0, xs, xsum); break;
+        case 4: gateup_item<FMT, 4, CB>(a, g, c0, xs, xsum); break;
+        case 5: gateup_item<FMT, 5, CB>(a, g, c0, xs, xsum); break;
+        case 6: gateup_item<FMT, 6, CB>(a, g, c0, xs, xsum); break;
+        case 7: gateup_item<FMT, 7, CB>(a, g, c0, xs, xsum); break;
+        default: gateup_item<FMT, 8, CB>(a, g, c0, xs, xsum); break;
     }
 }
 
@@ -383,7 +502,9 @@ __device__ __forceinline__ void item_of(const ExpertArgs& a, int it, int nrouted
     }
 }
 
-template <int W4, int CB>
+// FMT: the routed experts' format (0 bf16, 1 W4A16, 2 MLX affine, 3 NVFP4);
+// the shared expert is bf16 in every format.
+template <int FMT, int CB>
 __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a, int lds_rows) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -410,7 +531,10 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
         const bool has_next = itn < total;
         ItemMeta mn = m;
         const Group& g = m.g;
-        const bool w4 = W4 && g.expert >= 0;
+        const bool w4 = FMT != 0 && g.expert >= 0;
+        // the 4-bit layout of staged rows (pairwise-permuted, with per-32
+        // sums) for W4A16 and MLX affine; NVFP4 reads them in plain order
+        const bool perm = w4 && FMT != 3;
         if (!w4 && g.n <= 2 && fast_ok) {
             const bool restage = m.gi != cur;
             if (restage) buf ^= 1;
@@ -423,24 +547,25 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
             staged = -1;  // its buffers overlap the synchronous staging area
         } else {
             // rows staged synchronously across the whole LDS area
-            const int key = g.n == 1 ? 2 * m.tok0 + (w4 ? 1 : 0) : -1;
+            const int key = g.n == 1 ? 2 * m.tok0 + (perm ? 1 : 0) : -1;
             if (key < 0 || key != staged) {
                 __syncthreads();  // a fast-path item before may still read its buffer
-                stage_rows(a, g, false, a.H, g.n, w4, xs, xsum);
+                stage_rows(a, g, false, a.H, g.n, perm, xs, xsum);
                 __syncthreads();
                 staged = key;
             }
             if (has_next) mn = load_meta(a, itn, nrouted, TR);
             if (w4)
-                gateup_dispatch_rows<1, CB>(a, g, m.tile * kGuCols, xs, xsum);
+                gateup_dispatch_rows<FMT, CB>(a, g, m.tile * kGuCols, xs, xsum);
             else
                 gateup_dispatch_rows<0, CB>(a, g, m.tile * kGuCols, xs, xsum);
             // The next item overwrites these rows only if it stages others
             // (or takes the fast path, whose buffers overlap them); one-row
             // groups of the same token and format keep them, and need no
             // barrier (every 4-bit item at T = 1).
-            const bool w4n = W4 && mn.g.expert >= 0;
-            const bool keeps = has_next && mn.g.n == 1 && key >= 0 && 2 * mn.tok0 + (w4n ? 1 : 0) == key &&
+            const bool w4n = FMT != 0 && mn.g.expert >= 0;
+            const bool keeps = has_next && mn.g.n == 1 && key >= 0 &&
+                               2 * mn.tok0 + (w4n && FMT != 3 ? 1 : 0) == key &&
                                !(!w4n && mn.g.n <= 2 && fast_ok);
             if (!keeps) __syncthreads();
             cur = -1;
@@ -455,7 +580,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
 
 // One work item: output columns n0 .. n0+63 of group g; wave w owns 8 of them,
 // streamed as two passes of 4 rows of the down weight (16 loads in flight).
-template <int W4, int NR>
+template <int FMT, int NR>
 __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uint16_t* xs,
                           const float* xsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -470,7 +595,7 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < NR; ++r) acc[u][r] = 0.0f;
-    if (!W4 && K == 512 * 4) {
+    if (FMT == 0 && K == 512 * 4) {
         // rows of exactly 4 lane steps (K = 2048): no clamping, no selects
         const uint16_t* wrow = (shared ? a.swd : a.wd + (size_t)g.expert * H * K) + (size_t)cbase * K + 8 * lane;
         const uint16_t* xl = xs + 8 * lane;
@@ -494,7 +619,7 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
                     acc[u][r] = t;
                 }
             }
-    } else if (!W4) {
+    } else if (FMT == 0) {
         const uint16_t* wbase = shared ? a.swd : a.wd + (size_t)g.expert * H * K;
         constexpr int CB = 4;
         const int nch = (K + 511) / 512;
@@ -542,21 +667,21 @@ __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uin
             for (int u = 0; u < U; ++u) {
                 const size_t row = rbase + cbase + u;
                 qv[u] = wload(a.qd + row * (K / 2) + kq / 2);
-                sv[u] = a.sd[row * (K / 32) + kq / 32];
-                zv[u] = a.zd[row * (K / 32) + kq / 32];
+                load_scales<FMT>(a.sd, a.zd, row, K, kq, &sv[u], &zv[u]);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                dot_step_w4<NR>(qv[u], ok ? bf16_bits_to_f32(sv[u]) : 0.0f, bf16_bits_to_f32(zv[u]),
-                                xs, xsum, K, kq, acc[u]);
+            for (int u = 0; u < U; ++u) quant_step<FMT, NR>(qv[u], sv[u], zv[u], ok, xs, xsum, K, kq, acc[u]);
         }
     }
+    // NVFP4: the down matrix scale multiplies the finished sums
+    const float md = FMT == 3 && !shared ? a.gd[g.expert] : 1.0f;
     float* yout = shared ? a.y_s : a.y_r + (size_t)g.row0 * H;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const float v = wave_sum(acc[u][r]);
+            float v = wave_sum(acc[u][r]);
+            if (FMT == 3) v *= md;
             if (lane == ((u * NR + r) & 63)) yout[(size_t)r * H + cbase + u] = v;
         }
     }
@@ -628,22 +753,22 @@ __device__ void down_fast(const ExpertArgs& a, const Group& g, int n0, bool rest
     }
 }
 
-template <int W4>
+template <int FMT>
 __device__ __forceinline__ void down_dispatch_rows(const ExpertArgs& a, const Group& g, int n0,
                                                    const uint16_t* xs, const float* xsum) {
     switch (g.n) {
-        case 1: down_item<W4, 1>(a, g, n0, xs, xsum); break;
-        case 2: down_item<W4, 2>(a, g, n0, xs, xsum); break;
-        case 3: down_item<W4, 3>(a, g, n0, xs, xsum); break;
-        case 4: down_item<W4, 4>(a, g, n0, xs, xsum); break;
-        case 5: down_item<W4, 5>(a, g, n0, xs, xsum); break;
-        case 6: down_item<W4, 6>(a, g, n0, xs, xsum); break;
-        case 7: down_item<W4, 7>(a, g, n0, xs, xsum); break;
-        default: down_item<W4, 8>(a, g, n0, xs, xsum); break;
+        case 1: down_item<FMT, 1>(a, g, n0, xs, xsum); break;
+        case 2: down_item<FMT, 2>(a, g, n0, xs, xsum); break;
+        case 3: down_item<FMT, 3>(a, g, n0, xs, xsum); break;
+        case 4: down_item<FMT, 4>(a, g, n0, xs, xsum); break;
+        case 5: down_item<FMT, 5>(a, g, n0, xs, xsum); break;
+        case 6: down_item<FMT, 6>(a, g, n0, xs, xsum); break;
+        case 7: down_item<FMT, 7>(a, g, n0, xs, xsum); break;
+        default: down_item<FMT, 8>(a, g, n0, xs, xsum); break;
     }
 }
 
-template <int W4>
+template <int FMT>
 __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, int lds_rows,
                                                                  int kmax) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -663,10 +788,10 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, i
     for (int it = blockIdx.x; it < total; it += gridDim.x) {
         const int gi = it / TR, tile = it - gi * TR;
         const Group g = a.groups[a.gemv_list[gi]];
-        const bool w4 = W4 && g.expert >= 0;
+        const bool w4 = FMT != 0 && g.expert >= 0;
         const int K = g.expert < 0 ? a.Is : a.I;
-        // (not in the 4-bit kernel: its registers would spill)
-        if (!W4 && g.n <= 2 && K == 512 * 4) {
+        // (not in the 4-bit kernels: their registers would spill)
+        if (FMT == 0 && g.n <= 2 && K == 512 * 4) {
             if (prev_slow) __syncthreads();  // the synchronous item's LDS reads are done
             const bool restage = gi != fcur;
             if (restage) buf ^= 1;
@@ -682,12 +807,12 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, i
         }
         if (gi != scur) {
             __syncthreads();
-            stage_rows(a, g, true, K, g.n, w4, xs, xsum);
+            stage_rows(a, g, true, K, g.n, w4 && FMT != 3, xs, xsum);
             __syncthreads();
             scur = gi;
         }
         if (w4)
-            down_dispatch_rows<1>(a, g, tile * kDnCols, xs, xsum);
+            down_dispatch_rows<FMT>(a, g, tile * kDnCols, xs, xsum);
         else
             down_dispatch_rows<0>(a, g, tile * kDnCols, xs, xsum);
         fcur = -1;
@@ -702,15 +827,20 @@ static int gemv_grid(size_t lds, int num_cu, long long ub) {
     return (int)(g < 1 ? 1 : g);
 }
 
+template <int FMT, int CB>
+static void launch_gateup_fmt(const ExpertArgs& a, int grid, size_t lds, int lds_rows, hipStream_t st) {
+    allow_lds(gateup_gemv_kernel<FMT, CB>, lds);
+    gateup_gemv_kernel<FMT, CB><<<grid, kGemvThreads, lds, st>>>(a, lds_rows);
+}
+
 template <int CB>
 static void launch_gateup_cb(const ExpertArgs& a, int grid, size_t lds, int lds_rows,
                              hipStream_t st) {
-    if (a.fmt) {
-        allow_lds(gateup_gemv_kernel<1, CB>, lds);
-        gateup_gemv_kernel<1, CB><<<grid, kGemvThreads, lds, st>>>(a, lds_rows);
-    } else {
-        allow_lds(gateup_gemv_kernel<0, CB>, lds);
-        gateup_gemv_kernel<0, CB><<<grid, kGemvThreads, lds, st>>>(a, lds_rows);
+    switch (a.fmt) {
+        case 1: launch_gateup_fmt<1, CB>(a, grid, lds, lds_rows, st); break;
+        case 2: launch_gateup_fmt<2, CB>(a, grid, lds, lds_rows, st); break;
+        case 3: launch_gateup_fmt<3, CB>(a, grid, lds, lds_rows, st); break;
+        default: launch_gateup_fmt<0, CB>(a, grid, lds, lds_rows, st); break;
     }
 }
 
@@ -739,12 +869,16 @@ void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream
     const int lds_rows = max_rows > 4 ? max_rows : 4;
     const size_t lds = (size_t)lds_rows * kmax * 2 + (a.fmt ? (size_t)max_rows * (kmax / 32) * 4 : 0);
     const int grid = gemv_grid(lds, num_cu, (long long)max_groups * (a.H / kDnCols));
-    if (a.fmt) {
-        allow_lds(down_gemv_kernel<1>, lds);
-        down_gemv_kernel<1><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
-    } else {
-        allow_lds(down_gemv_kernel<0>, lds);
-        down_gemv_kernel<0><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
+    auto go = [&](auto fmt) {
+        constexpr int F = decltype(fmt)::value;
+        allow_lds(down_gemv_kernel<F>, lds);
+        down_gemv_kernel<F><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
+    };
+    switch (a.fmt) {
+        case 1: go(std::integral_constant<int, 1>{}); break;
+        case 2: go(std::integral_constant<int, 2>{}); break;
+        case 3: go(std::integral_constant<int, 3>{}); break;
+        default: go(std::integral_constant<int, 0>{}); break;
     }
 }
 

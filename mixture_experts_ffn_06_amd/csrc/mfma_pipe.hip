@@ -583,11 +583,60 @@ __device__ __forceinline__ bf16x8_p dequant8(uint32_t c, float s, float n) {
     return __builtin_bit_cast(bf16x8_p, o);
 }
 
+// The per-group arrays of the 4-bit formats as the scale/zero blocks stage
+// them.  Every lane of a piece load takes 4 bytes of one row: W4A16 one step
+// (its two 32-input groups' bf16 scales, or zeros), MLX affine two steps (a
+// bf16 scale, or bias, per 64-input group = per step), NVFP4 one step (its
+// four 16-input groups' E4M3 scales).  A piece takes AL lanes (64, or 32 when
+// the format's arrays are half as many bytes per block), so a block of G
+// steps is always 4 G pieces, one per wave and step.
+template <int FMT>
+struct W4Fmt {
+    static constexpr int NA = FMT == 3 ? 1 : 2;             // arrays (scales [, zeros / biases])
+    static constexpr int BPS = FMT == 2 ? 2 : 4;            // bytes per row and step, per array
+    static constexpr int SPL = 4 / BPS;                     // steps per 4-byte lane load
+    static constexpr int AL = FMT == 1 ? 64 : 32;           // lanes per piece
+    static constexpr int PB = 4 * AL;                       // bytes per piece
+};
+
+// MLX affine: eight codes (one word, k = 0..7 in nibbles 0..7) -> eight bf16
+// weights RNE(RNE_f32(s * q + b)).  The fp16 bit pattern q is the value
+// q * 2^-24 (a subnormal), so v_fma_mix with s * 2^24 (exact: a power of two)
+// gives s * q + b with one fp32 rounding.
+__device__ __forceinline__ bf16x8_p dequant8_affine(uint32_t c, float s24, float b) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f16x2_p h = __builtin_bit_cast(f16x2_p, (c >> (4 * j)) & 0x000f000fu);
+        v[j] = fmaf((float)h.x, s24, b);
+        v[j + 4] = fmaf((float)h.y, s24, b);
+    }
+    const u32x4_p o = {pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]), pack2_bf16(v[4], v[5]),
+                       pack2_bf16(v[6], v[7])};
+    return __builtin_bit_cast(bf16x8_p, o);
+}
+
+// NVFP4: eight E2M1 codes (one word, byte j holding k = 2j and 2j + 1) -> the
+// exact products e2m1(q) * e4m3(s) as bf16 (two significant bits times four
+// fit in bf16's eight); the matrix scale is applied to the finished sums.
+typedef float f32x2_p __attribute__((ext_vector_type(2)));
+template <int B>
+__device__ __forceinline__ uint32_t fp4x2_scaled_bf16(uint32_t c, float s) {
+    const f32x2_p v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, B);
+    return pack2_bf16(v.x * s, v.y * s);
+}
+__device__ __forceinline__ bf16x8_p dequant8_nv(uint32_t c, float s) {
+    const u32x4_p o = {fp4x2_scaled_bf16<0>(c, s), fp4x2_scaled_bf16<1>(c, s), fp4x2_scaled_bf16<2>(c, s),
+                       fp4x2_scaled_bf16<3>(c, s)};
+    return __builtin_bit_cast(bf16x8_p, o);
+}
+
 // MTL: live 16-row subtiles of the tile (the group's rows past them take no
 // MFMA and no A fragment reads).
-template <bool GATEUP, int BM, int MTL>
+template <int FMT, bool GATEUP, int BM, int MTL>
 __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, int m0, int nt) {
     using C = W4Cfg<BM>;
+    using F = W4Fmt<FMT>;
     static_assert(MTL >= 1 && MTL <= C::MT, "live subtiles");
     typedef __attribute__((address_space(3))) const uint32_t lds_u32;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -621,24 +670,28 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     };
     const unsigned char* qsrc =
         (GATEUP ? a.qgu : a.qd) + wrow(32 * wave + (lane & 31)) * (K / 2) + 16 * (lane >> 5);
-    // Scale/zero block b (steps G b .. G b + G - 1) is 4 G pieces of 256
-    // bytes: piece i covers array i / 2G (scales, zeros), rows
-    // (i mod 2G) R .. + R - 1 (R = 64 / G), lane l taking step G b + l / R of
-    // row + l % R (4 bytes: the step's two groups), stored step-major within
-    // the piece.  Per row the G steps are contiguous in memory, so a piece
-    // touches R cache lines instead of 64.  Block 0 is loaded before the first
-    // stage, block b + 1 a piece per stage (one per wave) during the stages of
-    // block b, into buffer (b + 1) mod 3.
-    const uint16_t* sbase = GATEUP ? a.sgu : a.sd;
-    const uint16_t* zbase = GATEUP ? a.zgu : a.zd;
-    constexpr int R = 64 / C::G;  // rows per piece
+    // Scale/zero block b (steps G b .. G b + G - 1) is 4 G pieces of PB
+    // bytes: piece i covers array i / (4G / NA) (scales, then zeros or
+    // biases), rows (i mod (4G / NA)) R .. + R - 1, lane l < AL taking the 4
+    // bytes of row + l % R at steps G b + (l / R) SPL .. + SPL - 1, stored in
+    // lane order (step-major within the piece).  Per row the G steps are
+    // contiguous in memory, so a piece touches R cache lines instead of 64.
+    // Block 0 is loaded before the first stage, block b + 1 a piece per stage
+    // (one per wave) during the stages of block b, into buffer (b + 1) mod 3.
+    const unsigned char* sbase = reinterpret_cast<const unsigned char*>(GATEUP ? a.sgu : a.sd);
+    const unsigned char* zbase = reinterpret_cast<const unsigned char*>(GATEUP ? a.zgu : a.zd);
+    constexpr int R = F::AL * F::SPL / C::G;  // rows per piece
+    constexpr int PPA = 128 / R;              // pieces per array
+    const int RSB = KT * F::BPS;              // bytes of a row of one array
     auto issue_sz = [&](int b, int i) {
-        const int arr = i / (2 * C::G), rg = i % (2 * C::G);
+        const int arr = i / PPA, rg = i % PPA;
         const int r = rg * R + lane % R;
-        const int ks = min(C::G * b + lane / R, KT - 1);  // steps past the end: unused
-        const uint16_t* src = (arr ? zbase : sbase) + wrow(r) * (K / 32) + 2 * ks;
-        lds_u8* dst = smem + C::SZOff + (b % 3) * C::SZBlock + arr * (C::SZBlock / 2) + rg * 256;
-        __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+        // the 4-byte chunk of the row holding steps G b + (l / R) SPL ..; chunks
+        // past the row's end reload its last one (unused)
+        const int chunk = min(C::G * b / F::SPL + lane / R, RSB / 4 - 1);
+        const unsigned char* src = (arr ? zbase : sbase) + wrow(r) * RSB + 4 * chunk;
+        lds_u8* dst = smem + C::SZOff + (b % 3) * C::SZBlock + arr * (PPA * F::PB) + rg * F::PB;
+        if (F::AL == 64 || lane < F::AL) __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
     };
 
     auto issue = [&](int kt) {
@@ -692,16 +745,18 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         __builtin_amdgcn_s_barrier();  // stage kt visible to all waves; stage kt-1 free
         if (kt + C::S - 1 < KT) issue(kt + C::S - 1);
         const lds_u8* st = smem + (kt % C::S) * C::Stage;
-        const lds_u8* sz = smem + C::SZOff + ((kt / C::G) % 3) * C::SZBlock + (kt % C::G) * (4 * R);
+        // this step's 4-byte word of each array: chunk (kt mod G) / SPL of the
+        // block, byte (kt mod SPL) BPS within it
+        const lds_u8* sz = smem + C::SZOff + ((kt / C::G) % 3) * C::SZBlock + ((kt % C::G) / F::SPL) * (4 * R);
         // Every LDS read of the step first (one wait), then the expansion,
         // then the MFMAs.
         uint32_t sw[C::NT], zw[C::NT], codes[2][C::NT];
         bf16x8_p af[2][MTL];
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) {
-            const int off = (brow[j] / R) * 256 + (brow[j] % R) * 4;  // piece, row in piece
+            const int off = (brow[j] / R) * F::PB + (brow[j] % R) * 4;  // piece, row in piece
             sw[j] = *(lds_u32*)(sz + off);
-            zw[j] = *(lds_u32*)(sz + C::SZBlock / 2 + off);
+            zw[j] = F::NA == 2 ? *(lds_u32*)(sz + PPA * F::PB + off) : 0u;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -716,12 +771,30 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         bf16x8_p bfr[2][C::NT];
 #pragma unroll
         for (int j = 0; j < C::NT; ++j) {
+            if constexpr (FMT == 1) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                // scale and zero of this lane's column for group ks of the step
-                const float sc = __uint_as_float(ks ? (sw[j] & 0xffff0000u) : (sw[j] << 16));
-                const float zz = __uint_as_float(ks ? (zw[j] & 0xffff0000u) : (zw[j] << 16));
-                bfr[ks][j] = dequant8(codes[ks][j], sc, -((1024.0f + zz) * sc));
+                for (int ks = 0; ks < 2; ++ks) {
+                    // scale and zero of this lane's column for group ks of the step
+                    const float sc = __uint_as_float(ks ? (sw[j] & 0xffff0000u) : (sw[j] << 16));
+                    const float zz = __uint_as_float(ks ? (zw[j] & 0xffff0000u) : (zw[j] << 16));
+                    bfr[ks][j] = dequant8(codes[ks][j], sc, -((1024.0f + zz) * sc));
+                }
+            } else if constexpr (FMT == 2) {
+                // the step's one 64-input group: half kt mod 2 of the words
+                const uint32_t sh = kt & 1 ? sw[j] & 0xffff0000u : sw[j] << 16;
+                const uint32_t bh = kt & 1 ? zw[j] & 0xffff0000u : zw[j] << 16;
+                const float s24 = __uint_as_float(sh) * 16777216.0f;
+                const float bb = __uint_as_float(bh);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) bfr[ks][j] = dequant8_affine(codes[ks][j], s24, bb);
+            } else {
+                // the lane's eight inputs 32 ks + 8 (lane / 16) .. lie in the
+                // step's 16-input group 2 ks + lane / 32
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const float sblk = __builtin_amdgcn_cvt_f32_fp8(sw[j] >> (8 * (2 * ks + (lane >> 5))), 0);
+                    bfr[ks][j] = dequant8_nv(codes[ks][j], sblk);
+                }
             }
         }
 #pragma unroll
@@ -733,6 +806,12 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
     }
 
+    // NVFP4: the matrix scales multiply the finished sums
+    float mg = 1.0f, mu = 1.0f;
+    if (FMT == 3) {
+        mg = GATEUP ? a.ggu[2 * (size_t)g.expert] : a.gd[g.expert];
+        mu = GATEUP ? a.ggu[2 * (size_t)g.expert + 1] : mg;
+    }
     if (GATEUP) {
         uint16_t* hout = a.h_r + (size_t)(g.row0 + m0) * a.I;
         const int c = nt * 64 + 16 * wave + (lane & 15);
@@ -741,9 +820,17 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * i + 4 * (lane >> 4) + v;
-                if (r < rows) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(acc[i][0][v], acc[i][1][v]));
+                const float gv = FMT == 3 ? acc[i][0][v] * mg : acc[i][0][v];
+                const float uv = FMT == 3 ? acc[i][1][v] * mu : acc[i][1][v];
+                if (r < rows) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(gv, uv));
             }
     } else {
+        if (FMT == 3) {
+#pragma unroll
+            for (int i = 0; i < MTL; ++i)
+#pragma unroll
+                for (int j = 0; j < C::NT; ++j) acc[i][j] *= mg;
+        }
         float* yout = a.y_r + (size_t)(g.row0 + m0) * H;
 #pragma unroll
         for (int i = 0; i < MTL; ++i)
@@ -761,7 +848,7 @@ __device__ void pipe_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
 // Routed 4-bit groups only (the shared expert is bf16 and runs in
 // expert_mfma_pipe_kernel or expert_mfma_small_kernel).  BM = 128 also takes
 // the 256-row list, each tile as two 128-row halves.
-template <bool GATEUP, int BM>
+template <int FMT, bool GATEUP, int BM>
 __global__ __launch_bounds__(W4Cfg<BM>::Threads, W4Cfg<BM>::PerCU) void expert_mfma_w4_kernel(ExpertArgs a) {
     using C = W4Cfg<BM>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[C::Lds];
@@ -789,29 +876,29 @@ __global__ __launch_bounds__(W4Cfg<BM>::Threads, W4Cfg<BM>::PerCU) void expert_m
         const int live = (min(BM, g.n - m0) + 15) / 16;
         if constexpr (BM == 128) {
             if (live > 7)
-                pipe_tile_w4<GATEUP, BM, 8>(a, smem, g, m0, nt);
+                pipe_tile_w4<FMT, GATEUP, BM, 8>(a, smem, g, m0, nt);
             else if (live > 6)
-                pipe_tile_w4<GATEUP, BM, 7>(a, smem, g, m0, nt);
+                pipe_tile_w4<FMT, GATEUP, BM, 7>(a, smem, g, m0, nt);
             else if (live > 5)
-                pipe_tile_w4<GATEUP, BM, 6>(a, smem, g, m0, nt);
+                pipe_tile_w4<FMT, GATEUP, BM, 6>(a, smem, g, m0, nt);
             else if (live > 4)
-                pipe_tile_w4<GATEUP, BM, 5>(a, smem, g, m0, nt);
+                pipe_tile_w4<FMT, GATEUP, BM, 5>(a, smem, g, m0, nt);
             else if (live > 2)
-                pipe_tile_w4<GATEUP, BM, 4>(a, smem, g, m0, nt);
+                pipe_tile_w4<FMT, GATEUP, BM, 4>(a, smem, g, m0, nt);
             else
-                pipe_tile_w4<GATEUP, BM, 2>(a, smem, g, m0, nt);
+                pipe_tile_w4<FMT, GATEUP, BM, 2>(a, smem, g, m0, nt);
         } else if constexpr (BM == 64) {
             if (live > 3)
-                pipe_tile_w4<GATEUP, BM, 4>(a, smem, g, m0, nt);
+                pipe_tile_w4<FMT, GATEUP, BM, 4>(a, smem, g, m0, nt);
             else
-                pipe_tile_w4<GATEUP, BM, 3>(a, smem, g, m0, nt);
+                pipe_tile_w4<FMT, GATEUP, BM, 3>(a, smem, g, m0, nt);
         } else {
-            pipe_tile_w4<GATEUP, BM, 2>(a, smem, g, m0, nt);
+            pipe_tile_w4<FMT, GATEUP, BM, 2>(a, smem, g, m0, nt);
         }
     }
 }
 
-template <bool GATEUP, int BM>
+template <int FMT, bool GATEUP, int BM>
 static void launch_w4_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
     using C = W4Cfg<BM>;
     const int NT = GATEUP ? a.I / 64 : a.H / kBN;
@@ -819,19 +906,29 @@ static void launch_w4_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
     const long long ub = (long long)(BM == 128 ? 3 : 1) * a.mfma_cap * NT;
     if (ub < grid) grid = ub;
     grid = grid < 8 ? 8 : grid & ~7LL;  // the XCD walk deals blocks in groups of 8
-    expert_mfma_w4_kernel<GATEUP, BM><<<(int)grid, C::Threads, 0, st>>>(a);
+    expert_mfma_w4_kernel<FMT, GATEUP, BM><<<(int)grid, C::Threads, 0, st>>>(a);
+}
+
+template <int FMT>
+static void launch_w4_fmt(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st) {
+    if (gateup) {
+        launch_w4_bm<FMT, true, 128>(a, num_cu, st);
+        launch_w4_bm<FMT, true, 64>(a, num_cu, st);
+        launch_w4_bm<FMT, true, 32>(a, num_cu, st);
+    } else {
+        launch_w4_bm<FMT, false, 128>(a, num_cu, st);
+        launch_w4_bm<FMT, false, 64>(a, num_cu, st);
+        launch_w4_bm<FMT, false, 32>(a, num_cu, st);
+    }
 }
 
 void launch_mfma_w4(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st) {
-    if (gateup) {
-        launch_w4_bm<true, 128>(a, num_cu, st);
-        launch_w4_bm<true, 64>(a, num_cu, st);
-        launch_w4_bm<true, 32>(a, num_cu, st);
-    } else {
-        launch_w4_bm<false, 128>(a, num_cu, st);
-        launch_w4_bm<false, 64>(a, num_cu, st);
-        launch_w4_bm<false, 32>(a, num_cu, st);
-    }
+    if (a.fmt == 2)
+        launch_w4_fmt<2>(a, gateup, num_cu, st);
+    else if (a.fmt == 3)
+        launch_w4_fmt<3>(a, gateup, num_cu, st);
+    else
+        launch_w4_fmt<1>(a, gateup, num_cu, st);
     // the bf16 shared expert: one group of T rows, so one tile list (9 <= T
     // since no MFMA launch runs at T <= 8); the small-list launch walks the
     // three lists and skips the 4-bit groups

@@ -65,8 +65,29 @@ int32_t check_sizes(int32_t T, int32_t H, int32_t E, int32_t I, int32_t Is, int3
         (Is != 0 && (Is < 64 || Is % 64 != 0)) || E < 1 || E > MOE_MAX_E)
         return MOE_E_SHAPE;
     if (topk < 1 || topk > E || topk > MOE_MAX_TOPK) return MOE_E_TOPK;
-    if (fmt != MOE_BF16 && fmt != MOE_W4A16) return MOE_E_FORMAT;
+    if (fmt != MOE_BF16 && fmt != MOE_W4A16 && fmt != MOE_AFFINE4 && fmt != MOE_NVFP4) return MOE_E_FORMAT;
+    // MLX affine rows of bf16 scales (and biases) are K / 64 entries, read in
+    // 4-byte pieces: K a multiple of 128 keeps them whole and aligned
+    if (fmt == MOE_AFFINE4 && I % 128 != 0) return MOE_E_SHAPE;
     return MOE_OK;
+}
+
+// Inputs per scale group of a 4-bit format (0: bf16).
+int group_of(int fmt) {
+    return fmt == MOE_W4A16 ? 32 : (fmt == MOE_AFFINE4 ? 64 : (fmt == MOE_NVFP4 ? 16 : 0));
+}
+
+// The 4-bit arrays a format needs, in the order q, s, z of gate/up, q, s, z of
+// down, then the NVFP4 matrix scales (z unused by NVFP4, which needs g).
+int needed_arrays(const moe_experts* ex, const void** out) {
+    const bool nv = ex->fmt == MOE_NVFP4;
+    const void* all[8] = {ex->q_gate_up, ex->s_gate_up, nv ? nullptr : ex->z_gate_up, ex->q_down, ex->s_down,
+                          nv ? nullptr : ex->z_down, nv ? ex->g_gate_up : nullptr, nv ? ex->g_down : nullptr};
+    const bool need[8] = {true, true, !nv, true, true, !nv, nv, nv};
+    int n = 0;
+    for (int i = 0; i < 8; ++i)
+        if (need[i]) out[n++] = all[i];
+    return n;
 }
 
 struct DeviceInfo {
@@ -203,12 +224,14 @@ int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts*
     if (!x || !router_w || !experts || !out) return MOE_E_NULL;
     if (!x->ptr || !router_w->w || !out->y) return MOE_E_NULL;
     const int fmt = experts->fmt;
+    const void* qarr[8] = {};
+    int nq = 0;
     if (fmt == MOE_BF16) {
         if (!experts->w_gate_up || !experts->w_down) return MOE_E_NULL;
-    } else if (fmt == MOE_W4A16) {
-        if (!experts->q_gate_up || !experts->s_gate_up || !experts->z_gate_up || !experts->q_down ||
-            !experts->s_down || !experts->z_down)
-            return MOE_E_NULL;
+    } else if (group_of(fmt) > 0) {
+        nq = needed_arrays(experts, qarr);
+        for (int i = 0; i < nq; ++i)
+            if (!qarr[i]) return MOE_E_NULL;
     } else {
         return MOE_E_FORMAT;
     }
@@ -225,17 +248,16 @@ int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts*
         const int32_t rc = check_sizes(T, H, E, I, Is, topk, fmt);
         if (rc != MOE_OK) return rc;
     }
-    if (fmt == MOE_W4A16 && experts->group != 32) return MOE_E_FORMAT;
+    if (fmt != MOE_BF16 && experts->group != group_of(fmt)) return MOE_E_FORMAT;
     if (band_lo < 0 || band_hi > E || band_lo >= band_hi) return MOE_E_BAND;
     if (out->combine != MOE_COMBINE_PICK && out->combine != MOE_COMBINE_TREE) return MOE_E_COMBINE;
     if (x->norm_w && !(x->eps >= 0.0f && x->eps < INFINITY)) return MOE_E_SHAPE;
 
     const bool bf = fmt == MOE_BF16;
+    for (int i = 0; i < nq; ++i)
+        if (!aligned16(qarr[i])) return MOE_E_ALIGN;
     const void* ptrs[] = {x->ptr, router_w->w, router_w->bias,
                           bf ? experts->w_gate_up : nullptr, bf ? experts->w_down : nullptr,
-                          bf ? nullptr : experts->q_gate_up, bf ? nullptr : experts->s_gate_up,
-                          bf ? nullptr : experts->z_gate_up, bf ? nullptr : experts->q_down,
-                          bf ? nullptr : experts->s_down, bf ? nullptr : experts->z_down,
                           shared ? shared->w_gate_up : nullptr, shared ? shared->w_down : nullptr,
                           out->y, out->topk_ids, out->topk_w, out->counts, out->offsets,
                           out->perm, out->pos, static_ws ? nullptr : out->workspace,
@@ -349,6 +371,8 @@ int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts*
     a.qd = experts->q_down;
     a.sd = static_cast<const uint16_t*>(experts->s_down);
     a.zd = static_cast<const uint16_t*>(experts->z_down);
+    a.ggu = fmt == MOE_NVFP4 ? experts->g_gate_up : nullptr;
+    a.gd = fmt == MOE_NVFP4 ? experts->g_down : nullptr;
     a.Is = Is;
     a.swgu = shared ? static_cast<const uint16_t*>(shared->w_gate_up) : nullptr;
     a.swd = shared ? static_cast<const uint16_t*>(shared->w_down) : nullptr;
@@ -536,27 +560,22 @@ extern "C" int32_t moe_tp_slice_experts(const moe_experts* src, int32_t i_lo, in
                                         const moe_experts* dst, void* stream) {
     if (!src || !dst) return MOE_E_NULL;
     const int fmt = src->fmt;
-    if (fmt != MOE_BF16 && fmt != MOE_W4A16) return MOE_E_FORMAT;
-    if (dst->fmt != fmt || (fmt == MOE_W4A16 && (src->group != 32 || dst->group != 32)))
-        return MOE_E_FORMAT;
+    if (fmt != MOE_BF16 && group_of(fmt) == 0) return MOE_E_FORMAT;
+    const int G = group_of(fmt);
+    if (dst->fmt != fmt || (G > 0 && (src->group != G || dst->group != G))) return MOE_E_FORMAT;
     const int E = src->E, H = src->H, I = src->I;
-    if (E < 1 || E > MOE_MAX_E || H < 256 || H % 256 != 0 || I < 64 || I % 64 != 0)
+    // whole 64-column units, 128 for MLX affine (whose experts need I % 128 == 0)
+    const int unit = fmt == MOE_AFFINE4 ? 128 : 64;
+    if (E < 1 || E > MOE_MAX_E || H < 256 || H % 256 != 0 || I < unit || I % unit != 0)
         return MOE_E_SHAPE;
-    if (i_lo < 0 || i_hi > I || i_lo >= i_hi || i_lo % 64 != 0 || i_hi % 64 != 0) return MOE_E_SHAPE;
+    if (i_lo < 0 || i_hi > I || i_lo >= i_hi || i_lo % unit != 0 || i_hi % unit != 0) return MOE_E_SHAPE;
     if (dst->E != E || dst->H != H || dst->I != i_hi - i_lo) return MOE_E_SHAPE;
-    const void* need_src[6] = {src->w_gate_up, src->w_down, nullptr, nullptr, nullptr, nullptr};
-    const void* need_dst[6] = {dst->w_gate_up, dst->w_down, nullptr, nullptr, nullptr, nullptr};
+    const void* need_src[8] = {src->w_gate_up, src->w_down};
+    const void* need_dst[8] = {dst->w_gate_up, dst->w_down};
     int nneed = 2;
-    if (fmt == MOE_W4A16) {
-        const void* s6[6] = {src->q_gate_up, src->s_gate_up, src->z_gate_up, src->q_down,
-                             src->s_down, src->z_down};
-        const void* d6[6] = {dst->q_gate_up, dst->s_gate_up, dst->z_gate_up, dst->q_down,
-                             dst->s_down, dst->z_down};
-        for (int i = 0; i < 6; ++i) {
-            need_src[i] = s6[i];
-            need_dst[i] = d6[i];
-        }
-        nneed = 6;
+    if (G > 0) {
+        nneed = needed_arrays(src, need_src);
+        needed_arrays(dst, need_dst);
     }
     for (int i = 0; i < nneed; ++i) {
         if (!need_src[i] || !need_dst[i]) return MOE_E_NULL;
@@ -572,20 +591,33 @@ extern "C" int32_t moe_tp_slice_experts(const moe_experts* src, int32_t i_lo, in
             e = copy_cols(const_cast<void*>(dst->w_down), src->w_down, (size_t)E * H, (size_t)I * 2, (size_t)i_lo * 2,
                           n * 2, st);
     } else {
-        e = copy_gate_up(const_cast<void*>((const void*)dst->q_gate_up), src->q_gate_up, E, I, i_lo, i_hi, (size_t)H / 2, st);
-        if (e == hipSuccess)
-            e = copy_gate_up(const_cast<void*>((const void*)dst->s_gate_up), src->s_gate_up, E, I, i_lo, i_hi, (size_t)H / 16, st);
-        if (e == hipSuccess)
-            e = copy_gate_up(const_cast<void*>((const void*)dst->z_gate_up), src->z_gate_up, E, I, i_lo, i_hi, (size_t)H / 16, st);
-        if (e == hipSuccess)
-            e = copy_cols(const_cast<void*>((const void*)dst->q_down), src->q_down, (size_t)E * H, (size_t)I / 2,
-                          (size_t)i_lo / 2, n / 2, st);
-        if (e == hipSuccess)
-            e = copy_cols(const_cast<void*>((const void*)dst->s_down), src->s_down, (size_t)E * H, (size_t)I / 16,
-                          (size_t)i_lo / 16, n / 16, st);
-        if (e == hipSuccess)
-            e = copy_cols(const_cast<void*>((const void*)dst->z_down), src->z_down, (size_t)E * H, (size_t)I / 16,
-                          (size_t)i_lo / 16, n / 16, st);
+        // bytes of a per-group array per input: a bf16 per G inputs, or an
+        // E4M3 byte per 16 (NVFP4)
+        const size_t per = fmt == MOE_NVFP4 ? 16 : (size_t)G / 2;  // inputs per byte
+        auto cu = [&](const void* d, const void* s_, size_t row_bytes) {
+            if (e == hipSuccess) e = copy_gate_up(const_cast<void*>(d), s_, E, I, i_lo, i_hi, row_bytes, st);
+        };
+        auto cd = [&](const void* d, const void* s_, size_t in_per_byte) {
+            if (e == hipSuccess)
+                e = copy_cols(const_cast<void*>(d), s_, (size_t)E * H, (size_t)I / in_per_byte,
+                              (size_t)i_lo / in_per_byte, n / in_per_byte, st);
+        };
+        cu(dst->q_gate_up, src->q_gate_up, (size_t)H / 2);
+        cu(dst->s_gate_up, src->s_gate_up, (size_t)H / per);
+        cd(dst->q_down, src->q_down, 2);
+        cd(dst->s_down, src->s_down, per);
+        if (fmt == MOE_NVFP4) {
+            // the matrix scales belong to whole matrices: every slice keeps them
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(const_cast<float*>(dst->g_gate_up), src->g_gate_up, (size_t)E * 2 * 4,
+                                   hipMemcpyDeviceToDevice, st);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(const_cast<float*>(dst->g_down), src->g_down, (size_t)E * 4,
+                                   hipMemcpyDeviceToDevice, st);
+        } else {
+            cu(dst->z_gate_up, src->z_gate_up, (size_t)H / per);
+            cd(dst->z_down, src->z_down, per);
+        }
     }
     if (e != hipSuccess) return MOE_E_HIP;
     return MOE_OK;

@@ -76,6 +76,7 @@ def test_constants_match_header():
     assert define("MOE_MAX_TOPK") == moe.MOE_MAX_TOPK
     assert define("MOE_MAX_E") == moe.MOE_MAX_E
     assert define("MOE_BF16") == moe.MOE_BF16 and define("MOE_W4A16") == moe.MOE_W4A16
+    assert define("MOE_AFFINE4") == moe.MOE_AFFINE4 and define("MOE_NVFP4") == moe.MOE_NVFP4
     m = re.search(r"#define MOE_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert int(m.group(1)) << int(m.group(2)) == moe.MOE_STATIC_SCRATCH_BYTES
 
@@ -108,7 +109,7 @@ def _call(T=4, H=256, E=8, I=128, Is=128, topk=2, lo=0, hi=8, fmt=0, group=32, r
           eH=None, sH=None, shared=True, ws_bytes=None, null=None, misalign=None):
     ptr = {name: A * (i + 1) for i, name in enumerate(
         ["x", "wr", "bias", "wgu", "wd", "qgu", "sgu", "zgu", "qd", "sd", "zd", "swgu", "swd",
-         "y", "ws"])}
+         "y", "ws", "ggu", "gd"])}
     if null:
         ptr[null] = None
     if misalign:
@@ -116,9 +117,9 @@ def _call(T=4, H=256, E=8, I=128, Is=128, topk=2, lo=0, hi=8, fmt=0, group=32, r
     dx = moe.MoeX(ptr["x"], T, H)
     dr = moe.MoeRouter(ptr["wr"], ptr["bias"], E if rE is None else rE, H if rH is None else rH)
     de = moe.MoeExperts(E, H if eH is None else eH, I, fmt, group, ptr["wgu"], ptr["wd"], ptr["qgu"],
-                        ptr["sgu"], ptr["zgu"], ptr["qd"], ptr["sd"], ptr["zd"])
+                        ptr["sgu"], ptr["zgu"], ptr["qd"], ptr["sd"], ptr["zd"], ptr["ggu"], ptr["gd"])
     ds = moe.MoeShared(Is, H if sH is None else sH, ptr["swgu"], ptr["swd"]) if shared else None
-    need = moe.workspace_bytes(T, H, E, I, Is if shared else 0, max(1, min(topk, 16)), fmt if fmt in (0, 1) else 0)
+    need = moe.workspace_bytes(T, H, E, I, Is if shared else 0, max(1, min(topk, 16)), fmt if fmt in (0, 1, 2, 3) else 0)
     do = moe.MoeOut(ptr["y"], None, None, None, None, None, None, ptr["ws"],
                     need if ws_bytes is None else ws_bytes, None)
     lib = moe.load_library()
@@ -150,8 +151,16 @@ def _call(T=4, H=256, E=8, I=128, Is=128, topk=2, lo=0, hi=8, fmt=0, group=32, r
     (dict(topk=0), -5),
     (dict(topk=9), -5),  # more picks than experts
     (dict(topk=17, E=32, hi=32), -5),
-    (dict(fmt=2), -6),
+    (dict(fmt=2), -6),  # MLX affine with 32-input groups
     (dict(fmt=1, group=64), -6),
+    (dict(fmt=3, group=32), -6),
+    (dict(fmt=4), -6),
+    (dict(fmt=2, group=64, I=192), -2),  # MLX affine needs I % 128 == 0
+    (dict(fmt=2, group=64, null="zd"), -1),  # the biases
+    (dict(fmt=3, group=16, null="ggu"), -1),  # the matrix scales
+    (dict(fmt=3, group=16, null="gd"), -1),
+    (dict(fmt=3, group=16, null="sd"), -1),
+    (dict(fmt=3, group=16, misalign="ggu"), -8),
     (dict(ws_bytes=1024), -7),
     (dict(null="ws"), -7),
     (dict(misalign="x"), -8),
@@ -167,6 +176,9 @@ def test_unused_format_pointers_ignored():
     # bf16 experts: the 4-bit pointers may be anything (here: misaligned).
     assert _call(misalign="qgu", ws_bytes=1024) == -7
     assert _call(fmt=1, misalign="wgu", ws_bytes=1024) == -7
+    # NVFP4 has no zeros; W4A16 and MLX affine no matrix scales
+    assert _call(fmt=3, group=16, null="zgu", ws_bytes=1024) == -7
+    assert _call(fmt=2, group=64, null="ggu", ws_bytes=1024) == -7
 
 
 def test_python_binding_raises(monkeypatch):

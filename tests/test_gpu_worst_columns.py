@@ -31,7 +31,7 @@ BASE = synth.Workload("classes", T=1, H=6144, E=8, topk=4, I=2048, Is=0)
 CLASSES = [("gemv", 5), ("mfma32", 20), ("mfma64", 50), ("mfma128", 100), ("mfma256", 300)]
 
 
-@pytest.fixture(scope="module", params=["bf16", "w4"])
+@pytest.fixture(scope="module", params=["bf16", "w4", "affine4", "nvfp4"])
 def experts(request):
     w = BASE.with_(fmt=request.param)
     return w, synth.make_experts(w, "cuda")
