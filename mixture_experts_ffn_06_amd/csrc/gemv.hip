@@ -347,9 +347,15 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
     }
 }
 
-template <int FMT, int CB>
+// MAXNR: the most rows a group of the launch has (1 at T = 1: the one-row
+// kernels need fewer registers, so two blocks fit on a CU).
+template <int FMT, int CB, int MAXNR>
 __device__ __forceinline__ void gateup_dispatch_rows(const ExpertArgs& a, const Group& g, int c0,
                                                      const uint16_t* xs, const float* xsum) {
+    if constexpr (MAXNR == 1) {
+        gateup_item<FMT, 1, CB>(a, g, c0, xs, xsum);
+        return;
+    }
     switch (g.n) {
         case 1: gateup_item<FMT, 1, CB>(a, g, c0, xs, xsum); break;
         case 2: gateup_item<FMT, 2, CB>(a, g, c0, xs, xsum); break;
@@ -504,8 +510,10 @@ __device__ __forceinline__ void item_of(const ExpertArgs& a, int it, int nrouted
 
 // FMT: the routed experts' format (0 bf16, 1 W4A16, 2 MLX affine, 3 NVFP4);
 // the shared expert is bf16 in every format.
-template <int FMT, int CB>
-__global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a, int lds_rows) {
+// (launch bounds: at least 4 waves per SIMD, i.e. two blocks per CU, for the
+// one-row kernels)
+template <int FMT, int CB, int MAXNR>
+__global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? 4 : 1) void gateup_gemv_kernel(ExpertArgs a, int lds_rows) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     float* xsum = reinterpret_cast<float*>(smem + (size_t)lds_rows * a.H * 2);
@@ -539,9 +547,9 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
             const bool restage = m.gi != cur;
             if (restage) buf ^= 1;
             uint16_t* xb = xs + (size_t)buf * 2 * a.H;
-            if (g.n == 1)
+            if (MAXNR == 1 || g.n == 1)
                 mn = gateup_fast<1, CB>(a, m, restage, xb, has_next, itn, nrouted, TR);
-            else
+            else if constexpr (MAXNR > 1)
                 mn = gateup_fast<2, CB>(a, m, restage, xb, has_next, itn, nrouted, TR);
             cur = m.gi;
             staged = -1;  // its buffers overlap the synchronous staging area
@@ -556,9 +564,9 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(ExpertArgs a,
             }
             if (has_next) mn = load_meta(a, itn, nrouted, TR);
             if (w4)
-                gateup_dispatch_rows<FMT, CB>(a, g, m.tile * kGuCols, xs, xsum);
+                gateup_dispatch_rows<FMT, CB, MAXNR>(a, g, m.tile * kGuCols, xs, xsum);
             else
-                gateup_dispatch_rows<0, CB>(a, g, m.tile * kGuCols, xs, xsum);
+                gateup_dispatch_rows<0, CB, MAXNR>(a, g, m.tile * kGuCols, xs, xsum);
             // The next item overwrites these rows only if it stages others
             // (or takes the fast path, whose buffers overlap them); one-row
             // groups of the same token and format keep them, and need no
@@ -753,9 +761,13 @@ __device__ void down_fast(const ExpertArgs& a, const Group& g, int n0, bool rest
     }
 }
 
-template <int FMT>
+template <int FMT, int MAXNR>
 __device__ __forceinline__ void down_dispatch_rows(const ExpertArgs& a, const Group& g, int n0,
                                                    const uint16_t* xs, const float* xsum) {
+    if constexpr (MAXNR == 1) {
+        down_item<FMT, 1>(a, g, n0, xs, xsum);
+        return;
+    }
     switch (g.n) {
         case 1: down_item<FMT, 1>(a, g, n0, xs, xsum); break;
         case 2: down_item<FMT, 2>(a, g, n0, xs, xsum); break;
@@ -768,9 +780,9 @@ __device__ __forceinline__ void down_dispatch_rows(const ExpertArgs& a, const Gr
     }
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, int lds_rows,
-                                                                 int kmax) {
+template <int FMT, int MAXNR>
+__global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? 4 : 1) void down_gemv_kernel(ExpertArgs a, int lds_rows,
+                                                                                    int kmax) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     float* xsum = reinterpret_cast<float*>(smem + (size_t)lds_rows * kmax * 2);
@@ -796,9 +808,9 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, i
             const bool restage = gi != fcur;
             if (restage) buf ^= 1;
             uint16_t* xb = xs + (size_t)buf * 2 * K;
-            if (g.n == 1)
+            if (MAXNR == 1 || g.n == 1)
                 down_fast<1>(a, g, tile * kDnCols, restage, xb);
-            else
+            else if constexpr (MAXNR > 1)
                 down_fast<2>(a, g, tile * kDnCols, restage, xb);
             fcur = gi;
             scur = -1;
@@ -812,9 +824,9 @@ __global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(ExpertArgs a, i
             scur = gi;
         }
         if (w4)
-            down_dispatch_rows<FMT>(a, g, tile * kDnCols, xs, xsum);
+            down_dispatch_rows<FMT, MAXNR>(a, g, tile * kDnCols, xs, xsum);
         else
-            down_dispatch_rows<0>(a, g, tile * kDnCols, xs, xsum);
+            down_dispatch_rows<0, MAXNR>(a, g, tile * kDnCols, xs, xsum);
         fcur = -1;
         prev_slow = true;
     }
@@ -827,20 +839,34 @@ static int gemv_grid(size_t lds, int num_cu, long long ub) {
     return (int)(g < 1 ? 1 : g);
 }
 
-template <int FMT, int CB>
+template <int FMT, int CB, int MAXNR>
 static void launch_gateup_fmt(const ExpertArgs& a, int grid, size_t lds, int lds_rows, hipStream_t st) {
-    allow_lds(gateup_gemv_kernel<FMT, CB>, lds);
-    gateup_gemv_kernel<FMT, CB><<<grid, kGemvThreads, lds, st>>>(a, lds_rows);
+    allow_lds(gateup_gemv_kernel<FMT, CB, MAXNR>, lds);
+    gateup_gemv_kernel<FMT, CB, MAXNR><<<grid, kGemvThreads, lds, st>>>(a, lds_rows);
 }
 
+// 4-bit experts at T = 1 take the one-row kernels (two blocks per CU; their
+// bf16 path, for the shared expert when the top-k launch has not done it,
+// loads at most 8 lane steps at a time to stay within 128 registers).
 template <int CB>
 static void launch_gateup_cb(const ExpertArgs& a, int grid, size_t lds, int lds_rows,
                              hipStream_t st) {
+    constexpr int CB1 = CB < 8 ? CB : 8;
+    const bool one = a.T == 1;
     switch (a.fmt) {
-        case 1: launch_gateup_fmt<1, CB>(a, grid, lds, lds_rows, st); break;
-        case 2: launch_gateup_fmt<2, CB>(a, grid, lds, lds_rows, st); break;
-        case 3: launch_gateup_fmt<3, CB>(a, grid, lds, lds_rows, st); break;
-        default: launch_gateup_fmt<0, CB>(a, grid, lds, lds_rows, st); break;
+        case 1:
+            one ? launch_gateup_fmt<1, CB1, 1>(a, grid, lds, lds_rows, st)
+                : launch_gateup_fmt<1, CB, 8>(a, grid, lds, lds_rows, st);
+            break;
+        case 2:
+            one ? launch_gateup_fmt<2, CB1, 1>(a, grid, lds, lds_rows, st)
+                : launch_gateup_fmt<2, CB, 8>(a, grid, lds, lds_rows, st);
+            break;
+        case 3:
+            one ? launch_gateup_fmt<3, CB1, 1>(a, grid, lds, lds_rows, st)
+                : launch_gateup_fmt<3, CB, 8>(a, grid, lds, lds_rows, st);
+            break;
+        default: launch_gateup_fmt<0, CB, 8>(a, grid, lds, lds_rows, st); break;
     }
 }
 
@@ -871,8 +897,13 @@ void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream
     const int grid = gemv_grid(lds, num_cu, (long long)max_groups * (a.H / kDnCols));
     auto go = [&](auto fmt) {
         constexpr int F = decltype(fmt)::value;
-        allow_lds(down_gemv_kernel<F>, lds);
-        down_gemv_kernel<F><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
+        if (a.T == 1) {  // one-row kernels: two blocks per CU
+            allow_lds(down_gemv_kernel<F, 1>, lds);
+            down_gemv_kernel<F, 1><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
+        } else {
+            allow_lds(down_gemv_kernel<F, 8>, lds);
+            down_gemv_kernel<F, 8><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
+        }
     };
     switch (a.fmt) {
         case 1: go(std::integral_constant<int, 1>{}); break;
