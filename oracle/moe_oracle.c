@@ -436,6 +436,26 @@ int oracle_tree_merge(int E, int nparts, const int32_t* lo, const int32_t* hi,
     return ok ? OR_OK : OR_EINVAL;
 }
 
+/* Sum of rank partials in rank order.  [P4] (maintainer reply and the      */
+/* --tp 3 comments): each rank returns a full-width fp32 partial and the      */
+/* partials are added in rank order, so the sum is a left fold: ((p0 + p1) +  */
+/* p2) + ..., each addition one fp32 rounding; the shared expert's output     */
+/* (when not NULL) is added after the partials and the bf16 residual (when    */
+/* not NULL, widened exactly) last.  parts [nparts][n], out [n].             */
+int oracle_rank_merge(int nparts, const float* const* parts, const float* shared, const uint16_t* residual,
+                      size_t n, float* out)
+{
+    if (nparts < 1) return OR_EINVAL;
+    for (size_t c = 0; c < n; ++c) {
+        float v = parts[0][c];
+        for (int p = 1; p < nparts; ++p) v = v + parts[p][c];
+        if (shared) v = v + shared[c];
+        if (residual) v = v + bf16_to_f32(residual[c]);
+        out[c] = v;
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Tensor-parallel shares.                                                    */
 /*                                                                            */

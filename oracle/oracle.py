@@ -104,6 +104,8 @@ def _load():
         lib.oracle_tp_shares.argtypes = [I32, I32, I32, P]
         lib.oracle_tree_merge.restype = I32
         lib.oracle_tree_merge.argtypes = [I32, I32, P, P, P, P, ctypes.c_size_t, P]
+        lib.oracle_rank_merge.restype = I32
+        lib.oracle_rank_merge.argtypes = [I32, P, P, P, ctypes.c_size_t, P]
         lib.oracle_moe_ffn_monolith.restype = I32
         lib.oracle_moe_ffn_monolith.argtypes = layer + [I32, P, I32, P]
         _lib = lib
@@ -334,6 +336,21 @@ def tree_merge(parts, bands, E: int, shared: Optional[torch.Tensor] = None) -> t
     out = torch.empty(n, dtype=torch.float32)
     _check(_load().oracle_tree_merge(E, len(ps), _ptr(lo), _ptr(hi), ctypes.cast(arr, ctypes.c_void_p),
                                      _ptr(sh), n, _ptr(out)), "tree_merge")
+    return out.reshape(ps[0].shape)
+
+
+def rank_merge(parts, shared: Optional[torch.Tensor] = None,
+               residual: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 rank partials added in rank order (a left fold), then + shared,
+    then + the bf16 residual."""
+    ps = [_cpu(p).float().contiguous() for p in parts]
+    n = ps[0].numel()
+    arr = (ctypes.c_void_p * len(ps))(*[p.data_ptr() for p in ps])
+    sh = None if shared is None else _cpu(shared).float().contiguous()
+    res = None if residual is None else _cpu(residual).to(torch.bfloat16).contiguous().view(torch.int16)
+    out = torch.empty(n, dtype=torch.float32)
+    _check(_load().oracle_rank_merge(len(ps), ctypes.cast(arr, ctypes.c_void_p), _ptr(sh), _ptr(res), n,
+                                     _ptr(out)), "rank_merge")
     return out.reshape(ps[0].shape)
 
 

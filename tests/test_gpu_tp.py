@@ -84,11 +84,8 @@ def test_tp_layer_adds_up_to_the_whole_layer(fmt, unit, ranks):
     assert drift <= 1e-3 * scale
     side = OracleSide(w, d)
     compare(y, side.layer(list(range(w.T)), 0, w.E), f"tp {fmt} {unit}x{ranks}")
-    # the rank-order sum is a plain left fold of the partials
-    acc = parts[0]
-    for p in parts[1:]:
-        acc = acc + p
-    assert torch.equal(y, acc)
+    # the rank-order sum, bit for bit the oracle's merge of the same partials
+    assert torch.equal(y.cpu(), orc.rank_merge([p.cpu() for p in parts]))
 
 
 def test_tp_decode_full_size_three_ranks():

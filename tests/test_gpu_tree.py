@@ -186,18 +186,21 @@ def test_reduce_tree_matches_the_oracle_merge(E):
         assert torch.equal(_bits(y), _bits(want)), (E, trial, bands)
 
 
-def test_reduce_rank_order_is_the_left_fold():
-    g = torch.Generator().manual_seed(3)
+@pytest.mark.parametrize("nparts", [1, 2, 5, 8])
+def test_reduce_rank_order_matches_the_oracle(nparts):
+    # partials of very different scales (fp32 addition is not associative on
+    # them), the shared output and a residual: bit-exact against the oracle's
+    # rank-order merge
+    g = torch.Generator().manual_seed(3 + nparts)
     T, H = 5, 768
-    parts = [(torch.randn(T, H, generator=g) * 10.0 ** (3 * i)).cuda() for i in range(5)]
+    parts = [(torch.randn(T, H, generator=g) * 10.0 ** (3 * (i % 4))).cuda() for i in range(nparts)]
     sh = torch.randn(T, H, generator=g).cuda()
     res = torch.randn(T, H, generator=g).to(torch.bfloat16).cuda()
     y = moe.reduce(parts, "rank", y_shared=sh, residual=res)
-    want = parts[0]
-    for p in parts[1:]:
-        want = want + p
-    want = (want + sh) + res.float()
-    assert torch.equal(_bits(y), _bits(want))
+    want = orc.rank_merge([p.cpu() for p in parts], shared=sh.cpu(), residual=res.cpu())
+    assert torch.equal(_bits(y.cpu()), _bits(want))
+    y2 = moe.reduce(parts, "rank")
+    assert torch.equal(_bits(y2.cpu()), _bits(orc.rank_merge([p.cpu() for p in parts])))
 
 
 def test_reduce_rejects_bad_parts():
