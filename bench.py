@@ -144,10 +144,10 @@ def roofline_for(w, counts, stage_ms, counted=True):
     nbytes = wbytes + act
     flops = 2.0 * routed * 2 * w.I * w.H + 2.0 * sh_rows * 2 * w.Is * w.H
     if w.T <= 8:
-        # (one-row 4-bit calls take the one-row kernel, whose bf16 path loads 8
+        # (one-row 4-bit calls take the one-row kernel, whose bf16 path loads 4
         # lane steps at a time; H = 6144 otherwise takes 12)
         one = w.T == 1 and w.fmt != "bf16"
-        cb = min(8 if one else 12, max(4, -(-((w.H + 511) // 512) // 4) * 4))
+        cb = min(4 if one else 12, max(4, -(-((w.H + 511) // 512) // 4) * 4))
         kernel = f"gateup_gemv_kernel<{FMT_CODE[w.fmt]},{cb},{1 if one else 8}>"
         ms = stage_ms["gu_gemv"]
         traffic = measured_traffic(w.name, [f"moe::{kernel}"])

@@ -510,10 +510,14 @@ __device__ __forceinline__ void item_of(const ExpertArgs& a, int it, int nrouted
 
 // FMT: the routed experts' format (0 bf16, 1 W4A16, 2 MLX affine, 3 NVFP4);
 // the shared expert is bf16 in every format.
-// (launch bounds: at least 4 waves per SIMD, i.e. two blocks per CU, for the
-// one-row kernels)
+// Launch bounds of the one-row kernels, in waves per SIMD: 6 (at most 80
+// registers, three blocks per CU) where that needs no spills -- the 4-bit down
+// kernels and the NVFP4 gate/up kernel -- else 4 (two blocks per CU; W4A16 and
+// MLX affine gate/up items hold a scale and a zero or bias per step and row).
+constexpr int one_row_waves(int fmt, bool gateup) { return fmt == 0 ? 4 : (gateup && fmt != 3 ? 4 : 6); }
+
 template <int FMT, int CB, int MAXNR>
-__global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? 4 : 1) void gateup_gemv_kernel(ExpertArgs a, int lds_rows) {
+__global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? one_row_waves(FMT, true) : 1) void gateup_gemv_kernel(ExpertArgs a, int lds_rows) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     float* xsum = reinterpret_cast<float*>(smem + (size_t)lds_rows * a.H * 2);
@@ -587,17 +591,20 @@ __global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? 4 : 1) void gateup_gemv_
 // ---- down ------------------------------------------------------------------
 
 // One work item: output columns n0 .. n0+63 of group g; wave w owns 8 of them,
-// streamed as two passes of 4 rows of the down weight (16 loads in flight).
-template <int FMT, int NR>
+// streamed as passes of UP rows of the down weight (UP = 4: 16 loads in
+// flight for a bf16 row of K = 2048; each column's arithmetic is the same
+// whatever UP).
+template <int FMT, int NR, int UP = 4>
 __device__ void down_item(const ExpertArgs& a, const Group& g, int n0, const uint16_t* xs,
                           const float* xsum) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const bool shared = g.expert < 0;
     const int K = shared ? a.Is : a.I;
     const int H = a.H;
-    constexpr int U = kDnCols / kGemvWaves / 2;  // 4 columns per pass, two passes
-    for (int pass = 0; pass < 2; ++pass) {
-    const int cbase = n0 + 2 * U * wave + U * pass;
+    constexpr int U = UP;
+    constexpr int CW = kDnCols / kGemvWaves;  // columns per wave
+    for (int pass = 0; pass < CW / U; ++pass) {
+    const int cbase = n0 + CW * wave + U * pass;
     float acc[U][NR];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -765,7 +772,7 @@ template <int FMT, int MAXNR>
 __device__ __forceinline__ void down_dispatch_rows(const ExpertArgs& a, const Group& g, int n0,
                                                    const uint16_t* xs, const float* xsum) {
     if constexpr (MAXNR == 1) {
-        down_item<FMT, 1>(a, g, n0, xs, xsum);
+        down_item<FMT, 1, FMT == 0 ? 2 : 4>(a, g, n0, xs, xsum);
         return;
     }
     switch (g.n) {
@@ -781,7 +788,7 @@ __device__ __forceinline__ void down_dispatch_rows(const ExpertArgs& a, const Gr
 }
 
 template <int FMT, int MAXNR>
-__global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? 4 : 1) void down_gemv_kernel(ExpertArgs a, int lds_rows,
+__global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? one_row_waves(FMT, false) : 1) void down_gemv_kernel(ExpertArgs a, int lds_rows,
                                                                                     int kmax) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
@@ -832,8 +839,10 @@ __global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? 4 : 1) void down_gemv_ke
     }
 }
 
-static int gemv_grid(size_t lds, int num_cu, long long ub) {
-    int occ = lds <= 64 * 1024 ? 2 : 1;
+// blocks per CU: three for the one-row kernels bounded to 6 waves per SIMD
+// when their LDS allows
+static int gemv_grid(size_t lds, int num_cu, long long ub, bool six_waves = false) {
+    int occ = six_waves && lds <= 53 * 1024 ? 3 : (lds <= 64 * 1024 ? 2 : 1);
     long long g = (long long)num_cu * occ;
     if (ub < g) g = ub;
     return (int)(g < 1 ? 1 : g);
@@ -845,13 +854,13 @@ static void launch_gateup_fmt(const ExpertArgs& a, int grid, size_t lds, int lds
     gateup_gemv_kernel<FMT, CB, MAXNR><<<grid, kGemvThreads, lds, st>>>(a, lds_rows);
 }
 
-// 4-bit experts at T = 1 take the one-row kernels (two blocks per CU; their
-// bf16 path, for the shared expert when the top-k launch has not done it,
-// loads at most 8 lane steps at a time to stay within 128 registers).
+// 4-bit experts at T = 1 take the one-row kernels; their bf16 path, for the
+// shared expert when the top-k launch has not done it, loads at most 4 lane
+// steps at a time to stay within the registers of two or three blocks per CU.
 template <int CB>
 static void launch_gateup_cb(const ExpertArgs& a, int grid, size_t lds, int lds_rows,
                              hipStream_t st) {
-    constexpr int CB1 = CB < 8 ? CB : 8;
+    constexpr int CB1 = CB < 4 ? CB : 4;
     const bool one = a.T == 1;
     switch (a.fmt) {
         case 1:
@@ -876,7 +885,7 @@ void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStre
     const int lds_rows = max_rows > 4 ? max_rows : 4;
     const size_t lds = (size_t)lds_rows * a.H * 2 + (a.fmt ? (size_t)max_rows * (a.H / 32) * 4 : 0);
     const int tiles = (a.I > a.Is ? a.I : a.Is) / kGuCols;
-    const int grid = gemv_grid(lds, num_cu, (long long)max_groups * tiles);
+    const int grid = gemv_grid(lds, num_cu, (long long)max_groups * tiles, a.T == 1 && one_row_waves(a.fmt, true) == 6);
     // lane steps per load block for bf16 rows: the whole row when it has at
     // most 12 steps of 512 inputs (H <= 6144)
     const int nch = (a.H + 511) / 512;
@@ -894,7 +903,8 @@ void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream
     // rows of LDS: the largest group, and at least two buffers of two rows
     const int lds_rows = max_rows > 4 ? max_rows : 4;
     const size_t lds = (size_t)lds_rows * kmax * 2 + (a.fmt ? (size_t)max_rows * (kmax / 32) * 4 : 0);
-    const int grid = gemv_grid(lds, num_cu, (long long)max_groups * (a.H / kDnCols));
+    const int grid = gemv_grid(lds, num_cu, (long long)max_groups * (a.H / kDnCols),
+                               a.T == 1 && one_row_waves(a.fmt, false) == 6);
     auto go = [&](auto fmt) {
         constexpr int F = decltype(fmt)::value;
         if (a.T == 1) {  // one-row kernels: two blocks per CU
