@@ -54,15 +54,15 @@ def _capture_and_replay(w, d, replays=3, **opts):
     log(f"{w.name}: {replays} replays equal the eager call")
 
 
-@pytest.mark.parametrize("wname", ["decode", "w4_t1"])
+@pytest.mark.parametrize("wname", ["decode", "w4_t1", "affine4_t1", "nvfp4_t1"])
 def test_graph_replay_full_size(wname):
     w = W[wname]
     _capture_and_replay(w, gpu_inputs(w))
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "w4"])
+@pytest.mark.parametrize("fmt", ["bf16", "w4", "affine4", "nvfp4"])
 def test_graph_replay_mfma_lists_and_multiblock_dispatch(fmt):
-    w = MID.with_(fmt=fmt)
+    w = MID.with_(fmt=fmt, I=256 if fmt == "affine4" else MID.I)  # MLX affine needs I % 128 == 0
     d = gpu_inputs(w)
     d["bias"] = (-0.35 * torch.arange(w.E, dtype=torch.float32)).cuda()  # groups of 0 to > 256 rows
     _capture_and_replay(w, d)

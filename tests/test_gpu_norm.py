@@ -72,9 +72,9 @@ def test_normed_rows_adversarial():
     assert abs(float(inv[0]) - 316.2278) < 1e-3
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "w4"])
+@pytest.mark.parametrize("fmt", ["bf16", "w4", "affine4", "nvfp4"])
 def test_norm_and_residual_layer_against_the_oracle(fmt):
-    w = MID.with_(fmt=fmt)
+    w = MID.with_(fmt=fmt, I=256 if fmt == "affine4" else MID.I)  # MLX affine needs I % 128 == 0
     d = gpu_inputs(w)
     gamma = _gamma(w.H, 3)
     y, ex = _run(w, d, gamma, residual=True)

@@ -41,7 +41,8 @@ def _call(w, d, lo, hi, combine="tree", shared=True, y_shared=None, y_picks=None
     return y
 
 
-@pytest.mark.parametrize("wname,fmt", [("mid", "bf16"), ("odd", "bf16"), ("odd", "w4")])
+@pytest.mark.parametrize("wname,fmt", [("mid", "bf16"), ("odd", "bf16"), ("odd", "w4"), ("odd", "affine4"),
+                                      ("odd", "nvfp4")])
 def test_tree_combine_bit_exact_from_gpu_leaves(wname, fmt):
     w = {"mid": MID, "odd": ODD}[wname].with_(fmt=fmt)
     d = gpu_inputs(w)
@@ -85,9 +86,9 @@ def test_shared_apart_pick_order_bit_exact():
     assert torch.equal(_bits(y + ysh), _bits(y_add))
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "w4"])
+@pytest.mark.parametrize("fmt", ["bf16", "w4", "affine4", "nvfp4"])
 def test_tree_combine_against_the_oracle_layer(fmt):
-    w = MID.with_(fmt=fmt)
+    w = MID.with_(fmt=fmt, I=256 if fmt == "affine4" else MID.I)  # MLX affine needs I % 128 == 0
     d = gpu_inputs(w)
     d["bias"] = (-0.5 * torch.arange(w.E, dtype=torch.float32)).cuda()
     side = OracleSide(w, d)

@@ -2,7 +2,7 @@
 allocation in the call) against moe_ffn (caller's workspace): the same
 kernels, so outputs and every routing export must agree bit for bit.  Two
 calls in a row, the second with fewer rows, so the second reuses the array
-the first left full; in both weight formats, on the GEMV and MFMA paths.
+the first left full; in every weight format, on the GEMV and MFMA paths.
 """
 
 import pytest
@@ -16,6 +16,7 @@ pytestmark = pytest.mark.gpu
 
 BIG = synth.Workload("noalloc", T=100, H=2048, E=64, topk=8, I=512, Is=256)
 EXPORTS = ("topk_ids", "topk_w", "counts", "offsets", "pos")
+FMT_CODE = {"bf16": moe.MOE_BF16, "w4": moe.MOE_W4A16, "affine4": moe.MOE_AFFINE4, "nvfp4": moe.MOE_NVFP4}
 
 
 def _run(fn, w, d, T, **kw):
@@ -26,7 +27,7 @@ def _run(fn, w, d, T, **kw):
     return y, ex
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "w4"])
+@pytest.mark.parametrize("fmt", ["bf16", "w4", "affine4", "nvfp4"])
 def test_static_matches_workspace_entry_two_calls(fmt):
     w = BIG.with_(fmt=fmt)
     d = synth.make_inputs(w, "cuda")
@@ -34,7 +35,7 @@ def test_static_matches_workspace_entry_two_calls(fmt):
     d["bias"] = (-0.05 * torch.arange(w.E, dtype=torch.float32)).cuda()
     for T in (w.T, 5):
         log(f"moe_ffn_static vs moe_ffn: fmt={fmt} T={T}")
-        need = moe.workspace_bytes(T, w.H, w.E, w.I, w.Is, w.topk, 0 if fmt == "bf16" else 1)
+        need = moe.workspace_bytes(T, w.H, w.E, w.I, w.Is, w.topk, FMT_CODE[fmt])
         assert need <= moe.MOE_STATIC_SCRATCH_BYTES
         y_ref, ex_ref = _run(moe.moe_ffn, w, d, T)
         y_st, ex_st = _run(moe.moe_ffn_static, w, d, T)
