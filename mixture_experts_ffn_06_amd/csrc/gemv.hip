@@ -348,7 +348,7 @@ __device__ void gateup_item(const ExpertArgs& a, const Group& g, int c0, const u
 }
 
 // MAXNR: the most rows a group of the launch has (1 at T = 1: the one-row
-// kernels need fewer registers, so two blocks fit on a CU).
+// kernels need fewer registers, so two or three blocks fit on a CU).
 template <int FMT, int CB, int MAXNR>
 __device__ __forceinline__ void gateup_dispatch_rows(const ExpertArgs& a, const Group& g, int c0,
                                                      const uint16_t* xs, const float* xsum) {
@@ -907,7 +907,7 @@ void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream
                                a.T == 1 && one_row_waves(a.fmt, false) == 6);
     auto go = [&](auto fmt) {
         constexpr int F = decltype(fmt)::value;
-        if (a.T == 1) {  // one-row kernels: two blocks per CU
+        if (a.T == 1) {  // one-row kernels: two or three blocks per CU
             allow_lds(down_gemv_kernel<F, 1>, lds);
             down_gemv_kernel<F, 1><<<grid, kGemvThreads, lds, st>>>(a, lds_rows, kmax);
         } else {
