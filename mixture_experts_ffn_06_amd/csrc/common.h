@@ -168,6 +168,12 @@ void launch_dispatch(const int32_t* ids, int T, int k, int lo, int hi, bool has_
                      int mfma_cap, int32_t* plan_counts, hipStream_t st);
 void launch_gateup_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
 void launch_down_gemv(const ExpertArgs& a, int max_groups, int num_cu, hipStream_t st);
+// T = 1, 4-bit routed experts, K = I = Is = 2048, at most 8 picks: the down
+// projection with the pick-order combine folded in (bit for bit the pair of
+// down_gemv and combine launches); down_combine_one_ok says when it applies.
+bool down_combine_one_ok(const ExpertArgs& a, int k, bool has_shared);
+void launch_down_combine_one(const ExpertArgs& a, const int32_t* ids, const int32_t* pos, const float* wts, int k,
+                             const uint16_t* res, bool has_shared, float* out, hipStream_t st);
 // bf16 experts: the direct-to-LDS pipelined tiles, one launch for the
 // 256-row tiles and one for the 128-, 64- and 32-row tiles (gate/up or
 // down).  With 4-bit experts these launches run the (bf16) shared expert's

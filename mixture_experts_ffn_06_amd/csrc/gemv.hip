@@ -839,6 +839,160 @@ __global__ __launch_bounds__(kGemvThreads, MAXNR == 1 ? one_row_waves(FMT, false
     }
 }
 
+// ---- one row: the down projection with the combine folded in -------------
+//
+// At T = 1 with 4-bit routed experts and K = I = Is = 2048 (one 4-bit lane
+// step per weight row), the token-major form ([P2] "Per MoE layer": the rows
+// come back as one weighted sum per token): wave w of block b owns output
+// column c = 8 b + w, loads that column's row of every pick's down matrix and
+// of the shared expert's, reduces each exactly as down_item does (same staged
+// layout -- pairwise-permuted with per-32 sums for W4A16 and MLX affine, plain
+// for NVFP4 -- same lane steps, same helpers, same wave sums) and adds them in
+// pick order as combine_kernel does, then the shared output, then the
+// residual -- bit for
+// bit the unfused pair of launches, without the per-pick outputs' round trip
+// and the combine's launch.  All in-band picks' rows of h (slots 0..N_in-1,
+// T = 1) and the shared row are staged once per block, every load in flight
+// before the first LDS write.
+constexpr int kOneMaxPicks = 8;
+
+template <int FMT>
+__global__ __launch_bounds__(kGemvThreads, 4) void down_combine_one_kernel(ExpertArgs a, const int32_t* __restrict__ ids,
+                                                                           const int32_t* __restrict__ pos,
+                                                                           const float* __restrict__ wts, int k,
+                                                                           const uint16_t* __restrict__ res,
+                                                                           int has_shared, float* __restrict__ out) {
+    constexpr int K = 2048, C8N = K / 8, GN = K / 32;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                         // [kOneMaxPicks + 1][K]
+    float* xsum = reinterpret_cast<float*>(smem + (kOneMaxPicks + 1) * K * 2);  // [kOneMaxPicks][K / 32]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = a.H;
+    int p[kOneMaxPicks], nin = 0;
+#pragma unroll
+    for (int j = 0; j < kOneMaxPicks; ++j) {
+        p[j] = j < k ? pos[j] : -1;
+        nin += p[j] >= 0 ? 1 : 0;
+    }
+    // staging: chunk i of the routed rows (slot i / C8N, permuted as
+    // stage_rows does) or of the shared row (plain); every load first
+    constexpr int PER = ((kOneMaxPicks + 1) * C8N + kGemvThreads - 1) / kGemvThreads;
+    uint4 v[PER];
+    const int nchunk = (nin + (has_shared ? 1 : 0)) * C8N;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int idx = tid + u * kGemvThreads;
+        const int r = idx / C8N, c8 = idx - r * C8N;
+        const uint16_t* src = r < nin ? a.h_r + (size_t)r * a.I : a.h_s;
+        v[u] = idx < nchunk ? *reinterpret_cast<const uint4*>(src + 8 * c8) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int idx = tid + u * kGemvThreads;
+        if (idx >= nchunk) continue;
+        const int r = idx / C8N, c8 = idx - r * C8N;
+        uint4 w = v[u];
+        int dst = c8;
+        uint16_t* row = xs + (size_t)(r < nin ? r : kOneMaxPicks) * K;
+        if (r < nin && FMT != 3) {
+            uint4 q;
+            q.x = (w.x & 0xffffu) | (w.z << 16);
+            q.y = (w.x >> 16) | (w.z & 0xffff0000u);
+            q.z = (w.y & 0xffffu) | (w.w << 16);
+            q.w = (w.y >> 16) | (w.w & 0xffff0000u);
+            w = q;
+            dst = (c8 & ~3) | w4_chunk(c8 >> 2, c8 & 3);
+        }
+        *reinterpret_cast<uint4*>(row + 8 * dst) = w;
+    }
+    __syncthreads();
+    // per-32 sums of the routed rows, as stage_rows forms them (NVFP4 reads
+    // its rows in plain order and uses no sums)
+    for (int idx = tid; FMT != 3 && idx < nin * GN; idx += kGemvThreads) {
+        const int r = idx / GN, gi = idx - r * GN;
+        const uint4* src = reinterpret_cast<const uint4*>(xs + (size_t)r * K + 32 * gi);
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 w = src[w4_chunk(gi, q)];
+            sum += bf16_lo(w.x) + bf16_hi(w.x);
+            sum += bf16_lo(w.y) + bf16_hi(w.y);
+            sum += bf16_lo(w.z) + bf16_hi(w.z);
+            sum += bf16_lo(w.w) + bf16_hi(w.w);
+        }
+        xsum[r * GN + gi] = sum;
+    }
+    __syncthreads();
+
+    const int c = blockIdx.x * kGemvWaves + wave;
+    if (c >= H) return;
+    // every pick's row of column c (picks outside the band read expert 0's,
+    // unused), then the shared row, all in flight at once
+    uint4 qv[kOneMaxPicks];
+    uint32_t sv[kOneMaxPicks], zv[kOneMaxPicks];
+    int ej[kOneMaxPicks];
+#pragma unroll
+    for (int j = 0; j < kOneMaxPicks; ++j) {
+        ej[j] = p[j] >= 0 ? ids[j] : 0;
+        const size_t row = (size_t)ej[j] * H + c;
+        qv[j] = wload(a.qd + row * (K / 2) + 16 * lane);
+        load_scales<FMT>(a.sd, a.zd, row, K, 32 * lane, &sv[j], &zv[j]);
+    }
+    // (no shared expert: any valid address, unused)
+    const uint16_t* swr = has_shared ? a.swd + (size_t)c * K : reinterpret_cast<const uint16_t*>(a.qd);
+    uint4 wv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wv[q] = wload(swr + 512 * q + 8 * lane);
+
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kOneMaxPicks; ++j) {
+        if (p[j] < 0) continue;  // wave-uniform
+        float part[1] = {0.0f};
+        quant_step<FMT, 1>(qv[j], sv[j], zv[j], true, xs + (size_t)(p[j] < 0 ? 0 : p[j]) * K,
+                           xsum + (size_t)(p[j] < 0 ? 0 : p[j]) * GN, K, 32 * lane, part);
+        float y = wave_sum(part[0]);
+        if (FMT == 3) y *= a.gd[ej[j]];
+        acc = __builtin_fmaf(wts[j], y, acc);
+    }
+    if (has_shared) {
+        const uint16_t* xl = xs + (size_t)kOneMaxPicks * K + 8 * lane;
+        float t = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(xl + 512 * q);
+            t = dot2_bf16(wv[q].x, xv.x, t);
+            t = dot2_bf16(wv[q].y, xv.y, t);
+            t = dot2_bf16(wv[q].z, xv.z, t);
+            t = dot2_bf16(wv[q].w, xv.w, t);
+        }
+        acc = acc + wave_sum(t);
+    }
+    if (res) acc = acc + bf16_bits_to_f32(res[c]);
+    if (lane == 0) out[c] = acc;
+}
+
+bool down_combine_one_ok(const ExpertArgs& a, int k, bool has_shared) {
+    return a.T == 1 && a.fmt != 0 && k <= kOneMaxPicks && a.I == 2048 && (!has_shared || a.Is == 2048) &&
+           a.H % kGemvWaves == 0;
+}
+
+void launch_down_combine_one(const ExpertArgs& a, const int32_t* ids, const int32_t* pos, const float* wts, int k,
+                             const uint16_t* res, bool has_shared, float* out, hipStream_t st) {
+    const size_t lds = (size_t)(kOneMaxPicks + 1) * 2048 * 2 + (size_t)kOneMaxPicks * (2048 / 32) * 4;
+    const int grid = a.H / kGemvWaves;
+    auto go = [&](auto fmt) {
+        constexpr int F = decltype(fmt)::value;
+        allow_lds(down_combine_one_kernel<F>, lds);
+        down_combine_one_kernel<F><<<grid, kGemvThreads, lds, st>>>(a, ids, pos, wts, k, res, has_shared ? 1 : 0, out);
+    };
+    switch (a.fmt) {
+        case 2: go(std::integral_constant<int, 2>{}); break;
+        case 3: go(std::integral_constant<int, 3>{}); break;
+        default: go(std::integral_constant<int, 1>{}); break;
+    }
+}
+
 // blocks per CU: three for the one-row kernels bounded to 6 waves per SIMD
 // when their LDS allows
 static int gemv_grid(size_t lds, int num_cu, long long ub, bool six_waves = false) {

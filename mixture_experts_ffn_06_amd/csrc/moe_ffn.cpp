@@ -405,8 +405,16 @@ int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts*
         else
             moe::launch_mfma_w4(a, true, num_cu, st);
     }
+    // one row, 4-bit experts, pick order, no per-pick or shared outputs
+    // asked for: the down projection and the combine in one launch
+    const bool fused_one = out->combine == MOE_COMBINE_PICK && !out->y_picks && !shared_apart &&
+                           moe::down_combine_one_ok(a, topk, has_shared);
+    const uint16_t* res = out->residual ? static_cast<const uint16_t*>(x->ptr) : nullptr;
     mark(MOE_EV_DN_GEMV);
-    moe::launch_down_gemv(a, max_groups, num_cu, st);
+    if (fused_one)
+        moe::launch_down_combine_one(a, ids, pos, wts, topk, res, has_shared, out->y, st);
+    else
+        moe::launch_down_gemv(a, max_groups, num_cu, st);
     mark(MOE_EV_DN_MFMA);
     if (mfma_possible) {
         if (fmt == MOE_BF16)
@@ -416,11 +424,10 @@ int32_t run_layer(const moe_x* x, const moe_router* router_w, const moe_experts*
     }
     mark(MOE_EV_COMBINE);
     const float* add_s = has_shared && !shared_apart ? a.y_s : nullptr;
-    const uint16_t* res = out->residual ? static_cast<const uint16_t*>(x->ptr) : nullptr;
     if (out->combine == MOE_COMBINE_TREE)
         moe::launch_combine_tree(a.y_r, add_s, res, ids, pos, wts, T, H, topk,
                                  tree_level(band_lo, band_hi), out->y, st);
-    else
+    else if (!fused_one)  // (the fused launch has combined)
         moe::launch_combine(a.y_r, add_s, res, pos, wts, T, H, topk, out->y, st);
     mark(MOE_EV_END);
 
