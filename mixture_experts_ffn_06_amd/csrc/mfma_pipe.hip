@@ -520,14 +520,16 @@ void launch_mfma_pipe(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t 
 // Blocks of 4 waves for BM = 128, 64, 32 (a 256-row tile runs as two 128-row
 // halves); wave w owns all BM rows and 32 columns (16 gate and the matching 16
 // up columns, or 32 down columns), so no two waves expand the same weights.
-// Per K step of 64 a stage holds the A rows (bf16, as above), the weight codes
-// (128 rows x 32 bytes) and each row's scale and zero for the step's two
-// 32-input groups, all loaded straight into LDS.  A wave expands its own B
-// operand in registers just before the MFMAs that use it:
+// Per K step of 64 a stage holds the A rows (bf16, as above) and the weight
+// codes (128 rows x 32 bytes), loaded straight into LDS; each row's per-group
+// words (W4A16: scale and zero of the step's two 32-input groups; MLX affine:
+// scale and bias of its 64-input group; NVFP4: the E4M3 scales of its four
+// 16-input blocks) come in blocks of steps beside them.  A wave expands its
+// own B operand in registers just before the MFMAs that use it.  W4A16:
 // (1024 + q) as an fp16 pair per two codes (one AND and one OR), then
 // v_fma_mix ((1024 + q) s - (1024 + z) s, exact in fp32: both products fit in
 // 24 bits) and v_cvt_pk_bf16_f32 (round to nearest even) -- the bf16 weight
-// RNE((q - z) s).
+// RNE((q - z) s).  MLX affine and NVFP4: dequant8_affine, dequant8_nv below.
 
 template <int BM>
 struct W4Cfg {
@@ -541,8 +543,9 @@ struct W4Cfg {
     static constexpr int ATile = BM * kBK * 2;
     static constexpr int QOff = ATile;                   // 128 rows x 32 bytes of codes
     static constexpr int Stage = QOff + 4096;
-    // Scales and zeros come in blocks of G steps: [scales | zeros] x 128
-    // rows x G steps x 4 bytes (the step's two groups), three blocks in LDS.
+    // The per-group words come in blocks of G steps, sized for the largest
+    // format (W4A16: [scales | zeros] x 128 rows x G steps x 4 bytes, the
+    // step's two groups), three blocks in LDS.
     static constexpr int G = BM == 128 ? 4 : 8;
     static constexpr int SZBlock = 1024 * G;
     static constexpr int SZOff = S * Stage;
