@@ -158,8 +158,15 @@ def roofline_for(w, counts, stage_ms, counted=True):
             nbytes = wbytes + act
             flops = 2.0 * routed * 2 * w.I * w.H
     else:
+        # 4-bit: the 128-row tiles, and the 64- and 32-row lists in the
+        # 512-weight-row launch when H % 512 == 0 and I % 256 == 0, else in
+        # 64- and 32-row launches
+        wide = w.H % 512 == 0 and w.I % 256 == 0
+        fc = FMT_CODE[w.fmt]
+        w4_names = ([f"expert_mfma_w4_kernel<{fc},true,128>", f"expert_mfma_w4w_kernel<{fc},true>"] if wide
+                    else [f"expert_mfma_w4_kernel<{fc},true,{bm}>" for bm in (128, 64, 32)])
         kernel = ("expert_mfma_pipe_kernel<true,256> + expert_mfma_small_kernel<true>" if w.fmt == "bf16"
-                  else f"expert_mfma_w4_kernel<{FMT_CODE[w.fmt]},true,128|64|32> + shared-expert bf16 launch")
+                  else " + ".join(w4_names) + " + shared-expert bf16 launch")
         ms = stage_ms["gu_mfma"]
         if w.fmt == "bf16":
             traffic = measured_traffic(
@@ -168,9 +175,7 @@ def roofline_for(w, counts, stage_ms, counted=True):
             # the 4-bit launches, plus the one bf16 launch that holds the shared
             # expert's rows (256-row tiles above 128 rows, else the small-tile launch)
             sh = "expert_mfma_pipe_kernel<true,256>" if w.T > 128 else "expert_mfma_small_kernel<true>"
-            traffic = measured_traffic(
-                w.name, [f"moe::expert_mfma_w4_kernel<{FMT_CODE[w.fmt]},true,{bm}>" for bm in (128, 64, 32)] +
-                [f"moe::{sh}"])
+            traffic = measured_traffic(w.name, [f"moe::{k}" for k in w4_names] + [f"moe::{sh}"])
         # rows on the GEMV path (groups of 1..8 rows) are not in this launch
         small = counts[(counts > 0) & (counts <= 8)]
         n_touched -= int(small.numel())

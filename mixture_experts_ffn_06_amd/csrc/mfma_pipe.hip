@@ -912,8 +912,339 @@ static void launch_w4_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
     expert_mfma_w4_kernel<FMT, GATEUP, BM><<<(int)grid, C::Threads, 0, st>>>(a);
 }
 
+// ---- 4-bit experts, wide column tiles ---------------------------------------
+//
+// For the 64- and 32-row tile lists (groups of 9..64 rows), whose 128-weight-
+// row tiles above are bound by their loads.  One block of 8 waves per CU (two
+// per SIMD).  An item is up to 64 rows of a group by 512 weight rows
+// (gate/up: 256 gate and the matching 256 up columns; down: 512 output
+// columns); wave w owns 64 of the weight rows as four 16-column subtiles, so
+// each A fragment read from LDS feeds four MFMAs and each expanded weight
+// serves all the item's rows.  K advances 128 per step.  Within a step, lane
+// l (column l % 16 of a subtile, lane group l / 16) takes the 32 inputs
+// 32 (l / 16) .. + 31 of the step, one 32-input group; its chunk c (c =
+// 0..3) is the MFMA operand pair of inputs 32 (l / 16) + 8 c .. + 7 on both
+// sides (the MFMA's inputs relabelled consistently in A and B, so the sum over
+// the step is unchanged).  So a lane's codes for a step are 16 contiguous
+// bytes of its weight row, loaded straight into registers three steps ahead;
+// the A rows (bf16) go through an LDS ring of four steps, 16-byte chunks
+// XOR-swizzled by row; the per-group words come in blocks of G steps, 32
+// bytes of each weight row per array, through a ring of two blocks in LDS.
+// Needs K % 512 == 0 and whole column tiles (I % 256 == 0 for gate/up,
+// H % 512 == 0 for down).
+constexpr int kWK = 128;                                   // K per step
+constexpr int kWRows = 64;                                 // A rows per stage
+constexpr int kWS = 4;                                     // A stages (= the loop's unroll)
+constexpr int kWAStage = kWRows * kWK * 2;                 // 16 KiB
+constexpr int kWSzArr = 512 * 32;                          // one array of a block
+constexpr int kWSzBlock = 2 * kWSzArr;                     // 32 KiB
+constexpr int kWLds = kWS * kWAStage + 2 * kWSzBlock;      // 128 KiB
+constexpr int kWExpand = 20;                               // VALU instructions of one expansion (about)
+
+template <int FMT>
+struct WFmt {
+    static constexpr int NA = FMT == 3 ? 1 : 2;    // arrays (scales [, zeros / biases])
+    static constexpr int BPS = FMT == 2 ? 4 : 8;   // bytes per weight row, step and array
+    static constexpr int G = 32 / BPS;             // steps per block of per-group words
+};
+
+// Wave-uniform wait counts of the step loop: vmcnt(N) for the four cases.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    wait_vmcnt<N>();
+}
+
+template <int FMT, bool GATEUP, int MTL>
+__device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, int m0, int nt) {
+    using F = WFmt<FMT>;
+    typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, lg = lane >> 4;
+    const int Ig = a.I, H = a.H;
+    const int K = GATEUP ? H : Ig;
+    const int KT = K / kWK;
+    const int rows = min(16 * MTL, g.n - m0);
+    const size_t erows = GATEUP ? 2 * (size_t)Ig : (size_t)H;  // weight rows per expert
+    const int RB = KT * F::BPS;                                  // bytes of a weight row of one array
+    // the item's 512 weight rows: local row lr -> weight row of the expert
+    // (gate/up: lr < 256 gate column nt 256 + lr, else the up row of column
+    // nt 256 + lr - 256; down: output column nt 512 + lr); the widths are
+    // whole tiles
+    auto wrow = [&](int lr) -> int {
+        if (GATEUP) return lr < 256 ? nt * 256 + lr : Ig + nt * 256 + (lr - 256);
+        return nt * 512 + lr;
+    };
+    // subtile j of this wave: local rows lr0 + dlr(j) + 0..15
+    const int lr0 = GATEUP ? 32 * wave : 64 * wave;
+    auto dlr = [&](int j) -> int { return GATEUP ? 16 * (j & 1) + (j >= 2 ? 256 : 0) : 16 * j; };
+
+    // A rows: instruction ii (= wave + 8 j) fills rows 4 ii .. 4 ii + 3 of a
+    // stage; lane L writes chunk position L % 16 of row 4 ii + L / 16, which
+    // holds the row's chunk (L % 16) ^ (row % 16)
+    constexpr int LA = MTL / 2;  // A instructions per wave and step
+    const uint16_t* asrc[LA];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) {
+        const int r = 4 * (wave + 8 * j) + (lane >> 4);
+        const int q = (lane & 15) ^ (r & 15);
+        const int rr = r < rows ? r : 0;
+        const uint16_t* arow = GATEUP ? a.x + (size_t)(a.perm[g.row0 + m0 + rr] / a.topk) * H
+                                      : a.h_r + (size_t)(g.row0 + m0 + rr) * Ig;
+        asrc[j] = arow + 8 * q;
+    }
+    auto issue_a = [&](int kt) {
+        lds_u8* st = smem + (kt % kWS) * kWAStage;
+#pragma unroll
+        for (int j = 0; j < LA; ++j)
+            __builtin_amdgcn_global_load_lds(asrc[j] + kt * kWK, st + (wave + 8 * j) * 1024, 16, 0, 0);
+    };
+    // per-group words: block b is 32 bytes of each of the 512 weight rows per
+    // array; piece i (= wave + 8 p) covers array p / 2, rows 32 (i % 16) ..
+    // + 31, lane L the half L % 2 of row 32 (i % 16) + L / 2 (a half past the
+    // row's end reloads its last 16 bytes, unused).  A wave's 2 NA pieces of
+    // block b + 1 are issued at step G b, and with G = 8 again at step G b + 4
+    // (the same bytes to the same place), so that every fourth step issues
+    // them.
+    constexpr int NP = 2 * F::NA;
+    const unsigned char* sbase = reinterpret_cast<const unsigned char*>(GATEUP ? a.sgu : a.sd);
+    const unsigned char* zbase = reinterpret_cast<const unsigned char*>(GATEUP ? a.zgu : a.zd);
+    auto issue_pieces = [&](int b) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int i = wave + 8 * p;
+            const int lr = 32 * (i & 15) + (lane >> 1);
+            const int off = min(32 * b + 16 * (lane & 1), RB - 16);
+            const unsigned char* src =
+                ((p >> 1) ? zbase : sbase) + ((size_t)g.expert * erows + wrow(lr)) * RB + off;
+            __builtin_amdgcn_global_load_lds(src, smem + kWS * kWAStage + (b & 1) * kWSzBlock + i * 1024, 16,
+                                             0, 0);
+        }
+    };
+
+    // codes: lane's 16 bytes of each subtile's weight row for step kt, three
+    // steps ahead in four register buffers.  Buffer loads from the wave's
+    // first weight row: the lane offset in one register, the subtile's and
+    // the step's offset wave-uniform (every offset is below 2^31; the
+    // descriptor's last word is the gfx9 raw 32-bit data format).
+    const unsigned char* qw =
+        (GATEUP ? a.qgu : a.qd) + ((size_t)g.expert * erows + wrow(lr0)) * (size_t)(K / 2);
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)qw, (short)0, 0x7fffffff, 0x00020000);
+    const int qlane = n * (K / 2) + 16 * lg;
+    auto load_codes = [&](int kt, uint4* cb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int dj = (GATEUP ? 16 * (j & 1) + (j >= 2 ? Ig : 0) : 16 * j) * (K / 2);
+            const u32x4_p v = __builtin_bit_cast(
+                u32x4_p, __builtin_amdgcn_raw_buffer_load_b128(qrs, qlane, dj + 64 * kt, 0));
+            cb[j] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    };
+
+    f32x4_p acc[MTL][4];
+#pragma unroll
+    for (int i = 0; i < MTL; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+
+    // Step kt issues, in this order: the pieces (kt % 4 == 0), the codes and
+    // A stage of step kt + 3 (the last steps' loads past the end reload the
+    // last step: the same bytes into the same places), so the vector-memory
+    // counts depend only on kt % 4; at the top of step kt the wait leaves in
+    // flight exactly what steps kt - 2 and kt - 1 issued.  The A stage of
+    // step kt is kt % 4, a constant of each unrolled step.
+    __builtin_amdgcn_s_barrier();  // every wave is done with the previous item's LDS
+    uint4 cb0[4], cb1[4], cb2[4], cb3[4];
+    issue_pieces(0);
+    load_codes(0, cb0);
+    issue_a(0);
+    load_codes(min(1, KT - 1), cb1);
+    issue_a(min(1, KT - 1));
+    load_codes(min(2, KT - 1), cb2);
+    issue_a(min(2, KT - 1));
+
+    auto step = [&](int kt, int p4, const uint4* cur, uint4* ahead) {
+        if (p4 == 1 || p4 == 2)
+            wait_vm<NP + 8 + 2 * LA>();
+        else
+            wait_vm<8 + 2 * LA>();
+        __builtin_amdgcn_s_barrier();  // stage kt and block kt / G visible; stage kt - 1 free
+        asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+        if (p4 == 0) issue_pieces(kt / F::G + 1);
+        load_codes(min(kt + 3, KT - 1), ahead);
+        issue_a(min(kt + 3, KT - 1));
+
+        const lds_u8* st = smem + p4 * kWAStage;
+        const lds_u8* sz = smem + kWS * kWAStage + ((kt / F::G) & 1) * kWSzBlock;
+        const int t = kt % F::G;
+        // this lane's per-group words of each subtile
+        uint32_t sw[4], zw[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int off = (lr0 + n + dlr(j)) * 32 + (FMT == 2 ? 4 * t + 2 * (lg >> 1) : 8 * t + 2 * lg);
+            sw[j] = *(lds_cu16*)(sz + off);
+            zw[j] = F::NA == 2 ? *(lds_cu16*)(sz + kWSzArr + off) : 0u;
+        }
+        float s0[4], s1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (FMT == 1) {
+                const float sc = __uint_as_float(sw[j] << 16), zz = __uint_as_float(zw[j] << 16);
+                s0[j] = sc;
+                s1[j] = -((1024.0f + zz) * sc);
+            } else if constexpr (FMT == 2) {
+                s0[j] = __uint_as_float(sw[j] << 16) * 16777216.0f;
+                s1[j] = __uint_as_float(zw[j] << 16);
+            } else {
+                s0[j] = __builtin_amdgcn_cvt_f32_fp8(sw[j], 0);
+                s1[j] = __builtin_amdgcn_cvt_f32_fp8(sw[j], 1);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // One chunk at a time.  The expansion of subtile j + 1 is
+            // interleaved with the MFMAs of subtile j (a few VALU
+            // instructions issue while each MFMA runs), since the two waves
+            // of a SIMD pass the step barrier together and would otherwise
+            // expand, and then multiply, at the same time.
+            __builtin_amdgcn_sched_barrier(0);
+            auto expand = [&](int j) -> bf16x8_p {
+                const uint32_t w = c == 0 ? cur[j].x : c == 1 ? cur[j].y : c == 2 ? cur[j].z : cur[j].w;
+                if constexpr (FMT == 1)
+                    return dequant8(w, s0[j], s1[j]);
+                else if constexpr (FMT == 2)
+                    return dequant8_affine(w, s0[j], s1[j]);
+                else
+                    return dequant8_nv(w, c < 2 ? s0[j] : s1[j]);
+            };
+            bf16x8_p af[MTL];
+#pragma unroll
+            for (int i = 0; i < MTL; ++i) af[i] = *(lds_bf16x8*)(st + (16 * i + n) * 256 + (((4 * lg + c) ^ n) << 4));
+            bf16x8_p bw[2];
+            bw[0] = expand(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < 3) bw[(j + 1) & 1] = expand(j + 1);
+#pragma unroll
+                for (int i = 0; i < MTL; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[j & 1], acc[i][j], 0, 0, 0);
+            }
+            // order: the A reads, the first expansion, then per subtile its
+            // MFMAs each followed by a share of the next expansion
+            __builtin_amdgcn_sched_group_barrier(0x100, MTL, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kWExpand, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int i = 0; i < MTL; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (j < 3) __builtin_amdgcn_sched_group_barrier(0x002, (kWExpand + MTL - 1) / MTL, 0);
+                }
+        }
+    };
+    // KT is a multiple of 4
+    for (int kt = 0; kt < KT; kt += 4) {
+        step(kt, 0, cb0, cb3);
+        step(kt + 1, 1, cb1, cb0);
+        step(kt + 2, 2, cb2, cb1);
+        step(kt + 3, 3, cb3, cb2);
+    }
+
+    // NVFP4: the matrix scales multiply the finished sums
+    float mg = 1.0f, mu = 1.0f;
+    if (FMT == 3) {
+        mg = GATEUP ? a.ggu[2 * (size_t)g.expert] : a.gd[g.expert];
+        mu = GATEUP ? a.ggu[2 * (size_t)g.expert + 1] : mg;
+    }
+    if (GATEUP) {
+        uint16_t* hout = a.h_r + (size_t)(g.row0 + m0) * Ig;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            __builtin_amdgcn_sched_barrier(0);  // a subtile's sums at a time
+            const int c = nt * 256 + 32 * wave + 16 * j + n;
+#pragma unroll
+            for (int i = 0; i < MTL; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * i + 4 * lg + v;
+                    const float gv = FMT == 3 ? acc[i][j][v] * mg : acc[i][j][v];
+                    const float uv = FMT == 3 ? acc[i][j + 2][v] * mu : acc[i][j + 2][v];
+                    if (r < rows) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(gv, uv));
+                }
+        }
+    } else {
+        float* yout = a.y_r + (size_t)(g.row0 + m0) * H;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_sched_barrier(0);  // a subtile's sums at a time
+            const int c = nt * 512 + 64 * wave + 16 * j + n;
+#pragma unroll
+            for (int i = 0; i < MTL; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * i + 4 * lg + v;
+                    if (r < rows) yout[(size_t)r * H + c] = FMT == 3 ? acc[i][j][v] * mg : acc[i][j][v];
+                }
+        }
+    }
+}
+
+// The 64- and 32-row tile lists of the routed 4-bit groups in one launch,
+// walked per XCD as the other launches are (groups of more than 64 rows take
+// expert_mfma_w4_kernel's 128-row tiles).
+template <int FMT, bool GATEUP>
+__global__ __launch_bounds__(512, 2) void expert_mfma_w4w_kernel(ExpertArgs a) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kWLds];
+    lds_u8* smem = (lds_u8*)smem_raw;
+    const int n64 = a.plan_counts[2], n32 = a.plan_counts[3];
+    const int NT = GATEUP ? a.I / 256 : a.H / 512;
+    XcdWalk w(n64 + n32, NT);
+    int tile, nt;
+    while (w.next(&tile, &nt)) {
+        int l = 1;
+        if (tile >= n64) {
+            tile -= n64;
+            l = 2;
+        }
+        const int32_t* tl = a.mfma_list + 2 * (size_t)l * a.mfma_cap;
+        const Group g = a.groups[tl[2 * tile]];
+        if (g.expert < 0) continue;  // the shared expert is bf16
+        const int m0 = tl[2 * tile + 1];
+        const int rows = min(64, g.n - m0);
+        if (rows > 32)
+            wide_tile_w4<FMT, GATEUP, 4>(a, smem, g, m0, nt);
+        else
+            wide_tile_w4<FMT, GATEUP, 2>(a, smem, g, m0, nt);
+    }
+}
+
+static bool wide_ok(const ExpertArgs& a, bool gateup) {
+    const int K = gateup ? a.H : a.I;
+    return K % 512 == 0 && (gateup ? a.I % 256 == 0 : a.H % 512 == 0);
+}
+
+template <int FMT, bool GATEUP>
+static void launch_w4w(const ExpertArgs& a, int num_cu, hipStream_t st) {
+    const int NT = GATEUP ? a.I / 256 : a.H / 512;
+    long long grid = num_cu;
+    const long long ub = 2LL * a.mfma_cap * NT;
+    if (ub < grid) grid = ub;
+    grid = grid < 8 ? 8 : grid & ~7LL;  // the XCD walk deals blocks in groups of 8
+    expert_mfma_w4w_kernel<FMT, GATEUP><<<(int)grid, 512, 0, st>>>(a);
+}
+
 template <int FMT>
 static void launch_w4_fmt(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st) {
+    if (wide_ok(a, gateup)) {
+        if (gateup) {
+            launch_w4_bm<FMT, true, 128>(a, num_cu, st);
+            launch_w4w<FMT, true>(a, num_cu, st);
+        } else {
+            launch_w4_bm<FMT, false, 128>(a, num_cu, st);
+            launch_w4w<FMT, false>(a, num_cu, st);
+        }
+        return;
+    }
     if (gateup) {
         launch_w4_bm<FMT, true, 128>(a, num_cu, st);
         launch_w4_bm<FMT, true, 64>(a, num_cu, st);

@@ -43,7 +43,10 @@ from oracle import oracle as orc
 
 pytestmark = pytest.mark.gpu
 
-H, E, I, K = 512, 16, 256, 4
+H, E, K = 512, 16, 4
+# intermediate widths: 256 takes the 128-weight-row MFMA tiles for the down
+# projection, 512 the 512-weight-row tiles (K a multiple of 512)
+WIDTHS = [256, 512]
 
 
 def _pack(q):
@@ -63,7 +66,7 @@ def _router(T, g):
     return x.to(torch.bfloat16), bias
 
 
-def _inputs_affine(T, i0, seed):
+def _inputs_affine(T, i0, seed, I):
     g = torch.Generator().manual_seed(seed)
     q_gu = torch.zeros((E, 2 * I, H), dtype=torch.int64)
     s_gu = torch.full((E, 2 * I, H // 64), 0.01)
@@ -82,7 +85,7 @@ def _inputs_affine(T, i0, seed):
     return (*_router(T, g), experts)
 
 
-def _inputs_nvfp4(T, i0, seed):
+def _inputs_nvfp4(T, i0, seed, I):
     g = torch.Generator().manual_seed(seed)
     q_gu = torch.zeros((E, 2 * I, H), dtype=torch.int64)
     s_gu = torch.full((E, 2 * I, H // 16), 0x38, dtype=torch.uint8)  # 1.0
@@ -100,7 +103,7 @@ def _inputs_nvfp4(T, i0, seed):
     return (*_router(T, g), experts)
 
 
-def _inputs(T, i0, seed):
+def _inputs(T, i0, seed, I):
     g = torch.Generator().manual_seed(seed)
     # gate/up: zero point 8 everywhere, codes 8 (weight 0) except gate and up
     # row i0[e] of every expert: codes 9 with scales 32 and 1/32
@@ -122,12 +125,13 @@ def _inputs(T, i0, seed):
     return (*_router(T, g), experts)
 
 
+@pytest.mark.parametrize("I", WIDTHS)
 @pytest.mark.parametrize("fmt", ["w4", "affine4", "nvfp4"])
 @pytest.mark.parametrize("T", [1, 3, 8, 9, 20, 40, 100, 129, 300])
-def test_down_dequant_bit_exact(T, fmt):
+def test_down_dequant_bit_exact(T, fmt, I):
     i0 = [(37 * e + 11 * T) % I for e in range(E)]
     make = {"w4": _inputs, "affine4": _inputs_affine, "nvfp4": _inputs_nvfp4}[fmt]
-    x, bias, experts = make(T, i0, seed=100 + T)
+    x, bias, experts = make(T, i0, seed=100 + T, I=I)
     dev = "cuda"
     xg = x.to(dev)
     exg = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in experts.items()}
@@ -160,4 +164,4 @@ def test_down_dequant_bit_exact(T, fmt):
                                  f"{want[got != want][:3].tolist()}")
     path = "MFMA path" if mfma else "GEMV path"
     kind = "fp32" if fmt == "nvfp4" or not mfma else "bf16 RNE"
-    log(f"{fmt} T={T}: {T * K} pick rows x {H} values bit-exact ({kind}, {path})")
+    log(f"{fmt} T={T} I={I}: {T * K} pick rows x {H} values bit-exact ({kind}, {path})")
