@@ -927,8 +927,8 @@ static void launch_w4_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
 // sides (the MFMA's inputs relabelled consistently in A and B, so the sum over
 // the step is unchanged).  So a lane's codes for a step are 16 contiguous
 // bytes of its weight row, loaded straight into registers three steps ahead;
-// the A rows (bf16) go through an LDS ring of four steps, 16-byte chunks
-// XOR-swizzled by row; the per-group words come in blocks of G steps, 32
+// the A rows (bf16) go through an LDS ring of four steps, laid out for
+// conflict-free operand reads (below); the per-group words come in blocks of G steps, 32
 // bytes of each weight row per array, through a ring of two blocks in LDS.
 // Needs K % 512 == 0 and whole column tiles (I % 256 == 0 for gate/up,
 // H % 512 == 0 for down).
@@ -979,15 +979,23 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     const int lr0 = GATEUP ? 32 * wave : 64 * wave;
     auto dlr = [&](int j) -> int { return GATEUP ? 16 * (j & 1) + (j >= 2 ? 256 : 0) : 16 * j; };
 
-    // A rows: instruction ii (= wave + 8 j) fills rows 4 ii .. 4 ii + 3 of a
-    // stage; lane L writes chunk position L % 16 of row 4 ii + L / 16, which
-    // holds the row's chunk (L % 16) ^ (row % 16)
+    // A rows in a stage: two regions of 16 MTL lines of 128 bytes, region R
+    // holding, for row r, the chunks 4 lg + 2 R + h (lg = 0..3, h = 0..1:
+    // the 16-byte chunks that chunk steps c = 2 R + h read) at positions
+    // (4 h + lg) ^ (r % 8), so that the 64 lanes of an operand read (16 rows,
+    // four lane groups) meet no bank twice.  Instruction ii (= wave + 8 j)
+    // fills region ii / (2 MTL), lines 8 (ii % (2 MTL)) .. + 7: lane L writes
+    // position L % 8 of line 8 (ii % (2 MTL)) + L / 8.
     constexpr int LA = MTL / 2;  // A instructions per wave and step
+    constexpr int AReg = 16 * MTL * 128;  // bytes of a region
     const uint16_t* asrc[LA];
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
-        const int r = 4 * (wave + 8 * j) + (lane >> 4);
-        const int q = (lane & 15) ^ (r & 15);
+        const int ii = wave + 8 * j;
+        const int R = ii / (2 * MTL);
+        const int r = 8 * (ii % (2 * MTL)) + (lane >> 3);
+        const int hl = (lane & 7) ^ (r & 7);  // 4 h + lg
+        const int q = 4 * (hl & 3) + 2 * R + (hl >> 2);
         const int rr = r < rows ? r : 0;
         const uint16_t* arow = GATEUP ? a.x + (size_t)(a.perm[g.row0 + m0 + rr] / a.topk) * H
                                       : a.h_r + (size_t)(g.row0 + m0 + rr) * Ig;
@@ -1119,7 +1127,8 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
             };
             bf16x8_p af[MTL];
 #pragma unroll
-            for (int i = 0; i < MTL; ++i) af[i] = *(lds_bf16x8*)(st + (16 * i + n) * 256 + (((4 * lg + c) ^ n) << 4));
+            for (int i = 0; i < MTL; ++i)
+                af[i] = *(lds_bf16x8*)(st + (c >> 1) * AReg + (16 * i + n) * 128 + (((4 * (c & 1) + lg) ^ (n & 7)) << 4));
             bf16x8_p bw[2];
             bw[0] = expand(0);
 #pragma unroll
