@@ -159,9 +159,9 @@ def roofline_for(w, counts, stage_ms, counted=True):
             flops = 2.0 * routed * 2 * w.I * w.H
     else:
         # 4-bit: the 128-row tiles, and the 64- and 32-row lists in the
-        # 512-weight-row launch when H % 512 == 0 and I % 256 == 0, else in
-        # 64- and 32-row launches
-        wide = w.H % 512 == 0 and w.I % 256 == 0
+        # wide-tile launch when H % 512 == 0 and I % 128 == 0, else in 64- and
+        # 32-row launches
+        wide = w.H % 512 == 0 and w.I % 128 == 0
         fc = FMT_CODE[w.fmt]
         w4_names = ([f"expert_mfma_w4_kernel<{fc},true,128>", f"expert_mfma_w4w_kernel<{fc},true>"] if wide
                     else [f"expert_mfma_w4_kernel<{fc},true,{bm}>" for bm in (128, 64, 32)])

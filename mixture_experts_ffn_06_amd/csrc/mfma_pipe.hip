@@ -916,43 +916,36 @@ static void launch_w4_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
 //
 // For the 64- and 32-row tile lists (groups of 9..64 rows), whose 128-weight-
 // row tiles above are bound by their loads.  One block of 8 waves per CU (two
-// per SIMD).  An item is up to 64 rows of a group by 512 weight rows
-// (gate/up: 256 gate and the matching 256 up columns; down: 512 output
-// columns); wave w owns 64 of the weight rows as four 16-column subtiles, so
-// each A fragment read from LDS feeds four MFMAs and each expanded weight
-// serves all the item's rows.  K advances 128 per step.  Within a step, lane
-// l (column l % 16 of a subtile, lane group l / 16) takes the 32 inputs
-// 32 (l / 16) .. + 31 of the step, one 32-input group; its chunk c (c =
-// 0..3) is the MFMA operand pair of inputs 32 (l / 16) + 8 c .. + 7 on both
-// sides (the MFMA's inputs relabelled consistently in A and B, so the sum over
-// the step is unchanged).  So a lane's codes for a step are 16 contiguous
-// bytes of its weight row, loaded straight into registers three steps ahead;
-// the A rows (bf16) go through an LDS ring of four steps, laid out for
-// conflict-free operand reads (below); the per-group words come in blocks of G steps, 32
-// bytes of each weight row per array, through a ring of two blocks in LDS.
-// Needs K % 512 == 0 and whole column tiles (I % 256 == 0 for gate/up,
-// H % 512 == 0 for down).
+// per SIMD).  An item is up to 64 rows of a group by 256 weight rows
+// (gate/up: 128 gate and the matching 128 up columns; down: 256 output
+// columns); wave w owns 32 of the weight rows as two 16-column subtiles.  K
+// advances 128 per step.  Within a step, lane l (column l % 16 of a subtile,
+// lane group l / 16) takes the 32 inputs 32 (l / 16) .. + 31 of the step, one
+// 32-input group; its chunk c (c = 0..3) is the MFMA operand pair of inputs
+// 32 (l / 16) + 8 c .. + 7 on both sides (the MFMA's inputs relabelled
+// consistently in A and B, so the sum over the step is unchanged).  So a
+// lane's codes for a step are 16 contiguous bytes of its weight row, loaded
+// straight into registers four steps ahead (four buffers).  The A rows (bf16)
+// go through an LDS ring of two steps, laid out for conflict-free operand
+// reads (below).
+// The per-group words come in blocks of whole 128-byte lines of each weight
+// row per array (16 steps; MLX affine 32), through a ring of two blocks in
+// LDS, so each line is fetched once.  Needs K % 512 == 0 and whole column
+// tiles (I % 128 == 0 for gate/up, H % 256 == 0 for down).
 constexpr int kWK = 128;                                   // K per step
 constexpr int kWRows = 64;                                 // A rows per stage
-constexpr int kWS = 4;                                     // A stages (= the loop's unroll)
 constexpr int kWAStage = kWRows * kWK * 2;                 // 16 KiB
-constexpr int kWSzArr = 512 * 32;                          // one array of a block
-constexpr int kWSzBlock = 2 * kWSzArr;                     // 32 KiB
-constexpr int kWLds = kWS * kWAStage + 2 * kWSzBlock;      // 128 KiB
+constexpr int kWArr = 256 * 128;                           // one array of a block: 32 KiB
+constexpr int kWLds = 2 * kWAStage + 2 * 2 * kWArr;        // 160 KiB
 constexpr int kWExpand = 20;                               // VALU instructions of one expansion (about)
 
 template <int FMT>
 struct WFmt {
     static constexpr int NA = FMT == 3 ? 1 : 2;    // arrays (scales [, zeros / biases])
     static constexpr int BPS = FMT == 2 ? 4 : 8;   // bytes per weight row, step and array
-    static constexpr int G = 32 / BPS;             // steps per block of per-group words
+    static constexpr int SPB = 128 / BPS;          // steps per block of per-group words
+    static constexpr int NPS = 16 * NA / SPB;      // piece instructions per wave every fourth step
 };
-
-// Wave-uniform wait counts of the step loop: vmcnt(N) for the four cases.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    wait_vmcnt<N>();
-}
 
 template <int FMT, bool GATEUP, int MTL>
 __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, int m0, int nt) {
@@ -964,20 +957,21 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     const int Ig = a.I, H = a.H;
     const int K = GATEUP ? H : Ig;
     const int KT = K / kWK;
+    const int NB = (KT + F::SPB - 1) / F::SPB;                   // blocks of per-group words
     const int rows = min(16 * MTL, g.n - m0);
     const size_t erows = GATEUP ? 2 * (size_t)Ig : (size_t)H;  // weight rows per expert
     const int RB = KT * F::BPS;                                  // bytes of a weight row of one array
-    // the item's 512 weight rows: local row lr -> weight row of the expert
-    // (gate/up: lr < 256 gate column nt 256 + lr, else the up row of column
-    // nt 256 + lr - 256; down: output column nt 512 + lr); the widths are
+    // the item's 256 weight rows: local row lr -> weight row of the expert
+    // (gate/up: lr < 128 gate column nt 128 + lr, else the up row of column
+    // nt 128 + lr - 128; down: output column nt 256 + lr); the widths are
     // whole tiles
     auto wrow = [&](int lr) -> int {
-        if (GATEUP) return lr < 256 ? nt * 256 + lr : Ig + nt * 256 + (lr - 256);
-        return nt * 512 + lr;
+        if (GATEUP) return lr < 128 ? nt * 128 + lr : Ig + nt * 128 + (lr - 128);
+        return nt * 256 + lr;
     };
     // subtile j of this wave: local rows lr0 + dlr(j) + 0..15
-    const int lr0 = GATEUP ? 32 * wave : 64 * wave;
-    auto dlr = [&](int j) -> int { return GATEUP ? 16 * (j & 1) + (j >= 2 ? 256 : 0) : 16 * j; };
+    const int lr0 = GATEUP ? 16 * wave : 32 * wave;
+    auto dlr = [&](int j) -> int { return GATEUP ? 128 * j : 16 * j; };
 
     // A rows in a stage: two regions of 16 MTL lines of 128 bytes, region R
     // holding, for row r, the chunks 4 lg + 2 R + h (lg = 0..3, h = 0..1:
@@ -1001,36 +995,33 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
                                       : a.h_r + (size_t)(g.row0 + m0 + rr) * Ig;
         asrc[j] = arow + 8 * q;
     }
-    auto issue_a = [&](int kt) {
-        lds_u8* st = smem + (kt % kWS) * kWAStage;
+    auto issue_a = [&](int kt, int stage) {
+        lds_u8* st = smem + stage * kWAStage;
 #pragma unroll
         for (int j = 0; j < LA; ++j)
             __builtin_amdgcn_global_load_lds(asrc[j] + kt * kWK, st + (wave + 8 * j) * 1024, 16, 0, 0);
     };
-    // per-group words: block b is 32 bytes of each of the 512 weight rows per
-    // array; piece i (= wave + 8 p) covers array p / 2, rows 32 (i % 16) ..
-    // + 31, lane L the half L % 2 of row 32 (i % 16) + L / 2 (a half past the
-    // row's end reloads its last 16 bytes, unused).  A wave's 2 NA pieces of
-    // block b + 1 are issued at step G b, and with G = 8 again at step G b + 4
-    // (the same bytes to the same place), so that every fourth step issues
-    // them.
-    constexpr int NP = 2 * F::NA;
+    // per-group words: block b is the 128-byte line b of each of the 256
+    // weight rows per array (a line past the row's end reloads the row's last
+    // 16 bytes, unused).  In LDS, [array][row][128 bytes] with the row's
+    // 16-byte chunk k at position k ^ (row % 8).  Piece i (= wave + 8 p, p <
+    // 4 NA) covers array i / 32, rows 8 (i % 32) .. + 7; lane L writes
+    // position L % 8 of row 8 (i % 32) + L / 8.  A wave's pieces of block b + 1
+    // are issued NPS at a time at every fourth step of block b.
     const unsigned char* sbase = reinterpret_cast<const unsigned char*>(GATEUP ? a.sgu : a.sd);
     const unsigned char* zbase = reinterpret_cast<const unsigned char*>(GATEUP ? a.zgu : a.zd);
-    auto issue_pieces = [&](int b) {
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const int i = wave + 8 * p;
-            const int lr = 32 * (i & 15) + (lane >> 1);
-            const int off = min(32 * b + 16 * (lane & 1), RB - 16);
-            const unsigned char* src =
-                ((p >> 1) ? zbase : sbase) + ((size_t)g.expert * erows + wrow(lr)) * RB + off;
-            __builtin_amdgcn_global_load_lds(src, smem + kWS * kWAStage + (b & 1) * kWSzBlock + i * 1024, 16,
-                                             0, 0);
-        }
+    lds_u8* const szb = smem + 2 * kWAStage;
+    auto issue_piece = [&](int b, int p) {
+        const int i = wave + 8 * p;
+        const int lr = 8 * (i & 31) + (lane >> 3);
+        const int k = (lane & 7) ^ (lr & 7);
+        const int off = min(128 * b + 16 * k, RB - 16);
+        const unsigned char* src =
+            ((i >> 5) ? zbase : sbase) + ((size_t)g.expert * erows + wrow(lr)) * RB + off;
+        __builtin_amdgcn_global_load_lds(src, szb + (b & 1) * (F::NA * kWArr) + i * 1024, 16, 0, 0);
     };
 
-    // codes: lane's 16 bytes of each subtile's weight row for step kt, three
+    // codes: lane's 16 bytes of each subtile's weight row for step kt, four
     // steps ahead in four register buffers.  Buffer loads from the wave's
     // first weight row: the lane offset in one register, the subtile's and
     // the step's offset wave-uniform (every offset is below 2^31; the
@@ -1041,61 +1032,73 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     const int qlane = n * (K / 2) + 16 * lg;
     auto load_codes = [&](int kt, uint4* cb) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int dj = (GATEUP ? 16 * (j & 1) + (j >= 2 ? Ig : 0) : 16 * j) * (K / 2);
+        for (int j = 0; j < 2; ++j) {
+            const int dj = (GATEUP ? (j ? Ig : 0) : 16 * j) * (K / 2);
             const u32x4_p v = __builtin_bit_cast(
                 u32x4_p, __builtin_amdgcn_raw_buffer_load_b128(qrs, qlane, dj + 64 * kt, 0));
             cb[j] = make_uint4(v.x, v.y, v.z, v.w);
         }
     };
 
-    f32x4_p acc[MTL][4];
+    f32x4_p acc[MTL][2];
 #pragma unroll
     for (int i = 0; i < MTL; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_p{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_p{0.f, 0.f, 0.f, 0.f};
 
-    // Step kt issues, in this order: the pieces (kt % 4 == 0), the codes and
-    // A stage of step kt + 3 (the last steps' loads past the end reload the
-    // last step: the same bytes into the same places), so the vector-memory
-    // counts depend only on kt % 4; at the top of step kt the wait leaves in
-    // flight exactly what steps kt - 2 and kt - 1 issued.  The A stage of
-    // step kt is kt % 4, a constant of each unrolled step.
+    // Step kt issues, in this order: A stage kt + 1 and NPS pieces (kt % 4 ==
+    // 0) at its top, the codes of step kt + 4 into the buffer it has just
+    // used at its end (the last steps' loads past the end reload the last
+    // step: the same bytes into the same places), so the vector-memory counts
+    // depend only on kt % 4; the top of step kt waits until only what step
+    // kt - 1 issued after A stage kt may be in flight.  The A stage of step kt
+    // is kt % 2, a constant of each unrolled step.
     __builtin_amdgcn_s_barrier();  // every wave is done with the previous item's LDS
-    uint4 cb0[4], cb1[4], cb2[4], cb3[4];
-    issue_pieces(0);
+    uint4 cb0[2], cb1[2], cb2[2], cb3[2];
+#pragma unroll
+    for (int p = 0; p < 4 * F::NA; ++p) issue_piece(0, p);
+    issue_a(0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // (step 0's wait leaves only the last codes in flight)
     load_codes(0, cb0);
-    issue_a(0);
     load_codes(min(1, KT - 1), cb1);
-    issue_a(min(1, KT - 1));
     load_codes(min(2, KT - 1), cb2);
-    issue_a(min(2, KT - 1));
+    load_codes(min(3, KT - 1), cb3);
 
-    auto step = [&](int kt, int p4, const uint4* cur, uint4* ahead) {
-        if (p4 == 1 || p4 == 2)
-            wait_vm<NP + 8 + 2 * LA>();
+    auto step = [&](int kt, int p4, uint4* cur) {
+        if (p4 == 1)
+            wait_vmcnt<F::NPS + 2>();
         else
-            wait_vm<8 + 2 * LA>();
-        __builtin_amdgcn_s_barrier();  // stage kt and block kt / G visible; stage kt - 1 free
+            wait_vmcnt<2>();
+        __builtin_amdgcn_s_barrier();  // stage kt and block kt / SPB visible; stage kt - 1 free
         asm volatile("" ::: "memory");  // no LDS read moves above the barrier
-        if (p4 == 0) issue_pieces(kt / F::G + 1);
-        load_codes(min(kt + 3, KT - 1), ahead);
-        issue_a(min(kt + 3, KT - 1));
-
-        const lds_u8* st = smem + p4 * kWAStage;
-        const lds_u8* sz = smem + kWS * kWAStage + ((kt / F::G) & 1) * kWSzBlock;
-        const int t = kt % F::G;
-        // this lane's per-group words of each subtile
-        uint32_t sw[4], zw[4];
+        // (the wait counts rely on this issue order: no instruction moves
+        // across the scheduling barriers)
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(min(kt + 1, KT - 1), (p4 + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (p4 == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int off = (lr0 + n + dlr(j)) * 32 + (FMT == 2 ? 4 * t + 2 * (lg >> 1) : 8 * t + 2 * lg);
-            sw[j] = *(lds_cu16*)(sz + off);
-            zw[j] = F::NA == 2 ? *(lds_cu16*)(sz + kWSzArr + off) : 0u;
+            for (int q = 0; q < F::NPS; ++q) issue_piece(kt / F::SPB + 1, F::NPS * ((kt % F::SPB) / 4) + q);
         }
-        float s0[4], s1[4];
+        __builtin_amdgcn_sched_barrier(0);
+
+        const lds_u8* st = smem + (p4 & 1) * kWAStage;
+        const lds_u8* sz = szb + ((kt / F::SPB) & 1) * (F::NA * kWArr);
+        const int t = kt % F::SPB;
+        // this lane's per-group words of each subtile: byte bo of its row's
+        // line, in chunk bo / 16 at position (bo / 16) ^ (row % 8)
+        const int bo = FMT == 2 ? 4 * t + 2 * (lg >> 1) : 8 * t + 2 * lg;
+        uint32_t sw[2], zw[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 2; ++j) {
+            const int lr = lr0 + n + dlr(j);
+            const int off = lr * 128 + ((((bo >> 4) ^ (lr & 7))) << 4) + (bo & 15);
+            sw[j] = *(lds_cu16*)(sz + off);
+            zw[j] = F::NA == 2 ? *(lds_cu16*)(sz + kWArr + off) : 0u;
+        }
+        float s0[2], s1[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
             if constexpr (FMT == 1) {
                 const float sc = __uint_as_float(sw[j] << 16), zz = __uint_as_float(zw[j] << 16);
                 s0[j] = sc;
@@ -1110,11 +1113,11 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            // One chunk at a time.  The expansion of subtile j + 1 is
-            // interleaved with the MFMAs of subtile j (a few VALU
-            // instructions issue while each MFMA runs), since the two waves
-            // of a SIMD pass the step barrier together and would otherwise
-            // expand, and then multiply, at the same time.
+            // One chunk at a time.  The expansion of subtile 1 is interleaved
+            // with the MFMAs of subtile 0 (a few VALU instructions issue while
+            // each MFMA runs), since the two waves of a SIMD pass the step
+            // barrier together and would otherwise expand, and then multiply,
+            // at the same time.
             __builtin_amdgcn_sched_barrier(0);
             auto expand = [&](int j) -> bf16x8_p {
                 const uint32_t w = c == 0 ? cur[j].x : c == 1 ? cur[j].y : c == 2 ? cur[j].z : cur[j].w;
@@ -1129,34 +1132,35 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
 #pragma unroll
             for (int i = 0; i < MTL; ++i)
                 af[i] = *(lds_bf16x8*)(st + (c >> 1) * AReg + (16 * i + n) * 128 + (((4 * (c & 1) + lg) ^ (n & 7)) << 4));
-            bf16x8_p bw[2];
-            bw[0] = expand(0);
+            const bf16x8_p b0 = expand(0);
+            const bf16x8_p b1 = expand(1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < 3) bw[(j + 1) & 1] = expand(j + 1);
+            for (int i = 0; i < MTL; ++i)
+                acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b0, acc[i][0], 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < MTL; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[j & 1], acc[i][j], 0, 0, 0);
-            }
-            // order: the A reads, the first expansion, then per subtile its
-            // MFMAs each followed by a share of the next expansion
+            for (int i = 0; i < MTL; ++i)
+                acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], b1, acc[i][1], 0, 0, 0);
+            // order: the A reads, the first expansion, the first subtile's
+            // MFMAs each followed by a share of the second expansion, then
+            // the second subtile's MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, MTL, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, kWExpand, 0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < MTL; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (j < 3) __builtin_amdgcn_sched_group_barrier(0x002, (kWExpand + MTL - 1) / MTL, 0);
-                }
+            for (int i = 0; i < MTL; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, (kWExpand + MTL - 1) / MTL, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MTL, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        load_codes(min(kt + 4, KT - 1), cur);
     };
     // KT is a multiple of 4
     for (int kt = 0; kt < KT; kt += 4) {
-        step(kt, 0, cb0, cb3);
-        step(kt + 1, 1, cb1, cb0);
-        step(kt + 2, 2, cb2, cb1);
-        step(kt + 3, 3, cb3, cb2);
+        step(kt, 0, cb0);
+        step(kt + 1, 1, cb1);
+        step(kt + 2, 2, cb2);
+        step(kt + 3, 3, cb3);
     }
 
     // NVFP4: the matrix scales multiply the finished sums
@@ -1167,26 +1171,21 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     }
     if (GATEUP) {
         uint16_t* hout = a.h_r + (size_t)(g.row0 + m0) * Ig;
+        const int c = nt * 128 + 16 * wave + n;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            __builtin_amdgcn_sched_barrier(0);  // a subtile's sums at a time
-            const int c = nt * 256 + 32 * wave + 16 * j + n;
+        for (int i = 0; i < MTL; ++i)
 #pragma unroll
-            for (int i = 0; i < MTL; ++i)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * i + 4 * lg + v;
-                    const float gv = FMT == 3 ? acc[i][j][v] * mg : acc[i][j][v];
-                    const float uv = FMT == 3 ? acc[i][j + 2][v] * mu : acc[i][j + 2][v];
-                    if (r < rows) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(gv, uv));
-                }
-        }
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * i + 4 * lg + v;
+                const float gv = FMT == 3 ? acc[i][0][v] * mg : acc[i][0][v];
+                const float uv = FMT == 3 ? acc[i][1][v] * mu : acc[i][1][v];
+                if (r < rows) hout[(size_t)r * Ig + c] = f32_to_bf16_bits(silu_mul(gv, uv));
+            }
     } else {
         float* yout = a.y_r + (size_t)(g.row0 + m0) * H;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            __builtin_amdgcn_sched_barrier(0);  // a subtile's sums at a time
-            const int c = nt * 512 + 64 * wave + 16 * j + n;
+        for (int j = 0; j < 2; ++j) {
+            const int c = nt * 256 + 32 * wave + 16 * j + n;
 #pragma unroll
             for (int i = 0; i < MTL; ++i)
 #pragma unroll
@@ -1206,7 +1205,7 @@ __global__ __launch_bounds__(512, 2) void expert_mfma_w4w_kernel(ExpertArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kWLds];
     lds_u8* smem = (lds_u8*)smem_raw;
     const int n64 = a.plan_counts[2], n32 = a.plan_counts[3];
-    const int NT = GATEUP ? a.I / 256 : a.H / 512;
+    const int NT = GATEUP ? a.I / 128 : a.H / 256;
     XcdWalk w(n64 + n32, NT);
     int tile, nt;
     while (w.next(&tile, &nt)) {
@@ -1229,12 +1228,12 @@ __global__ __launch_bounds__(512, 2) void expert_mfma_w4w_kernel(ExpertArgs a) {
 
 static bool wide_ok(const ExpertArgs& a, bool gateup) {
     const int K = gateup ? a.H : a.I;
-    return K % 512 == 0 && (gateup ? a.I % 256 == 0 : a.H % 512 == 0);
+    return K % 512 == 0 && (gateup ? a.I % 128 == 0 : a.H % 256 == 0);
 }
 
 template <int FMT, bool GATEUP>
 static void launch_w4w(const ExpertArgs& a, int num_cu, hipStream_t st) {
-    const int NT = GATEUP ? a.I / 256 : a.H / 512;
+    const int NT = GATEUP ? a.I / 128 : a.H / 256;
     long long grid = num_cu;
     const long long ub = 2LL * a.mfma_cap * NT;
     if (ub < grid) grid = ub;

@@ -1,9 +1,9 @@
-"""GPU: the 4-bit MFMA launch with 512-weight-row tiles, every row against
-the oracle.
+"""GPU: the 4-bit MFMA launch with wide column tiles, every row against the
+oracle.
 
 Routed 4-bit experts whose K is a multiple of 512 and whose widths are whole
-tiles (I % 256 == 0 for gate/up, H % 512 == 0 for down) run their groups of
-9..64 rows as one launch of items of up to 64 rows by 512 weight rows, beside
+tiles (I % 128 == 0 for gate/up, H % 256 == 0 for down) run their groups of
+9..64 rows as one launch of items of up to 64 rows by 256 weight rows, beside
 the 128-row tiles of the larger groups ([P5] "GLM-5.3-Flash and full GLM-5.3
 on the native CUDA engine (tracker) #593", "The pieces, in order": quantised
 expert checkpoints dequantised in the kernels; the W4A16 workload's
