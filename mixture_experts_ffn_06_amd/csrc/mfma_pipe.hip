@@ -933,23 +933,32 @@ static void launch_w4_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
 // LDS, so each line is fetched once.  Needs K % 512 == 0 and whole column
 // tiles (I % 128 == 0 for gate/up, H % 256 == 0 for down).
 constexpr int kWK = 128;                                   // K per step
-constexpr int kWRows = 64;                                 // A rows per stage
-constexpr int kWAStage = kWRows * kWK * 2;                 // 16 KiB
-constexpr int kWArr = 256 * 128;                           // one array of a block: 32 KiB
-constexpr int kWLds = 2 * kWAStage + 2 * 2 * kWArr;        // 160 KiB
+constexpr int kWLds = 160 * 1024;                          // the larger of the two layouts below
 constexpr int kWExpand = 20;                               // VALU instructions of one expansion (about)
 
-template <int FMT>
-struct WFmt {
-    static constexpr int NA = FMT == 3 ? 1 : 2;    // arrays (scales [, zeros / biases])
-    static constexpr int BPS = FMT == 2 ? 4 : 8;   // bytes per weight row, step and array
-    static constexpr int SPB = 128 / BPS;          // steps per block of per-group words
-    static constexpr int NPS = 16 * NA / SPB;      // piece instructions per wave every fourth step
+// Items of up to 64 rows (MTL <= 4): A stages of 64 rows (16 KiB) and the
+// per-group words in whole 128-byte lines (two blocks of 32 KiB per array):
+// 160 KiB with two arrays.  Items of up to 128 rows: A stages of 32 KiB and
+// half lines of 64 bytes (two blocks of 16 KiB per array): 128 KiB.
+template <int FMT, int MTL>
+struct WCfg {
+    static constexpr int NA = FMT == 3 ? 1 : 2;      // arrays (scales [, zeros / biases])
+    static constexpr int BPS = FMT == 2 ? 4 : 8;     // bytes per weight row, step and array
+    static constexpr int LineB = MTL > 4 ? 64 : 128; // bytes of a row's words per block and array
+    static constexpr int CPR = LineB / 16;           // 16-byte chunks of them
+    static constexpr int SPB = LineB / BPS;          // steps per block
+    static constexpr int NPS = NA * BPS / 8;         // piece instructions per wave every fourth step
+    static constexpr int Arr = 256 * LineB;          // bytes of one array of a block
+    static constexpr int PPA = Arr / 1024;           // piece instructions per array
+    static constexpr int RPP = 1024 / LineB;         // rows per piece instruction
+    static constexpr int AStage = MTL > 4 ? 32768 : 16384;
+    static_assert(SPB % 4 == 0, "pieces are issued every fourth step");
+    static_assert(2 * AStage + 2 * NA * Arr <= kWLds, "LDS");
 };
 
 template <int FMT, bool GATEUP, int MTL>
 __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, int m0, int nt) {
-    using F = WFmt<FMT>;
+    using F = WCfg<FMT, MTL>;
     typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -996,29 +1005,30 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         asrc[j] = arow + 8 * q;
     }
     auto issue_a = [&](int kt, int stage) {
-        lds_u8* st = smem + stage * kWAStage;
+        lds_u8* st = smem + stage * F::AStage;
 #pragma unroll
         for (int j = 0; j < LA; ++j)
             __builtin_amdgcn_global_load_lds(asrc[j] + kt * kWK, st + (wave + 8 * j) * 1024, 16, 0, 0);
     };
-    // per-group words: block b is the 128-byte line b of each of the 256
-    // weight rows per array (a line past the row's end reloads the row's last
-    // 16 bytes, unused).  In LDS, [array][row][128 bytes] with the row's
-    // 16-byte chunk k at position k ^ (row % 8).  Piece i (= wave + 8 p, p <
-    // 4 NA) covers array i / 32, rows 8 (i % 32) .. + 7; lane L writes
-    // position L % 8 of row 8 (i % 32) + L / 8.  A wave's pieces of block b + 1
-    // are issued NPS at a time at every fourth step of block b.
+    // per-group words: block b is the LineB-byte piece b of each of the 256
+    // weight rows per array (a piece past the row's end reloads the row's
+    // last 16 bytes, unused).  In LDS, [array][row][LineB bytes] with the
+    // row's 16-byte chunk k at position k ^ (row % CPR).  Instruction i (=
+    // wave + 8 p) covers array i / PPA, rows RPP (i % PPA) .. + RPP - 1; lane
+    // L writes position L % CPR of row RPP (i % PPA) + L / CPR.  A wave's
+    // instructions of block b + 1 are issued NPS at a time at every fourth
+    // step of block b.
     const unsigned char* sbase = reinterpret_cast<const unsigned char*>(GATEUP ? a.sgu : a.sd);
     const unsigned char* zbase = reinterpret_cast<const unsigned char*>(GATEUP ? a.zgu : a.zd);
-    lds_u8* const szb = smem + 2 * kWAStage;
+    lds_u8* const szb = smem + 2 * F::AStage;
     auto issue_piece = [&](int b, int p) {
         const int i = wave + 8 * p;
-        const int lr = 8 * (i & 31) + (lane >> 3);
-        const int k = (lane & 7) ^ (lr & 7);
-        const int off = min(128 * b + 16 * k, RB - 16);
+        const int lr = F::RPP * (i % F::PPA) + lane / F::CPR;
+        const int k = (lane % F::CPR) ^ (lr % F::CPR);
+        const int off = min(F::LineB * b + 16 * k, RB - 16);
         const unsigned char* src =
-            ((i >> 5) ? zbase : sbase) + ((size_t)g.expert * erows + wrow(lr)) * RB + off;
-        __builtin_amdgcn_global_load_lds(src, szb + (b & 1) * (F::NA * kWArr) + i * 1024, 16, 0, 0);
+            ((i / F::PPA) ? zbase : sbase) + ((size_t)g.expert * erows + wrow(lr)) * RB + off;
+        __builtin_amdgcn_global_load_lds(src, szb + (b & 1) * (F::NA * F::Arr) + i * 1024, 16, 0, 0);
     };
 
     // codes: lane's 16 bytes of each subtile's weight row for step kt, four
@@ -1056,13 +1066,15 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     __builtin_amdgcn_s_barrier();  // every wave is done with the previous item's LDS
     uint4 cb0[2], cb1[2], cb2[2], cb3[2];
 #pragma unroll
-    for (int p = 0; p < 4 * F::NA; ++p) issue_piece(0, p);
+    for (int p = 0; p < F::NA * F::LineB / 32; ++p) issue_piece(0, p);
     issue_a(0, 0);
-    __builtin_amdgcn_sched_barrier(0);  // (step 0's wait leaves only the last codes in flight)
     load_codes(0, cb0);
     load_codes(min(1, KT - 1), cb1);
     load_codes(min(2, KT - 1), cb2);
     load_codes(min(3, KT - 1), cb3);
+    // the item starts with nothing in flight (also the compiler's count of
+    // the loop-carried code buffers then needs no wait of its own)
+    wait_vmcnt<0>();
 
     auto step = [&](int kt, int p4, uint4* cur) {
         if (p4 == 1)
@@ -1082,19 +1094,19 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        const lds_u8* st = smem + (p4 & 1) * kWAStage;
-        const lds_u8* sz = szb + ((kt / F::SPB) & 1) * (F::NA * kWArr);
+        const lds_u8* st = smem + (p4 & 1) * F::AStage;
+        const lds_u8* sz = szb + ((kt / F::SPB) & 1) * (F::NA * F::Arr);
         const int t = kt % F::SPB;
         // this lane's per-group words of each subtile: byte bo of its row's
-        // line, in chunk bo / 16 at position (bo / 16) ^ (row % 8)
+        // piece, in chunk bo / 16 at position (bo / 16) ^ (row % CPR)
         const int bo = FMT == 2 ? 4 * t + 2 * (lg >> 1) : 8 * t + 2 * lg;
         uint32_t sw[2], zw[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int lr = lr0 + n + dlr(j);
-            const int off = lr * 128 + ((((bo >> 4) ^ (lr & 7))) << 4) + (bo & 15);
+            const int off = lr * F::LineB + (((bo >> 4) ^ (lr % F::CPR)) << 4) + (bo & 15);
             sw[j] = *(lds_cu16*)(sz + off);
-            zw[j] = F::NA == 2 ? *(lds_cu16*)(sz + kWArr + off) : 0u;
+            zw[j] = F::NA == 2 ? *(lds_cu16*)(sz + F::Arr + off) : 0u;
         }
         float s0[2], s1[2];
 #pragma unroll
@@ -1197,32 +1209,54 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     }
 }
 
-// The 64- and 32-row tile lists of the routed 4-bit groups in one launch,
-// walked per XCD as the other launches are (groups of more than 64 rows take
-// expert_mfma_w4_kernel's 128-row tiles).
-template <int FMT, bool GATEUP>
+// The tile lists of the routed 4-bit groups in two launches with their own
+// register allocations: BIG, the groups of more than 64 rows (128-row tiles,
+// a 256-row tile as two 128-row items), else the groups of 9..64 rows; both
+// walked per XCD as the other launches are.
+template <int FMT, bool GATEUP, bool BIG>
 __global__ __launch_bounds__(512, 2) void expert_mfma_w4w_kernel(ExpertArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kWLds];
     lds_u8* smem = (lds_u8*)smem_raw;
-    const int n64 = a.plan_counts[2], n32 = a.plan_counts[3];
+    const int n128 = a.plan_counts[1], n64 = a.plan_counts[2], n32 = a.plan_counts[3];
+    const int n256 = a.plan_counts[4];
     const int NT = GATEUP ? a.I / 128 : a.H / 256;
-    XcdWalk w(n64 + n32, NT);
+    XcdWalk w(BIG ? n128 + 2 * n256 : n64 + n32, NT);
     int tile, nt;
     while (w.next(&tile, &nt)) {
-        int l = 1;
-        if (tile >= n64) {
-            tile -= n64;
-            l = 2;
+        int l, half = 0;
+        if (BIG) {
+            if (tile < n128) {
+                l = 0;
+            } else {
+                tile -= n128;
+                l = 3;
+                half = tile & 1;
+                tile >>= 1;
+            }
+        } else {
+            l = 1;
+            if (tile >= n64) {
+                tile -= n64;
+                l = 2;
+            }
         }
         const int32_t* tl = a.mfma_list + 2 * (size_t)l * a.mfma_cap;
         const Group g = a.groups[tl[2 * tile]];
         if (g.expert < 0) continue;  // the shared expert is bf16
-        const int m0 = tl[2 * tile + 1];
-        const int rows = min(64, g.n - m0);
-        if (rows > 32)
-            wide_tile_w4<FMT, GATEUP, 4>(a, smem, g, m0, nt);
-        else
-            wide_tile_w4<FMT, GATEUP, 2>(a, smem, g, m0, nt);
+        const int m0 = tl[2 * tile + 1] + 128 * half;
+        if (m0 >= g.n) continue;
+        const int rows = min(BIG ? 128 : 64, g.n - m0);
+        if constexpr (BIG) {
+            if (rows > 96)
+                wide_tile_w4<FMT, GATEUP, 8>(a, smem, g, m0, nt);
+            else
+                wide_tile_w4<FMT, GATEUP, 6>(a, smem, g, m0, nt);
+        } else {
+            if (rows > 32)
+                wide_tile_w4<FMT, GATEUP, 4>(a, smem, g, m0, nt);
+            else
+                wide_tile_w4<FMT, GATEUP, 2>(a, smem, g, m0, nt);
+        }
     }
 }
 
@@ -1235,22 +1269,17 @@ template <int FMT, bool GATEUP>
 static void launch_w4w(const ExpertArgs& a, int num_cu, hipStream_t st) {
     const int NT = GATEUP ? a.I / 128 : a.H / 256;
     long long grid = num_cu;
-    const long long ub = 2LL * a.mfma_cap * NT;
+    const long long ub = 3LL * a.mfma_cap * NT;
     if (ub < grid) grid = ub;
     grid = grid < 8 ? 8 : grid & ~7LL;  // the XCD walk deals blocks in groups of 8
-    expert_mfma_w4w_kernel<FMT, GATEUP><<<(int)grid, 512, 0, st>>>(a);
+    expert_mfma_w4w_kernel<FMT, GATEUP, true><<<(int)grid, 512, 0, st>>>(a);
+    expert_mfma_w4w_kernel<FMT, GATEUP, false><<<(int)grid, 512, 0, st>>>(a);
 }
 
 template <int FMT>
 static void launch_w4_fmt(const ExpertArgs& a, bool gateup, int num_cu, hipStream_t st) {
     if (wide_ok(a, gateup)) {
-        if (gateup) {
-            launch_w4_bm<FMT, true, 128>(a, num_cu, st);
-            launch_w4w<FMT, true>(a, num_cu, st);
-        } else {
-            launch_w4_bm<FMT, false, 128>(a, num_cu, st);
-            launch_w4w<FMT, false>(a, num_cu, st);
-        }
+        gateup ? launch_w4w<FMT, true>(a, num_cu, st) : launch_w4w<FMT, false>(a, num_cu, st);
         return;
     }
     if (gateup) {

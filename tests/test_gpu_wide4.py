@@ -2,9 +2,9 @@
 oracle.
 
 Routed 4-bit experts whose K is a multiple of 512 and whose widths are whole
-tiles (I % 128 == 0 for gate/up, H % 256 == 0 for down) run their groups of
-9..64 rows as one launch of items of up to 64 rows by 256 weight rows, beside
-the 128-row tiles of the larger groups ([P5] "GLM-5.3-Flash and full GLM-5.3
+tiles (I % 128 == 0 for gate/up, H % 256 == 0 for down) run every group of
+more than 8 rows in two launches of items 256 weight rows wide: one of items
+of up to 128 rows (groups of more than 64), one of up to 64 (9..64 rows) ([P5] "GLM-5.3-Flash and full GLM-5.3
 on the native CUDA engine (tracker) #593", "The pieces, in order": quantised
 expert checkpoints dequantised in the kernels; the W4A16 workload's
 (q - z) * s per 32 inputs, MLX affine's s * q + b per 64, NVFP4's e2m1 *
