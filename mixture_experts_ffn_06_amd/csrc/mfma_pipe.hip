@@ -986,15 +986,17 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     // holding, for row r, the chunks 4 lg + 2 R + h (lg = 0..3, h = 0..1:
     // the 16-byte chunks that chunk steps c = 2 R + h read) at positions
     // (4 h + lg) ^ (r % 8), so that the 64 lanes of an operand read (16 rows,
-    // four lane groups) meet no bank twice.  Instruction ii (= wave + 8 j)
-    // fills region ii / (2 MTL), lines 8 (ii % (2 MTL)) .. + 7: lane L writes
-    // position L % 8 of line 8 (ii % (2 MTL)) + L / 8.
-    constexpr int LA = MTL / 2;  // A instructions per wave and step
+    // four lane groups) meet no bank twice.  Instruction ii (= wave + 8 j,
+    // below 4 MTL) fills region ii / (2 MTL), lines 8 (ii % (2 MTL)) .. + 7:
+    // lane L writes position L % 8 of line 8 (ii % (2 MTL)) + L / 8.  With an
+    // odd MTL the first four waves issue one instruction more than the
+    // others; the waits below count only what was issued after a stage.
+    constexpr int LA = (4 * MTL + 7) / 8;  // A instructions per wave and step (at most)
     constexpr int AReg = 16 * MTL * 128;  // bytes of a region
     const uint16_t* asrc[LA];
 #pragma unroll
     for (int j = 0; j < LA; ++j) {
-        const int ii = wave + 8 * j;
+        const int ii = min(wave + 8 * j, 4 * MTL - 1);  // (an unused instruction's source stays in the tile)
         const int R = ii / (2 * MTL);
         const int r = 8 * (ii % (2 * MTL)) + (lane >> 3);
         const int hl = (lane & 7) ^ (r & 7);  // 4 h + lg
@@ -1008,7 +1010,8 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
         lds_u8* st = smem + stage * F::AStage;
 #pragma unroll
         for (int j = 0; j < LA; ++j)
-            __builtin_amdgcn_global_load_lds(asrc[j] + kt * kWK, st + (wave + 8 * j) * 1024, 16, 0, 0);
+            if ((4 * MTL) % 8 == 0 || wave + 8 * j < 4 * MTL)  // wave-uniform
+                __builtin_amdgcn_global_load_lds(asrc[j] + kt * kWK, st + (wave + 8 * j) * 1024, 16, 0, 0);
     };
     // per-group words: block b is the LineB-byte piece b of each of the 256
     // weight rows per array (a piece past the row's end reloads the row's
@@ -1246,14 +1249,22 @@ __global__ __launch_bounds__(512, 2) void expert_mfma_w4w_kernel(ExpertArgs a) {
         const int m0 = tl[2 * tile + 1] + 128 * half;
         if (m0 >= g.n) continue;
         const int rows = min(BIG ? 128 : 64, g.n - m0);
+        // as many 16-row subtiles as the rows fill (at least 5 in BIG: the
+        // second half of a 129..256-row group may be short)
         if constexpr (BIG) {
-            if (rows > 96)
+            if (rows > 112)
                 wide_tile_w4<FMT, GATEUP, 8>(a, smem, g, m0, nt);
-            else
+            else if (rows > 96)
+                wide_tile_w4<FMT, GATEUP, 7>(a, smem, g, m0, nt);
+            else if (rows > 80)
                 wide_tile_w4<FMT, GATEUP, 6>(a, smem, g, m0, nt);
+            else
+                wide_tile_w4<FMT, GATEUP, 5>(a, smem, g, m0, nt);
         } else {
-            if (rows > 32)
+            if (rows > 48)
                 wide_tile_w4<FMT, GATEUP, 4>(a, smem, g, m0, nt);
+            else if (rows > 32)
+                wide_tile_w4<FMT, GATEUP, 3>(a, smem, g, m0, nt);
             else
                 wide_tile_w4<FMT, GATEUP, 2>(a, smem, g, m0, nt);
         }
