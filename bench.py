@@ -158,12 +158,12 @@ def roofline_for(w, counts, stage_ms, counted=True):
             nbytes = wbytes + act
             flops = 2.0 * routed * 2 * w.I * w.H
     else:
-        # 4-bit: the two wide-tile launches (groups of more than 64 rows, and
-        # of 9..64) when H % 512 == 0 and I % 128 == 0, else the 128-, 64- and
+        # 4-bit: the wide-tile launch (groups of more than 64 rows, then of
+        # 9..64) when H % 512 == 0 and I % 128 == 0, else the 128-, 64- and
         # 32-row launches
         wide = w.H % 512 == 0 and w.I % 128 == 0
         fc = FMT_CODE[w.fmt]
-        w4_names = ([f"expert_mfma_w4w_kernel<{fc},true,true>", f"expert_mfma_w4w_kernel<{fc},true,false>"] if wide
+        w4_names = ([f"expert_mfma_w4w_kernel<{fc},true>"] if wide
                     else [f"expert_mfma_w4_kernel<{fc},true,{bm}>" for bm in (128, 64, 32)])
         kernel = ("expert_mfma_pipe_kernel<true,256> + expert_mfma_small_kernel<true>" if w.fmt == "bf16"
                   else " + ".join(w4_names) + " + shared-expert bf16 launch")

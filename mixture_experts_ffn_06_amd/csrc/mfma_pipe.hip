@@ -1212,22 +1212,24 @@ __device__ void wide_tile_w4(const ExpertArgs& a, lds_u8* smem, const Group& g, 
     }
 }
 
-// The tile lists of the routed 4-bit groups in two launches with their own
-// register allocations: BIG, the groups of more than 64 rows (128-row tiles,
-// a 256-row tile as two 128-row items), else the groups of 9..64 rows; both
-// walked per XCD as the other launches are.
-template <int FMT, bool GATEUP, bool BIG>
+// The tile lists of the routed 4-bit groups in one persistent launch: the
+// groups of more than 64 rows first (128-row items, a 256-row tile as two
+// 128-row items), then the groups of 9..64 rows, walked per XCD as the other
+// launches are.  (One block per CU either way: the LDS of an item fills it.)
+template <int FMT, bool GATEUP>
 __global__ __launch_bounds__(512, 2) void expert_mfma_w4w_kernel(ExpertArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[kWLds];
     lds_u8* smem = (lds_u8*)smem_raw;
     const int n128 = a.plan_counts[1], n64 = a.plan_counts[2], n32 = a.plan_counts[3];
     const int n256 = a.plan_counts[4];
+    const int nbig = n128 + 2 * n256;
     const int NT = GATEUP ? a.I / 128 : a.H / 256;
-    XcdWalk w(BIG ? n128 + 2 * n256 : n64 + n32, NT);
+    XcdWalk w(nbig + n64 + n32, NT);
     int tile, nt;
     while (w.next(&tile, &nt)) {
         int l, half = 0;
-        if (BIG) {
+        const bool big = tile < nbig;
+        if (big) {
             if (tile < n128) {
                 l = 0;
             } else {
@@ -1237,6 +1239,7 @@ __global__ __launch_bounds__(512, 2) void expert_mfma_w4w_kernel(ExpertArgs a) {
                 tile >>= 1;
             }
         } else {
+            tile -= nbig;
             l = 1;
             if (tile >= n64) {
                 tile -= n64;
@@ -1248,10 +1251,10 @@ __global__ __launch_bounds__(512, 2) void expert_mfma_w4w_kernel(ExpertArgs a) {
         if (g.expert < 0) continue;  // the shared expert is bf16
         const int m0 = tl[2 * tile + 1] + 128 * half;
         if (m0 >= g.n) continue;
-        const int rows = min(BIG ? 128 : 64, g.n - m0);
-        // as many 16-row subtiles as the rows fill (at least 5 in BIG: the
-        // second half of a 129..256-row group may be short)
-        if constexpr (BIG) {
+        const int rows = min(big ? 128 : 64, g.n - m0);
+        // as many 16-row subtiles as the rows fill (at least 5 for a big
+        // item: the second half of a 129..256-row group may be short)
+        if (big) {
             if (rows > 112)
                 wide_tile_w4<FMT, GATEUP, 8>(a, smem, g, m0, nt);
             else if (rows > 96)
@@ -1283,8 +1286,7 @@ static void launch_w4w(const ExpertArgs& a, int num_cu, hipStream_t st) {
     const long long ub = 3LL * a.mfma_cap * NT;
     if (ub < grid) grid = ub;
     grid = grid < 8 ? 8 : grid & ~7LL;  // the XCD walk deals blocks in groups of 8
-    expert_mfma_w4w_kernel<FMT, GATEUP, true><<<(int)grid, 512, 0, st>>>(a);
-    expert_mfma_w4w_kernel<FMT, GATEUP, false><<<(int)grid, 512, 0, st>>>(a);
+    expert_mfma_w4w_kernel<FMT, GATEUP><<<(int)grid, 512, 0, st>>>(a);
 }
 
 template <int FMT>
