@@ -3,8 +3,9 @@ oracle.
 
 Routed 4-bit experts whose K is a multiple of 512 and whose widths are whole
 tiles (I % 128 == 0 for gate/up, H % 256 == 0 for down) run every group of
-more than 8 rows in two launches of items 256 weight rows wide: one of items
-of up to 128 rows (groups of more than 64), one of up to 64 (9..64 rows) ([P5] "GLM-5.3-Flash and full GLM-5.3
+more than 8 rows in one launch of items 256 weight rows wide: first the items
+of up to 128 rows (groups of more than 64), then those of up to 64 (9..64
+rows) ([P5] "GLM-5.3-Flash and full GLM-5.3
 on the native CUDA engine (tracker) #593", "The pieces, in order": quantised
 expert checkpoints dequantised in the kernels; the W4A16 workload's
 (q - z) * s per 32 inputs, MLX affine's s * q + b per 64, NVFP4's e2m1 *
@@ -53,3 +54,22 @@ def test_band_and_no_shared(fmt):
     side = OracleSide(w, d)
     check_routing(ex, side, 2, 13)
     compare(y, side.layer(list(range(w.T)), 2, 13, shared=False), f"wide tiles band {fmt}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("T", [20, 40, 100, 200])
+def test_one_tile_list_alone(fmt, T):
+    # A zero router (every logit +0.0, ties to the lower id) sends every row
+    # to experts 0..3: four groups of T rows, so only one tile list of the
+    # launch has items (T = 20: 9..32 rows, 40: 33..64, 100: 65..128, 200:
+    # two 128-row items per group), and the other list is empty.
+    w = WIDE4.with_(fmt=fmt, T=T)
+    log(f"case {w}")
+    d = gpu_inputs(w)
+    d["router_w"].zero_()
+    d["bias"] = torch.zeros(w.E, dtype=torch.float32, device="cuda")
+    y, ex = run_gpu(w, d)
+    assert sorted(ex["counts"].cpu().tolist(), reverse=True)[:5] == [T, T, T, T, 0]
+    side = OracleSide(w, d)
+    check_routing(ex, side, 0, w.E)
+    compare(y, side.layer(list(range(w.T)), 0, w.E), f"one tile list {fmt} T={T}")
