@@ -914,11 +914,14 @@ static void launch_w4_bm(const ExpertArgs& a, int num_cu, hipStream_t st) {
 
 // ---- 4-bit experts, wide column tiles ---------------------------------------
 //
-// For the 64- and 32-row tile lists (groups of 9..64 rows), whose 128-weight-
-// row tiles above are bound by their loads.  One block of 8 waves per CU (two
-// per SIMD).  An item is up to 64 rows of a group by 256 weight rows
-// (gate/up: 128 gate and the matching 128 up columns; down: 256 output
-// columns); wave w owns 32 of the weight rows as two 16-column subtiles.  K
+// For every group of more than 8 rows when the widths are whole wide tiles
+// (the 128-weight-row tiles above are bound by their loads).  One block of 8
+// waves per CU (two per SIMD).  An item is up to 128 rows (groups of more
+// than 64 rows; a 256-row tile as two items) or up to 64 rows (groups of
+// 9..64) of a group by 256 weight rows (gate/up: 128 gate and the matching
+// 128 up columns; down: 256 output columns); wave w owns 32 of the weight
+// rows as two 16-column subtiles and runs as many 16-row subtiles as the
+// item's rows fill.  K
 // advances 128 per step.  Within a step, lane l (column l % 16 of a subtile,
 // lane group l / 16) takes the 32 inputs 32 (l / 16) .. + 31 of the step, one
 // 32-input group; its chunk c (c = 0..3) is the MFMA operand pair of inputs
