@@ -99,3 +99,19 @@ def test_committed_counters_parse():
                 assert int(f[3]) > 0 and len(f[4]) == 16
                 n += 1
     assert n >= 20
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "shared_probe", "bands", "bands_adversarial",
+                                  "w4_t1", "w4_t2048", "affine4_t1", "affine4_t2048", "nvfp4_t1",
+                                  "nvfp4_t2048"])
+def test_committed_counters_cover_the_reported_launches(name):
+    # The default run reports counter traffic for the dominant launches of
+    # every workload; the committed counters must name those launches and
+    # carry the hash of the current kernel sources.  A renamed kernel, or a
+    # kernel source changed without new counter runs, fails here instead of
+    # turning the reported traffic into null.
+    w = W[name]
+    counts = torch.zeros(w.E, dtype=torch.long)
+    counts[: w.topk] = w.T  # the launch names do not depend on the routing
+    r = bench.roofline_for(w, counts, _stages(), counted=True)
+    assert r["traffic"] is not None, f"{name}: no committed counters for {r['kernel']}"
